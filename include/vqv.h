@@ -1,0 +1,132 @@
+/*
+ * vqv.h - C ABI of libvqv: the block-verification projection of DFlash-style
+ * speculative decoding on AMD Instinct MI355X (gfx950).
+ *
+ * Two operations, each an asynchronous launch on the caller's HIP stream:
+ *
+ *   vqv_qgemm   y[M,N] = x[M,K] . W^T, W[N,K] 4-bit group-quantized (affine,
+ *               group 64 along K), fp32 output. This is the quantized linear
+ *               that a target model runs over the M rows of a verify block
+ *               ("perf: tune DFlash2 M=8 verification for M1 and M2", PR
+ *               description: tuned M=8 verification QMM with BF16/FP16
+ *               activations and a W4A32 draft/vocabulary path).
+ *   vqv_verify  per-row greedy argmax of fp32 logits[B*T, N], then per
+ *               sequence the number of leading drafts that the target
+ *               confirms ("perf(speculative): commit per-row accepts in
+ *               batched DFlash", commit message: each row commits its own
+ *               walk count; "dspark: fold first-token forward into verify +
+ *               bit-exact M5 Metal decode wins", first commit: the committed
+ *               token is verified as row 0 of the block).
+ *
+ * Memory and ownership
+ *   Every pointer is DEVICE memory owned by the caller; the library never
+ *   allocates, frees or keeps a pointer after the call returns. Tensors are
+ *   dense and row-major. `hip_stream` is a hipStream_t (NULL = the default
+ *   stream). Calls only enqueue work: results are valid once the stream has
+ *   been synchronized. Asynchronous faults surface at that synchronization.
+ *   Calls are thread-safe and deterministic: the same inputs give the same
+ *   output bits on every call.
+ *
+ * Errors
+ *   Arguments are checked on the host before anything is launched. A call
+ *   that returns anything but VQV_OK has launched nothing and written
+ *   nothing. VQV_ERR_HIP means the launch itself failed (hipGetLastError).
+ */
+#ifndef VQV_H
+#define VQV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VQV_ABI_VERSION 1
+
+typedef enum {
+  VQV_BF16 = 0, /* bfloat16 activations                                  */
+  VQV_FP16 = 1, /* IEEE half activations                                 */
+  VQV_FP32 = 2  /* IEEE single activations (the W4A32 draft projection)  */
+} vqv_dtype;
+
+typedef enum {
+  VQV_OK = 0,
+  VQV_ERR_ARG = 1,         /* NULL pointer, size out of range, or aliasing   */
+  VQV_ERR_UNSUPPORTED = 2, /* valid request this build does not handle     */
+  VQV_ERR_ALIGN = 3,       /* a pointer breaks its alignment requirement    */
+  VQV_ERR_WORKSPACE = 4,   /* workspace missing or smaller than queried     */
+  VQV_ERR_HIP = 5          /* the HIP runtime refused the launch            */
+} vqv_status;
+
+/* VQV_ABI_VERSION of the loaded library. */
+int vqv_abi_version(void);
+
+/* Static English text for a status code (never NULL). */
+const char* vqv_status_string(vqv_status s);
+
+/*
+ * Weight format (the affine 4-bit layout shared by the tuned kernels and the
+ * stock QMM path they fall back to, "perf: tune DFlash2 M=8 verification for
+ * M1 and M2", PR description; the pages do not spell out the bits, the
+ * reading used here is):
+ *   wq      uint8  [N, K/2]  row n holds column n's K codes, K-contiguous
+ *                            ("K-major"); byte j packs k=2j in bits 0-3 and
+ *                            k=2j+1 in bits 4-7. Codes q are 0..15.
+ *   scales  fp16   [N, K/group]  s[n,g]
+ *   biases  fp16   [N, K/group]  b[n,g]
+ *   w[n,k] = s[n, k/group] * q[n,k] + b[n, k/group]
+ *   y[m,n] = sum_k x[m,k] * w[n,k]      (accumulated in fp32)
+ *
+ * Arguments
+ *   x          [M, K] in act_dtype. 16-byte aligned.
+ *   wq         [N, K/2] uint8. 16-byte aligned.
+ *   scales     [N, K/group] fp16 bit patterns. 2-byte aligned.
+ *   biases     [N, K/group] fp16 bit patterns. 2-byte aligned.
+ *   y          [M, N] fp32, written. 4-byte aligned. Must not overlap any
+ *              input (VQV_ERR_ARG).
+ *   M          1..64 verify rows (a block of 8 or 16, up to 64 batched).
+ *   K          multiple of 64, >= 64; M*K*sizeof(act) < 2^31.
+ *   N          >= 1 output columns; any N (tails are masked).
+ *   group      must be 64 (else VQV_ERR_UNSUPPORTED).
+ *   act_dtype  a vqv_dtype (else VQV_ERR_ARG).
+ *   workspace  device scratch of at least vqv_qgemm_workspace_bytes(...)
+ *              bytes; may be NULL when that is 0.
+ *
+ * Numerics: products of x and the 4-bit codes are exact; sums are fp32; the
+ * per-group scale and bias are applied in fp32 after each group's partial
+ * sum. NaN/Inf in x, scales or biases propagate by IEEE rules.
+ */
+size_t vqv_qgemm_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype);
+
+vqv_status vqv_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
+                     const uint16_t* biases, float* y, int M, int K, int N, int group,
+                     vqv_dtype act_dtype, void* workspace, size_t workspace_bytes,
+                     void* hip_stream);
+
+/*
+ * Greedy verify over one verify block per sequence.
+ *   logits      [B*T, N] fp32, row b*T+i is sequence b's row i. Row 0 is the
+ *               committed token, rows 1..T-1 the drafts. 16-byte aligned.
+ *   draft       [B, T-1] int32: draft[b,i] is the token fed at row i+1.
+ *               May be NULL only when T == 1. 4-byte aligned.
+ *   argmax      [B*T] int32, written: lowest index of the row maximum; -0
+ *               and +0 are equal; a row holding NaN gives its first NaN.
+ *   accept_len  [B] int32, written: the largest L in 0..T-1 such that
+ *               argmax[b*T+i] == draft[b,i] for every i < L. The bonus token
+ *               argmax[b*T+L] is implied; tokens committed = L + 1.
+ *   B >= 1, 1 <= T <= 64, N >= 1, B*T*N < 2^31.
+ *   workspace   at least vqv_verify_workspace_bytes(B, T, N) bytes.
+ * Draft ids are compared as plain int32: ids outside [0, N) never match.
+ */
+size_t vqv_verify_workspace_bytes(int B, int T, int N);
+
+vqv_status vqv_verify(const float* logits, const int32_t* draft, int B, int T, int N,
+                      int32_t* argmax, int32_t* accept_len, void* workspace,
+                      size_t workspace_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VQV_H */

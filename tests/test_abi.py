@@ -1,0 +1,144 @@
+"""The C ABI: the library loads, exports every symbol include/vqv.h declares,
+and rejects bad arguments on the host with the documented status before any
+launch. The CPU tests pass fabricated (never dereferenced) pointers, which is
+safe because validation happens before anything touches the device."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vqv.h")
+
+OK, ARG, UNSUP, ALIGN, WS, HIP = range(6)
+BF16, FP16, FP32 = range(3)
+
+
+@pytest.fixture(scope="module")
+def L():
+    from w4_gemm_vqv_amd import vqv
+    if not os.path.exists(vqv.LIB_PATH):
+        from w4_gemm_vqv_amd.build import build
+        build(verbose=False)
+    return vqv.lib()
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return sorted(set(re.findall(r"^\s*[\w\s\*]+?\b(vqv_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_calls():
+    assert declared_functions() == sorted(
+        ["vqv_abi_version", "vqv_status_string", "vqv_qgemm_workspace_bytes", "vqv_qgemm",
+         "vqv_verify_workspace_bytes", "vqv_verify"])
+
+
+def test_exports_every_declared_symbol(L):
+    from w4_gemm_vqv_amd import vqv
+    out = subprocess.run(["nm", "-D", "--defined-only", vqv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (vqv_\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+    assert set(vqv.EXPORTS) == set(declared_functions())
+
+
+def test_version_and_strings(L):
+    assert L.vqv_abi_version() == 1
+    for s in range(6):
+        assert L.vqv_status_string(s)
+    assert L.vqv_status_string(99) == b"unknown status"
+
+
+def test_workspace_queries(L):
+    assert L.vqv_qgemm_workspace_bytes(8, 5120, 17408, 64, BF16) == 0
+    assert L.vqv_verify_workspace_bytes(1, 8, 17408) == 8 * 5 * 8
+    assert L.vqv_verify_workspace_bytes(4, 16, 151936) == 64 * 38 * 8
+    assert L.vqv_verify_workspace_bytes(1, 1, 1) == 8
+    assert L.vqv_verify_workspace_bytes(0, 8, 10) == 0
+
+
+# Fabricated, well-aligned and non-overlapping device addresses.
+X, W, S, B_, Y, WSP = (0x10000000 * i for i in range(1, 7))
+
+
+def q(L, x=X, wq=W, s=S, b=B_, y=Y, M=8, K=512, N=1024, group=64, act=BF16, ws=None, wsb=0):
+    return L.vqv_qgemm(x, wq, s, b, y, M, K, N, group, act, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), ARG), (dict(wq=None), ARG), (dict(s=None), ARG), (dict(b=None), ARG),
+    (dict(y=None), ARG), (dict(M=0), ARG), (dict(M=65), ARG), (dict(N=0), ARG), (dict(K=0), ARG),
+    (dict(K=32), ARG), (dict(K=100), ARG), (dict(group=32), UNSUP), (dict(group=128), UNSUP),
+    (dict(act=3), ARG), (dict(act=-1), ARG), (dict(x=X + 8), ALIGN), (dict(wq=W + 4), ALIGN),
+    (dict(s=S + 1), ALIGN), (dict(y=Y + 2), ALIGN), (dict(y=X), ARG), (dict(y=W + 64), ARG),
+    (dict(y=S), ARG), (dict(M=64, K=64 * 2 ** 20, act=FP32), UNSUP),
+])
+def test_qgemm_rejects(L, kw, status):
+    assert q(L, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(logits=None), ARG), (dict(argmax=None), ARG), (dict(acc=None), ARG),
+    (dict(B=0), ARG), (dict(T=0), ARG), (dict(T=65), ARG), (dict(N=0), ARG),
+    (dict(draft=None), ARG), (dict(B=2 ** 20, T=64, N=64), ARG), (dict(logits=X + 4), ALIGN),
+    (dict(argmax=Y + 2), ALIGN), (dict(ws=None), WS), (dict(wsb=8), WS), (dict(ws=WSP + 4), WS),
+    (dict(argmax=X + 64), ARG), (dict(acc=X), ARG), (dict(ws=X), ARG),
+])
+def test_verify_rejects(L, kw, status):
+    a = dict(logits=X, draft=W, B=1, T=8, N=1024, argmax=Y, acc=S, ws=WSP, wsb=1 << 20)
+    a.update(kw)
+    assert L.vqv_verify(a["logits"], a["draft"], a["B"], a["T"], a["N"], a["argmax"], a["acc"],
+                        a["ws"], a["wsb"], None) == status
+
+
+def test_python_binding_raises_with_status(L):
+    from w4_gemm_vqv_amd import vqv
+    with pytest.raises(vqv.VqvError) as e:
+        vqv._check(ARG)
+    assert e.value.status == ARG
+
+
+def test_binding_has_no_cpu_path():
+    """The binding and the library never import the oracle."""
+    pkg = os.path.join(ROOT, "w4_gemm_vqv_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("oracle's", ""), f
+                assert "import gen" not in text, f
+
+
+# ---------------------------------------------------------------- on the GPU
+
+
+@pytest.mark.gpu
+def test_rejected_calls_write_nothing():
+    import torch
+    from w4_gemm_vqv_amd import vqv
+    Lg = vqv.lib()
+    x = torch.zeros(8, 512, dtype=torch.bfloat16, device="cuda")
+    wq = torch.zeros(1024, 256, dtype=torch.uint8, device="cuda")
+    s = torch.zeros(1024, 8, dtype=torch.float16, device="cuda")
+    y = torch.full((8, 1024), 7.0, device="cuda")
+    for M, K, group in [(0, 512, 64), (8, 512, 32), (8, 500, 64)]:
+        st = Lg.vqv_qgemm(x.data_ptr(), wq.data_ptr(), s.data_ptr(), s.data_ptr(), y.data_ptr(),
+                          M, K, 1024, group, BF16, None, 0, None)
+        assert st != OK
+    lg = torch.zeros(8, 1024, device="cuda")
+    am = torch.full((8,), -3, dtype=torch.int32, device="cuda")
+    ac = torch.full((1,), -3, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(8, dtype=torch.uint8, device="cuda")
+    st = Lg.vqv_verify(lg.data_ptr(), None, 1, 8, 1024, am.data_ptr(), ac.data_ptr(),
+                       ws.data_ptr(), 8, None)
+    assert st == ARG
+    torch.cuda.synchronize()
+    assert (y == 7.0).all() and (am == -3).all() and (ac == -3).all()

@@ -1,0 +1,184 @@
+"""GPU parity of vqv_qgemm against the CPU oracle (through the C ABI).
+
+Small cases compare every output; the full-size workloads compare sampled
+columns (the oracle computes those one by one), in the launch configuration
+the benchmark uses.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+from oracle import qgemm_ref
+from tests.devutil import assert_close, sha, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def vqv():
+    import w4_gemm_vqv_amd as v
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    v.lib()  # fails loudly if the HIP library is missing
+    return v
+
+
+def run(vqv, c, M=None):
+    d = to_device(c)
+    x = d["x"] if M is None else d["x"][:M].contiguous()
+    y = vqv.vqv_qgemm(x, d["wq"], d["scales"], d["biases"])
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def case(M, K, N, act, seed, sigma=1.0, real_rows=None):
+    rng = np.random.default_rng(seed)
+    wq, s, b = gen.make_weights(rng, N, K)
+    x = gen.make_x(rng, M, K, act, sigma, real_rows)
+    return dict(M=M, K=K, N=N, act=act, wq=wq, scales=s, biases=b, x=x)
+
+
+# Shapes span several column tiles and work-group splits, ragged N tails,
+# odd group counts (K/64 odd), and M across row-set boundaries.
+SHAPES = [
+    (8, 512, 1024), (8, 64, 3), (1, 128, 17), (4, 192, 65), (5, 320, 1000), (8, 1088, 129),
+    (3, 5120, 200), (9, 256, 70), (16, 640, 300), (17, 128, 64), (32, 256, 96), (33, 384, 50),
+    (64, 512, 130), (7, 4096, 64), (8, 8192, 77),
+]
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_parity_small(vqv, act, M, K, N):
+    c = case(M, K, N, act, seed=M * 1000 + K + N)
+    y = run(vqv, c)
+    ref = qgemm_ref(c["x"], act, c["wq"], c["scales"], c["biases"])
+    assert_close(y, ref, act, f"M={M} K={K} N={N} {act}")
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("M,K,N", [(8, 512, 1024), (3, 192, 37), (16, 1280, 96), (64, 256, 40)])
+def test_integer_case_bit_exact(vqv, act, M, K, N):
+    """s = 1, integer biases, integer x in [-8, 8]: every partial sum is an
+    integer below 2^24, so fp32 is exact in any order and the GPU must equal
+    the oracle bit for bit. Pins unpacking, indexing, group mapping, tails."""
+    rng = np.random.default_rng(7 + M + K + N)
+    wq = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    G = K // 64
+    s = np.full((N, G), np.float16(1.0).view(np.uint16), dtype=np.uint16)
+    b = rng.integers(-8, 1, size=(N, G)).astype(np.float16).view(np.uint16)
+    xi = rng.integers(-8, 9, size=(M, K)).astype(np.float32)
+    x = {"bf16": lambda: gen.f32_to_bf16_bits(xi), "fp16": lambda: xi.astype(np.float16).view(np.uint16),
+         "fp32": lambda: xi}[act]()
+    c = dict(M=M, K=K, N=N, act=act, wq=wq, scales=s, biases=b, x=x)
+    y = run(vqv, c)
+    ref = qgemm_ref(x, act, wq, s, b)
+    np.testing.assert_array_equal(y, ref.astype(np.float32))
+
+
+def test_dyadic_scales_bit_exact(vqv):
+    """s = 2^-6 and b = -8*2^-6: still exact in fp32 (dyadic, small)."""
+    M, K, N = 8, 1024, 300
+    rng = np.random.default_rng(11)
+    wq = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    s = np.full((N, K // 64), np.float16(2.0 ** -6).view(np.uint16), dtype=np.uint16)
+    b = np.full((N, K // 64), np.float16(-8 * 2.0 ** -6).view(np.uint16), dtype=np.uint16)
+    x = gen.f32_to_bf16_bits(rng.integers(-8, 9, size=(M, K)).astype(np.float32))
+    c = dict(M=M, K=K, N=N, act="bf16", wq=wq, scales=s, biases=b, x=x)
+    np.testing.assert_array_equal(run(vqv, c), qgemm_ref(x, "bf16", wq, s, b).astype(np.float32))
+
+
+def test_zero_padded_rows_are_exact_zero(vqv):
+    """W4A32 draft projection: 1 real row + 7 zero rows; padding gives 0.0."""
+    c = gen.make_config("draft_w4a32", N=512, K=1024)
+    y = run(vqv, c)
+    assert np.all(y[1:] == 0.0)
+    ref = qgemm_ref(c["x"], "fp32", c["wq"], c["scales"], c["biases"])
+    assert_close(y, ref, "fp32", "draft_w4a32 scaled")
+
+
+def test_zero_codes_identity(vqv):
+    """All-zero codes: y = sum_g b * xsum_g (the bias-only identity)."""
+    c = case(8, 512, 256, "bf16", seed=5)
+    c["wq"][:] = 0
+    y = run(vqv, c)
+    ref = qgemm_ref(c["x"], "bf16", c["wq"], c["scales"], c["biases"])
+    assert_close(y, ref, "bf16", "zero codes")
+
+
+def test_rows_independent_of_M(vqv):
+    """Row r computed at M=1, 4 and 8 from the same x rows: each within the
+    contract. Bit equality across M is reported, not required."""
+    c = case(8, 1024, 500, "bf16", seed=9)
+    ref = qgemm_ref(c["x"], "bf16", c["wq"], c["scales"], c["biases"])
+    ys = {M: run(vqv, c, M=M) for M in (1, 4, 8)}
+    for M, y in ys.items():
+        assert_close(y, ref[:M], "bf16", f"M={M}")
+    same = np.array_equal(ys[1][0], ys[8][0]) and np.array_equal(ys[4], ys[8][:4])
+    print(f"row results bit-identical across M=1/4/8: {same}")
+
+
+def test_deterministic_fingerprint(vqv):
+    c = case(8, 2048, 4096, "bf16", seed=12)
+    d = to_device(c)
+    hs = set()
+    for _ in range(3):
+        y = vqv.vqv_qgemm(d["x"], d["wq"], d["scales"], d["biases"])
+        torch.cuda.synchronize()
+        hs.add(sha(y))
+    assert len(hs) == 1
+
+
+def test_nonfinite_activation_propagates(vqv):
+    c = case(4, 256, 64, "fp32", seed=13)
+    c["x"][1, 70] = np.nan
+    c["x"][2, 3] = np.inf
+    y = run(vqv, c)
+    assert np.isnan(y[1]).all()
+    assert (~np.isfinite(y[2])).all()
+    ref = qgemm_ref(c["x"], "fp32", c["wq"], c["scales"], c["biases"])
+    assert_close(y[[0, 3]], ref[[0, 3]], "fp32", "finite rows")
+
+
+def test_writes_only_its_output(vqv):
+    """y is written exactly in [M, N]; guard bytes around it stay untouched."""
+    c = case(5, 256, 70, "bf16", seed=14)
+    d = to_device(c)
+    buf = torch.full((5 * 70 + 64,), 123.0, dtype=torch.float32, device="cuda")
+    y = buf[32:32 + 5 * 70].view(5, 70)
+    vqv.vqv_qgemm(d["x"], d["wq"], d["scales"], d["biases"], y=y)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert np.all(b[:32] == 123.0) and np.all(b[32 + 350:] == 123.0)
+    ref = qgemm_ref(c["x"], "bf16", c["wq"], c["scales"], c["biases"])
+    assert_close(y.cpu().numpy(), ref, "bf16", "offset output")
+
+
+# ---------------------------------------------------------------- full sizes
+
+FULL = [("target", 8), ("target", 4), ("target", 1), ("draft_w4a32", 8), ("vocab_verify", 8),
+        ("batched_vocab", 64), ("gate_up", 16)]
+
+
+@pytest.fixture(scope="module")
+def full_cfgs():
+    return {}
+
+
+@pytest.mark.parametrize("name,M", FULL)
+def test_full_size_sampled_columns(vqv, full_cfgs, name, M):
+    if name not in full_cfgs:
+        full_cfgs.clear()  # keep one large workload in host memory at a time
+        full_cfgs[name] = gen.make_config(name)
+    c = full_cfgs[name]
+    y = run(vqv, c, M=M)
+    N = c["N"]
+    rng = np.random.default_rng(99)
+    cols = np.unique(np.concatenate([[0, 1, 15, 16, N // 2, N - 2, N - 1],
+                                     rng.integers(0, N, size=1024)]))
+    ref = qgemm_ref(c["x"][:M], c["act"], c["wq"], c["scales"], c["biases"], cols=cols)
+    worst = assert_close(y[:, cols], ref, c["act"], f"{name} M={M}")
+    print(f"{name} M={M}: worst error/allowance {worst:.3g}")
+    if c.get("real_rows"):
+        assert np.all(y[c["real_rows"]:] == 0.0)

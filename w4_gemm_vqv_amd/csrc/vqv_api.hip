@@ -1,0 +1,112 @@
+// C-ABI entry points of libvqv: argument checks on the host, then one launch
+// sequence on the caller's stream. Nothing is allocated or kept between calls.
+
+#include <stdint.h>
+
+#include "../../include/vqv.h"
+#include "vqv_internal.h"
+
+namespace {
+
+constexpr int kGroup = 64;
+constexpr int kMaxRows = 64;
+constexpr int kMaxBlock = 64;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return na && nb && a0 < b0 + nb && b0 < a0 + na;
+}
+
+int act_size(vqv_dtype a) { return a == VQV_FP32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+int vqv_abi_version(void) { return VQV_ABI_VERSION; }
+
+const char* vqv_status_string(vqv_status s) {
+  switch (s) {
+    case VQV_OK: return "ok";
+    case VQV_ERR_ARG: return "invalid argument (null pointer, size out of range or aliasing)";
+    case VQV_ERR_UNSUPPORTED: return "unsupported request (e.g. group size other than 64)";
+    case VQV_ERR_ALIGN: return "pointer alignment requirement not met";
+    case VQV_ERR_WORKSPACE: return "workspace missing or too small";
+    case VQV_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+size_t vqv_qgemm_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype) {
+  (void)M; (void)K; (void)N; (void)group; (void)act_dtype;
+  return 0;  // partial sums are reduced on chip
+}
+
+vqv_status vqv_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
+                     const uint16_t* biases, float* y, int M, int K, int N, int group,
+                     vqv_dtype act_dtype, void* workspace, size_t workspace_bytes,
+                     void* hip_stream) {
+  (void)workspace;
+  if (!x || !wq || !scales || !biases || !y) return VQV_ERR_ARG;
+  if (act_dtype != VQV_BF16 && act_dtype != VQV_FP16 && act_dtype != VQV_FP32)
+    return VQV_ERR_ARG;
+  if (M < 1 || M > kMaxRows || N < 1 || K < kGroup) return VQV_ERR_ARG;
+  if (group != kGroup) return VQV_ERR_UNSUPPORTED;
+  if (K % kGroup) return VQV_ERR_ARG;
+  const size_t esz = (size_t)act_size(act_dtype);
+  const size_t xbytes = (size_t)M * K * esz;
+  const size_t wbytes = (size_t)N * (K / 2);
+  const size_t sbytes = (size_t)N * (K / kGroup) * 2;
+  const size_t ybytes = (size_t)M * N * 4;
+  if (xbytes >= (1ull << 31) || wbytes >= (1ull << 32) || (size_t)N * (K / kGroup) >= (1ull << 31))
+    return VQV_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(scales, 2) || !aligned(biases, 2) ||
+      !aligned(y, 4))
+    return VQV_ERR_ALIGN;
+  if (overlaps(y, ybytes, x, xbytes) || overlaps(y, ybytes, wq, wbytes) ||
+      overlaps(y, ybytes, scales, sbytes) || overlaps(y, ybytes, biases, sbytes))
+    return VQV_ERR_ARG;
+  if (workspace_bytes < vqv_qgemm_workspace_bytes(M, K, N, group, act_dtype))
+    return VQV_ERR_WORKSPACE;
+  (void)hipGetLastError();  // start from a clean error state
+  const hipError_t e = vqv::launch_qgemm(x, wq, scales, biases, y, M, K, N, (int)act_dtype,
+                                         static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? VQV_OK : VQV_ERR_HIP;
+}
+
+size_t vqv_verify_workspace_bytes(int B, int T, int N) {
+  if (B < 1 || T < 1 || N < 1) return 0;
+  return (size_t)B * T * vqv::verify_chunks(N) * 8;
+}
+
+vqv_status vqv_verify(const float* logits, const int32_t* draft, int B, int T, int N,
+                      int32_t* argmax, int32_t* accept_len, void* workspace,
+                      size_t workspace_bytes, void* hip_stream) {
+  if (!logits || !argmax || !accept_len) return VQV_ERR_ARG;
+  if (B < 1 || T < 1 || T > kMaxBlock || N < 1) return VQV_ERR_ARG;
+  if (T > 1 && !draft) return VQV_ERR_ARG;
+  const size_t rows = (size_t)B * T;
+  if (rows * (size_t)N >= (1ull << 31)) return VQV_ERR_ARG;
+  if (!aligned(logits, 16) || !aligned(argmax, 4) || !aligned(accept_len, 4) ||
+      (draft && !aligned(draft, 4)))
+    return VQV_ERR_ALIGN;
+  const size_t lbytes = rows * N * 4;
+  if (overlaps(argmax, rows * 4, logits, lbytes) || overlaps(accept_len, (size_t)B * 4, logits, lbytes) ||
+      overlaps(argmax, rows * 4, accept_len, (size_t)B * 4) ||
+      (draft && (overlaps(argmax, rows * 4, draft, (size_t)B * (T - 1) * 4) ||
+                 overlaps(accept_len, (size_t)B * 4, draft, (size_t)B * (T - 1) * 4))))
+    return VQV_ERR_ARG;
+  const size_t need = vqv_verify_workspace_bytes(B, T, N);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 8)) return VQV_ERR_WORKSPACE;
+  if (overlaps(workspace, need, logits, lbytes) || overlaps(workspace, need, argmax, rows * 4) ||
+      overlaps(workspace, need, accept_len, (size_t)B * 4))
+    return VQV_ERR_ARG;
+  (void)hipGetLastError();
+  const hipError_t e = vqv::launch_verify(logits, draft, B, T, N, argmax, accept_len, workspace,
+                                          static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? VQV_OK : VQV_ERR_HIP;
+}
+
+}  // extern "C"

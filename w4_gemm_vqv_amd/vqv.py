@@ -1,0 +1,137 @@
+"""Thin Python binding of libvqv (include/vqv.h) through ctypes.
+
+The functions carry the C names and only marshal arguments: tensor data
+pointers, sizes and the stream handle go to the library, which checks them
+and launches its HIP kernels. There is no other code path; if the library is
+missing the import of any call fails loudly.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvqv.so")
+
+VQV_BF16, VQV_FP16, VQV_FP32 = 0, 1, 2
+VQV_OK, VQV_ERR_ARG, VQV_ERR_UNSUPPORTED, VQV_ERR_ALIGN, VQV_ERR_WORKSPACE, VQV_ERR_HIP = range(6)
+EXPORTS = ("vqv_abi_version", "vqv_status_string", "vqv_qgemm_workspace_bytes", "vqv_qgemm",
+           "vqv_verify_workspace_bytes", "vqv_verify")
+
+_DTYPES = {torch.bfloat16: VQV_BF16, torch.float16: VQV_FP16, torch.float32: VQV_FP32}
+_lib = None
+
+
+class VqvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"vqv status {status}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libvqv (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m w4_gemm_vqv_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.vqv_abi_version.restype = i
+        L.vqv_abi_version.argtypes = []
+        L.vqv_status_string.restype = ctypes.c_char_p
+        L.vqv_status_string.argtypes = [i]
+        L.vqv_qgemm_workspace_bytes.restype = sz
+        L.vqv_qgemm_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.vqv_qgemm.restype = i
+        L.vqv_qgemm.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, sz, vp]
+        L.vqv_verify_workspace_bytes.restype = sz
+        L.vqv_verify_workspace_bytes.argtypes = [i, i, i]
+        L.vqv_verify.restype = i
+        L.vqv_verify.argtypes = [vp, vp, i, i, i, vp, vp, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != VQV_OK:
+        raise VqvError(status, lib().vqv_status_string(status).decode())
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    return t.data_ptr()
+
+
+def vqv_abi_version() -> int:
+    return lib().vqv_abi_version()
+
+
+def vqv_status_string(status: int) -> str:
+    return lib().vqv_status_string(status).decode()
+
+
+def vqv_qgemm_workspace_bytes(M: int, K: int, N: int, group: int = 64,
+                              act_dtype: int = VQV_BF16) -> int:
+    return lib().vqv_qgemm_workspace_bytes(M, K, N, group, act_dtype)
+
+
+def vqv_qgemm(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,
+              y: torch.Tensor | None = None, group: int = 64,
+              workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y[M,N] fp32 = x[M,K] . W^T with W given as packed codes [N,K/2] uint8 and
+    fp16 scales/biases [N,K/group] (float16, or int16 bit patterns)."""
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported activation dtype {x.dtype}")
+    M, K = x.shape
+    N = wq.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    act = _DTYPES[x.dtype]
+    need = vqv_qgemm_workspace_bytes(M, K, N, group, act)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().vqv_qgemm(_dev(x, "x"), _dev(wq, "wq"), _dev(scales, "scales"),
+                           _dev(biases, "biases"), _dev(y, "y"), M, K, N, group, act,
+                           ws_ptr, ws_bytes, _stream_handle(stream)))
+    return y
+
+
+def vqv_verify_workspace_bytes(B: int, T: int, N: int) -> int:
+    return lib().vqv_verify_workspace_bytes(B, T, N)
+
+
+def vqv_verify(logits: torch.Tensor, draft: torch.Tensor | None, B: int, T: int,
+               argmax: torch.Tensor | None = None, accept_len: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, stream=None):
+    """(argmax [B*T] int32, accept_len [B] int32) of fp32 logits [B*T, N]
+    against int32 drafts [B, T-1]."""
+    N = logits.shape[-1]
+    dev = logits.device
+    if argmax is None:
+        argmax = torch.empty(B * T, dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(vqv_verify_workspace_bytes(B, T, N), 8), dtype=torch.uint8,
+                                device=dev)
+    dptr = _dev(draft, "draft") if (draft is not None and draft.numel()) else None
+    _check(lib().vqv_verify(_dev(logits, "logits"), dptr, B, T, N, _dev(argmax, "argmax"),
+                            _dev(accept_len, "accept_len"), _dev(workspace, "workspace"),
+                            workspace.numel() * workspace.element_size(),
+                            _stream_handle(stream)))
+    return argmax, accept_len
