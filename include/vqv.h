@@ -86,7 +86,8 @@ const char* vqv_status_string(vqv_status s);
  *   y          [M, N] fp32, written. 4-byte aligned. Must not overlap any
  *              input (VQV_ERR_ARG).
  *   M          1..64 verify rows (a block of 8 or 16, up to 64 batched).
- *   K          multiple of 64, >= 64; M*K*sizeof(act) < 2^31.
+ *   K          multiple of 64, 64 <= K <= 16384 (larger K returns
+ *              VQV_ERR_UNSUPPORTED); M*K*sizeof(act) < 2^31.
  *   N          >= 1 output columns; any N (tails are masked).
  *   group      must be 64 (else VQV_ERR_UNSUPPORTED).
  *   act_dtype  a vqv_dtype (else VQV_ERR_ARG).

@@ -79,7 +79,7 @@ def q(L, x=X, wq=W, s=S, b=B_, y=Y, M=8, K=512, N=1024, group=64, act=BF16, ws=N
     (dict(K=32), ARG), (dict(K=100), ARG), (dict(group=32), UNSUP), (dict(group=128), UNSUP),
     (dict(act=3), ARG), (dict(act=-1), ARG), (dict(x=X + 8), ALIGN), (dict(wq=W + 4), ALIGN),
     (dict(s=S + 1), ALIGN), (dict(y=Y + 2), ALIGN), (dict(y=X), ARG), (dict(y=W + 64), ARG),
-    (dict(y=S), ARG), (dict(M=64, K=64 * 2 ** 20, act=FP32), UNSUP),
+    (dict(y=S), ARG), (dict(M=64, K=64 * 2 ** 20, act=FP32), UNSUP), (dict(K=16384 + 64), UNSUP),
 ])
 def test_qgemm_rejects(L, kw, status):
     assert q(L, **kw) == status

@@ -44,7 +44,8 @@ def case(M, K, N, act, seed, sigma=1.0, real_rows=None):
 SHAPES = [
     (8, 512, 1024), (8, 64, 3), (1, 128, 17), (4, 192, 65), (5, 320, 1000), (8, 1088, 129),
     (3, 5120, 200), (9, 256, 70), (16, 640, 300), (17, 128, 64), (32, 256, 96), (33, 384, 50),
-    (64, 512, 130), (7, 4096, 64), (8, 8192, 77),
+    (64, 512, 130), (7, 4096, 64), (8, 8192, 77), (8, 16384, 40), (16, 16320, 33),
+    (64, 2560, 96), (5, 5120, 1000),
 ]
 
 

@@ -13,11 +13,10 @@
 // value is exact, and so is its product with a bf16 or fp16 activation in the
 // fp32 MFMA accumulator. Rounding the dequantized weight s*q + b to 16 bits
 // instead would cost far more than the 1e-3 contract. Per group the kernel
-// forms acc' = sum x*(c0+q) and xs = sum x (an MFMA against ones) and applies
-//     y += s*acc' + (b - c0*s)*xs
-// in fp32, which equals s*sum(x*q) + b*sum(x) up to fp32 rounding. fp32
-// activations (the W4A32 draft path) are split exactly into three bf16
-// terms, hi + mid + lo, each multiplied separately.
+// forms acc' = sum x*(c0+q) on MFMA and applies, in fp32,
+//     y += s*acc' + (b - c0*s)*xs,    xs = sum_{k in g} x,
+// which equals s*sum(x*q) + b*sum(x) up to fp32 rounding. fp32 activations
+// (the W4A32 draft path) are split exactly into three bf16 terms hi+mid+lo.
 //
 // Row-split MFMA layout (8 activation rows per row set). v_mfma_f32_16x16x32
 // has 16 A rows; rows 0-7 carry the 8 activation rows against group g0 = 2p
@@ -26,19 +25,28 @@
 // when (i < 8) == (h < 2). Lane (column j = lane%16, slot h) of B reads 16
 // contiguous bytes of its column, bytes [16h, 16h+16) of the 64-byte group
 // pair p, i.e. 32 codes of group 2p + h/2; dword t of that load feeds MFMA t.
-// Unpacking a dword yields the element order (k0,k4),(k1,k5),(k2,k6),(k3,k7);
-// the activation operand is permuted to match with v_perm_b32.
+// Unpacking a dword yields the element order (k0,k4),(k1,k5),(k2,k6),(k3,k7).
 //
-// Work split. A work-group of WK waves owns 16*TILES columns over all of K;
-// wave w takes a contiguous range of group pairs and keeps fp32 partials in
-// registers. The partials of the two row-split halves are added across lanes
-// and those of the WK waves in LDS in a fixed order, so results are
-// deterministic. Weights, scales and biases stream through a two-stage
-// register ring (the next pair's loads are in flight while the current pair
-// is computed). All loads are buffer loads: a per-lane offset fixed for the
-// whole kernel plus a scalar offset per pair. Activations come from L2; A
-// lanes that must supply zeros use an out-of-range offset, which the buffer
-// unit returns as 0.
+// Work split. A work-group has WN x WK waves and owns `cols` <= 16*TILES*WN
+// columns over all of K (the host sizes `cols` so that narrow problems give
+// every CU the same share). Wave (wn, wk) owns TILES column tiles and the
+// wk-th of WK contiguous ranges of S = ceil(GP/WK) group pairs ("steps"). The
+// two row-split halves are added across lanes and the WK partial sums of an
+// output in LDS in a fixed order, so results are deterministic.
+//
+// Memory. Only the weight codes stream from HBM in the K loop, through a
+// register ring D steps deep, issued with buffer loads (per-lane offset fixed,
+// pair offset scalar). The loop body has no data-dependent branches and, with
+// XALL, no barriers: steps past the end read zeros (an out-of-range weight
+// offset, a zero activation image, a zero scale/bias pad entry) and add
+// exactly nothing. The work-group's scale and bias rows (one contiguous block
+// each) are loaded once at the start and kept in LDS as (s, b) fp16 pairs.
+// Activations are staged into LDS permuted into the unpack order, with a zero
+// slot that the idle A lanes read and the per-group sums xs computed on the
+// way: with XALL the whole K range of the work-group once before the loop,
+// otherwise KC steps at a time, double buffered, each chunk's loads issued
+// with the weights of its first step so that storing it never drains the
+// ring.
 
 #include "vqv_internal.h"
 
@@ -57,21 +65,18 @@ template <int ACT> struct ActTraits;
 template <> struct ActTraits<ACT_BF16> {
   static constexpr unsigned magic = 0x43004300u;  // bf16 pair (128, 128)
   static constexpr float c0 = 128.0f;
-  static constexpr unsigned ones = 0x3F803F80u;   // bf16 pair (1, 1)
   static constexpr int esz = 2, parts = 1;
   static constexpr bool f16 = false;
 };
 template <> struct ActTraits<ACT_FP16> {
   static constexpr unsigned magic = 0x64006400u;  // fp16 pair (1024, 1024)
   static constexpr float c0 = 1024.0f;
-  static constexpr unsigned ones = 0x3C003C00u;   // fp16 pair (1, 1)
   static constexpr int esz = 2, parts = 1;
   static constexpr bool f16 = true;
 };
 template <> struct ActTraits<ACT_FP32> {           // three bf16 terms per value
   static constexpr unsigned magic = 0x43004300u;
   static constexpr float c0 = 128.0f;
-  static constexpr unsigned ones = 0x3F803F80u;
   static constexpr int esz = 4, parts = 3;
   static constexpr bool f16 = false;
 };
@@ -126,75 +131,258 @@ __device__ __forceinline__ void split3(unsigned f, unsigned& hi, unsigned& mid, 
   lo = __float_as_uint(r1 - __uint_as_float(mid)) & 0xFFFF0000u;
 }
 
-__device__ __forceinline__ float half_bits_to_float(unsigned v) {
+__device__ __forceinline__ float half_lo(unsigned v) {
   return (float)__builtin_bit_cast(_Float16, (unsigned short)(v & 0xFFFFu));
 }
+__device__ __forceinline__ float half_hi(unsigned v) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(v >> 16));
+}
 
-// Weights, scale and bias of one group pair for every tile of the wave.
-template <int TILES>
-struct Stage {
-  u32x4 w[TILES];
-  unsigned s[TILES], b[TILES];
+template <int ACT>
+__device__ __forceinline__ float act16_to_float(unsigned bits16) {
+  if constexpr (ACT == ACT_FP16) return half_lo(bits16);
+  else return __uint_as_float(bits16 << 16);
+}
+
+// LDS image of the activations for one step, row set and term: four t-rows
+// (one per MFMA step) of 32 A slots of 16 bytes plus one zero slot.
+constexpr int kSlotBytes = 16;
+constexpr int kTRowBytes = 33 * kSlotBytes;
+constexpr int kPairBytes = 4 * kTRowBytes;
+
+// Dynamic LDS of one work-group. XALL: one activation image per (range, step,
+// row set, term) plus one zero image; otherwise two chunk buffers of KC
+// steps. Then the row sums (likewise, 16 floats per image group) and the
+// (s, b) table, G + 4 dwords per column (the 4 pad entries are zero).
+struct LdsLayout {
+  int xl, xs, sb, total, sbs, zimg, zxs;
 };
 
-// ODDG: K/64 is odd, so the last pair has no second group and the scale and
-// bias rows are not dword aligned; that path reads them 16 bits at a time.
-template <int ACT, int R, int TILES, int WK, bool ODDG>
-__global__ __launch_bounds__(64 * WK) void qgemm_rowsplit(
+template <int R, int P, int WK, int KC, int WGC, bool XALL>
+__host__ __device__ inline LdsLayout lds_layout(int G) {
+  LdsLayout L{};
+  const int GP = (G + 1) >> 1;
+  const int S = (GP + WK - 1) / WK;
+  const int nimg = XALL ? WK * S * R * P + 1 : 2 * WK * KC * R * P;
+  const int nxs = XALL ? WK * S * R + 1 : 2 * WK * KC * R;
+  L.xl = 0;
+  L.zimg = XALL ? WK * S * R * P : 0;      // index of the zero image (XALL)
+  L.xs = nimg * kPairBytes;
+  L.zxs = XALL ? WK * S * R : 0;           // index of the zero row-sum group (XALL)
+  L.sb = L.xs + nxs * 16 * 4;
+  L.sbs = G + 4;
+  L.total = L.sb + WGC * L.sbs * 4;
+  return L;
+}
+
+template <int ACT, int R, int TILES, int WN, int WK, int D, int KC, bool XALL>
+__global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
-    float* __restrict__ y, int M, int K, int N) {
+    float* __restrict__ y, int M, int K, int N, int cols) {
   using TR = ActTraits<ACT>;
   constexpr int P = TR::parts;
-  constexpr int COLS = 16 * TILES;
+  constexpr int NT = 64 * WN * WK;                  // threads
+  constexpr int WCOLS = 16 * TILES;                 // columns per wave
+  constexpr int WGC = WN * WCOLS;                   // column slots per work-group
+  constexpr int NS = XALL ? 1 : D / KC;             // staging register sets in flight
+  constexpr int XBLK = WK * R * 8 * KC * 16;        // activation blocks per chunk
+  constexpr int BPT = XALL ? 4 : (XBLK + NT - 1) / NT;
+  constexpr int VPB = TR::esz == 4 ? 2 : 1;         // 16-byte loads per block
+  constexpr int SBU = 4;                            // scale/bias units per thread per round
+  static_assert(XALL || D % KC == 0, "ring depth must hold whole chunks");
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % WN;                          // column slice of this wave
+  const int wk = wave / WN;                          // K range of this wave
   const int j = lane & 15;       // B/C column, A row
   const int h = lane >> 4;       // k slot
   const int half = h >> 1;       // 0: group 2p, 1: group 2p+1
   const int G = K >> 6;
   const int GP = (G + 1) >> 1;
-  const int p0 = (wave * GP) / WK;
-  const int p1 = ((wave + 1) * GP) / WK;
-  const int col0 = blockIdx.x * COLS;
-  const int ncols = min(COLS, N - col0);
+  const int S = (GP + WK - 1) / WK;                  // steps per K range
+  const bool oddg = (G & 1) != 0;
   const unsigned rowbytes = (unsigned)K >> 1;
+  const LdsLayout L = lds_layout<R, P, WK, KC, WGC, XALL>(G);
+  unsigned char* xl = lds + L.xl;
+  float* xsl = reinterpret_cast<float*>(lds + L.xs);
+  unsigned* sbl = reinterpret_cast<unsigned*>(lds + L.sb);
 
-  // The code-to-float magic lives in a VGPR so that unpack_codes maps onto
-  // v_and_or_b32 (gfx9 VOP3 takes no literal and one scalar operand).
-  unsigned magic;
+  // Columns: the work-group owns [wg0, wg0 + wgcols). Buffer descriptors
+  // depend on the work-group only (they must be scalar). Tail lanes re-read
+  // the group's last column and never store.
+  const int wg0 = blockIdx.x * cols;
+  const int wgcols = min(cols, N - wg0);
+  const int wcol = wn * WCOLS;                       // first column of this wave in the group
+
+  unsigned magic;  // in a VGPR so that unpack_codes maps onto v_and_or_b32
   asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(TR::magic));
-  u32x4 ones;
-  ones.x = ones.y = ones.z = ones.w = TR::ones;
 
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(wq) + (size_t)col0 * rowbytes, (short)0, ncols * rowbytes, kBufferFlags);
+      const_cast<uint8_t*>(wq) + (size_t)wg0 * rowbytes, (short)0, wgcols * rowbytes,
+      kBufferFlags);
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(scales) + (size_t)col0 * G, (short)0, ncols * G * 2, kBufferFlags);
+      const_cast<uint16_t*>(scales) + (size_t)wg0 * G, (short)0, wgcols * G * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(biases) + (size_t)col0 * G, (short)0, ncols * G * 2, kBufferFlags);
+      const_cast<uint16_t*>(biases) + (size_t)wg0 * G, (short)0, wgcols * G * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(x), (short)0, M * K * TR::esz, kBufferFlags);
 
-  // Per-lane offsets, constant over the K loop. Tail columns re-read the last
-  // valid column and are never stored.
-  unsigned woff[TILES], soff[TILES];
+  unsigned woff[TILES];
 #pragma unroll
   for (int t = 0; t < TILES; ++t) {
-    const unsigned n = (unsigned)min(16 * t + j, ncols - 1);
+    const unsigned n = (unsigned)min(wcol + 16 * t + j, wgcols - 1);
     woff[t] = n * rowbytes + 16u * h;
-    soff[t] = ODDG ? (n * G + half) * 2u : n * G * 2u;
   }
-  const bool a_lane = ((j < 8) == (h < 2));   // A row j pairs with this lane's group
-  unsigned xoff[R];
+  const bool a_lane = ((j < 8) == (h < 2));          // A row j meets this lane's group
+  const int aslot = a_lane ? (h * 8 + (j & 7)) : 32; // the zero slot for idle lanes
+
+  // ---- scale/bias table: issued first, written to LDS after the prologue.
+  // Vector path (K/64 a multiple of 8, 16-byte aligned bases): 16-byte units
+  // of the work-group's contiguous block; otherwise 16-bit loads.
+  const bool sb_vec = (G % 8) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
+                                        reinterpret_cast<uintptr_t>(biases)) & 15) == 0;
+  const int sb_units = sb_vec ? wgcols * G / 8 : wgcols * G;
+  u32x4 sbs[SBU], sbb[SBU];
+  auto sb_load = [&](int round) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int m = 8 * r + (j & 7);
-    xoff[r] = (a_lane && m < M) ? (unsigned)((m * K + 64 * half + 32 * (h & 1)) * TR::esz)
-                                : kOutOfRange;
-  }
-  const unsigned sshift = ODDG ? 0u : 16u * half;   // which fp16 of the pair's dword
+    for (int u = 0; u < SBU; ++u) {
+      const int i = (round * SBU + u) * NT + tid;
+      if (sb_vec) {
+        const unsigned off = i < sb_units ? 16u * i : kOutOfRange;
+        sbs[u] = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
+        sbb[u] = __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0);
+      } else {
+        const unsigned off = i < sb_units ? 2u * i : kOutOfRange;
+        sbs[u].x = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
+        sbb[u].x = __builtin_amdgcn_raw_buffer_load_b16(br, off, 0, 0);
+      }
+    }
+  };
+  auto sb_store = [&](int round) {
+#pragma unroll
+    for (int u = 0; u < SBU; ++u) {
+      const int i = (round * SBU + u) * NT + tid;
+      if (i < sb_units) {
+        if (sb_vec) {
+          const int e0 = 8 * i;                       // first element of the unit
+          const int n = e0 / G, g = e0 - n * G;
+          u32x4 lo, hi;                               // (s_g | b_g << 16) for g .. g+7
+          lo.x = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x05040100u);
+          lo.y = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x07060302u);
+          lo.z = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x05040100u);
+          lo.w = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x07060302u);
+          hi.x = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x05040100u);
+          hi.y = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x07060302u);
+          hi.z = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x05040100u);
+          hi.w = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x07060302u);
+          *reinterpret_cast<u32x4*>(&sbl[n * L.sbs + g]) = lo;
+          *reinterpret_cast<u32x4*>(&sbl[n * L.sbs + g + 4]) = hi;
+        } else {
+          const int n = i / G, g = i - n * G;
+          sbl[n * L.sbs + g] = (sbs[u].x & 0xFFFFu) | (sbb[u].x << 16);
+        }
+      }
+    }
+  };
+
+  // ---- activation staging. A block is 8 consecutive k of one row. With
+  // XALL a "chunk" is the whole range (steps 0..S-1 of all WK ranges);
+  // otherwise chunk c holds steps [c*KC, c*KC + KC).
+  const int csteps = XALL ? S : KC;                  // steps per chunk
+  const int cblocks = WK * R * 8 * csteps * 16;       // blocks per chunk
+  u32x4 sreg[NS][BPT][VPB];
+  auto block_coords = [&](int bi, int& ks, int& mm, int& kb) {
+    ks = bi / (R * 8 * csteps * 16);                  // K range
+    const int rem = bi - ks * (R * 8 * csteps * 16);
+    mm = rem / (16 * csteps);                         // activation row 0..8R-1
+    kb = rem - mm * 16 * csteps;                      // 8-value block within the chunk
+  };
+  auto stage_load = [&](int c, int set, int base) {
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int bi = base + tid + i * NT;
+      int ks, mm, kb;
+      block_coords(bi, ks, mm, kb);
+      const int q = c * csteps + (kb >> 4);           // step within the range
+      const int p = ks * S + q;                       // group pair
+      const int k = 128 * p + 8 * (kb & 15);
+      const bool ok = bi < cblocks && mm < M && q < S && k < K;
+      const unsigned off = ok ? (unsigned)((mm * K + k) * TR::esz) : kOutOfRange;
+#pragma unroll
+      for (int v = 0; v < VPB; ++v)
+        sreg[set][i][v] = __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16 * v, 0, 0);
+    }
+  };
+  auto stage_store = [&](int set, int buf, int base) {
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int bi = base + tid + i * NT;
+      int ks, mm, kb;
+      block_coords(bi, ks, mm, kb);
+      const int pp = kb >> 4;                         // step within the chunk
+      const int r128 = 8 * (kb & 15);                 // offset within the pair's 128 k
+      const int hf = r128 >> 6, hh = (r128 >> 5) & 1, t = (r128 >> 3) & 3;
+      const int r = mm >> 3;
+      const int slot = (hf * 2 + hh) * 8 + (mm & 7);
+      // Sum of the block; the 8 blocks of one (row, group) are 8 adjacent lanes.
+      float s8 = 0.0f;
+      if constexpr (P == 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s8 += act16_to_float<ACT>(sreg[set][i][0][e] & 0xFFFFu);
+          s8 += act16_to_float<ACT>(sreg[set][i][0][e] >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s8 += __uint_as_float(sreg[set][i][v][e]);
+      }
+      s8 += __shfl_xor(s8, 1);
+      s8 += __shfl_xor(s8, 2);
+      s8 += __shfl_xor(s8, 4);
+      if (bi < cblocks) {
+        const int grp = ((buf * WK + ks) * csteps + pp) * R + r;   // (image group)
+        unsigned char* dst = xl + grp * P * kPairBytes + t * kTRowBytes + slot * kSlotBytes;
+        if constexpr (P == 1) {
+          *reinterpret_cast<u32x4*>(dst) = permute_pairs(sreg[set][i][0]);
+        } else {
+          u32x4 hi0, mi0, lo0, hi1, mi1, lo1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            unsigned a, b, cc;
+            split3(sreg[set][i][0][e], a, b, cc);
+            hi0[e] = a; mi0[e] = b; lo0[e] = cc;
+            split3(sreg[set][i][1][e], a, b, cc);
+            hi1[e] = a; mi1[e] = b; lo1[e] = cc;
+          }
+          *reinterpret_cast<u32x4*>(dst) = high_halves(hi0, hi1);
+          *reinterpret_cast<u32x4*>(dst + kPairBytes) = high_halves(mi0, mi1);
+          *reinterpret_cast<u32x4*>(dst + 2 * kPairBytes) = high_halves(lo0, lo1);
+        }
+        if ((bi & 7) == 0) xsl[(grp * 2 + hf) * 8 + (mm & 7)] = s8;
+      }
+    }
+  };
+
+  // ---- weight ring: step q of this wave is pair wk*S + q; out-of-range steps
+  // (past this range or past GP) read zeros.
+  u32x4 st[D][TILES];
+  auto load = [&](int q, u32x4 (&w)[TILES]) {
+    const int p = wk * S + q;
+    const bool in = q < S && p < GP;                 // uniform
+    const bool full = !oddg || (2 * p + 1 < G);
+    const unsigned wshift = full ? 0u : 32u * half;  // a missing g1 re-reads g0
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+      w[t] = __builtin_amdgcn_raw_buffer_load_b128(wr, in ? woff[t] - wshift : kOutOfRange,
+                                                   64 * (in ? p : 0), 0);
+  };
 
   float acc[R][TILES][4];
 #pragma unroll
@@ -204,101 +392,111 @@ __global__ __launch_bounds__(64 * WK) void qgemm_rowsplit(
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[r][t][e] = 0.0f;
 
-  auto load = [&](int p, Stage<TILES>& st) {
-    const bool full = !ODDG || (2 * p + 1 < G);   // uniform
-    // A missing second group re-reads the first (its products are discarded).
-    const unsigned wshift = full ? 0u : 32u * half;
-#pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      st.w[t] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff[t] - wshift, 64 * p, 0);
-      if constexpr (ODDG) {
-        const unsigned so = soff[t] - (full ? 0u : 2u * half);
-        st.s[t] = __builtin_amdgcn_raw_buffer_load_b16(sr, so, 4 * p, 0);
-        st.b[t] = __builtin_amdgcn_raw_buffer_load_b16(br, so, 4 * p, 0);
-      } else {
-        st.s[t] = __builtin_amdgcn_raw_buffer_load_b32(sr, soff[t], 4 * p, 0);
-        st.b[t] = __builtin_amdgcn_raw_buffer_load_b32(br, soff[t], 4 * p, 0);
-      }
-    }
-  };
-
-  auto compute = [&](int p, const Stage<TILES>& st) {
-    const bool full = !ODDG || (2 * p + 1 < G);   // uniform
-    const bool g_ok = full || half == 0;
+  // One step: A and xs from this step's image group (the zero group past the
+  // range), (s, b) of this lane's group (the zero pad entry past the range),
+  // four MFMAs per tile and row set, then acc += s*C + (b - c0*s)*xs.
+  auto compute = [&](int q, const u32x4 (&w)[TILES], int buf) {
+    const int p = wk * S + q;
+    const bool in = q < S;                            // uniform
+    const int grp0 = XALL ? (in ? (wk * S + q) * R : L.zxs) : ((buf * WK + wk) * KC + q % KC) * R;
+    const int sbi = in ? min(2 * p + half, G) : G;
     u32x4 bq[4][TILES];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int tt = 0; tt < TILES; ++tt) bq[t][tt] = unpack_codes(st.w[tt][t], magic);
+      for (int tt = 0; tt < TILES; ++tt) bq[t][tt] = unpack_codes(w[tt][t], magic);
     float sv[TILES], bb[TILES];
 #pragma unroll
     for (int tt = 0; tt < TILES; ++tt) {
-      sv[tt] = half_bits_to_float(st.s[tt] >> sshift);
-      bb[tt] = fmaf(-TR::c0, sv[tt], half_bits_to_float(st.b[tt] >> sshift));
-      if (!g_ok) { sv[tt] = 0.0f; bb[tt] = 0.0f; }
+      const unsigned v = sbl[(wcol + 16 * tt + j) * L.sbs + sbi];
+      sv[tt] = half_lo(v);
+      bb[tt] = fmaf(-TR::c0, sv[tt], half_hi(v));
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const unsigned xo = g_ok ? xoff[r] : kOutOfRange;
-      const int xs = 128 * TR::esz * p;
-      u32x4 A[4][P];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if constexpr (P == 1) {
-          A[t][0] = permute_pairs(__builtin_amdgcn_raw_buffer_load_b128(xr, xo + 16 * t, xs, 0));
-        } else {
-          const u32x4 f0 = __builtin_amdgcn_raw_buffer_load_b128(xr, xo + 32 * t, xs, 0);
-          const u32x4 f1 = __builtin_amdgcn_raw_buffer_load_b128(xr, xo + 32 * t + 16, xs, 0);
-          u32x4 hi0, mi0, lo0, hi1, mi1, lo1;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            unsigned a, b, c;
-            split3(f0[e], a, b, c);
-            hi0[e] = a; mi0[e] = b; lo0[e] = c;
-            split3(f1[e], a, b, c);
-            hi1[e] = a; mi1[e] = b; lo1[e] = c;
-          }
-          A[t][0] = high_halves(hi0, hi1);
-          A[t][1] = high_halves(mi0, mi1);
-          A[t][2] = high_halves(lo0, lo1);
-        }
-      }
-      f32x4 C[TILES], O;
+      const int grp = XALL && !in ? L.zxs : grp0 + r;
+      const int img = XALL && !in ? L.zimg : (grp0 + r) * P;
+      const unsigned char* ab = xl + img * kPairBytes + aslot * kSlotBytes;
+      const f32x4 xs = *reinterpret_cast<const f32x4*>(&xsl[(grp * 2 + half) * 8 + 4 * (h & 1)]);
+      f32x4 C[TILES];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int q = 0; q < P; ++q) {
-          const bool first = (t == 0) && (q == 0);
+        for (int u = 0; u < P; ++u) {
+          const unsigned char* ap = XALL && !in ? ab : ab + u * kPairBytes;
+          const u32x4 A = *reinterpret_cast<const u32x4*>(ap + t * kTRowBytes);
+          const bool first = (t == 0) && (u == 0);
           const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-          O = mfma16x16x32<TR::f16>(A[t][q], ones, first ? zero : O);
 #pragma unroll
           for (int tt = 0; tt < TILES; ++tt)
-            C[tt] = mfma16x16x32<TR::f16>(A[t][q], bq[t][tt], first ? zero : C[tt]);
+            C[tt] = mfma16x16x32<TR::f16>(A, bq[t][tt], first ? zero : C[tt]);
         }
-      // Group epilogue in fp32: acc += s*C + (b - c0*s)*O.
 #pragma unroll
       for (int tt = 0; tt < TILES; ++tt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          acc[r][tt][e] = fmaf(sv[tt], C[tt][e], fmaf(bb[tt], O[e], acc[r][tt][e]));
+          acc[r][tt][e] = fmaf(sv[tt], C[tt][e], fmaf(bb[tt], xs[e], acc[r][tt][e]));
     }
   };
 
-  // Two-stage ring: pair q+1 loads while pair q is computed.
-  Stage<TILES> s0, s1;
-  const int np = p1 - p0;
-  if (np > 0) load(p0, s0);
-  for (int q = 0; q < np; q += 2) {
-    if (q + 1 < np) load(p0 + q + 1, s1);
-    compute(p0 + q, s0);
-    if (q + 1 < np) {
-      if (q + 2 < np) load(p0 + q + 2, s0);
-      compute(p0 + q + 1, s1);
+  // ---- prologue: zero slots, zero image and pads, the scale/bias table, the
+  // first D steps of weights, the activations.
+  {
+    const int nimg = XALL ? L.zimg : 2 * WK * KC * R * P;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < nimg * 4; i += NT)
+      *reinterpret_cast<u32x4*>(xl + (i >> 2) * kPairBytes + (i & 3) * kTRowBytes +
+                                32 * kSlotBytes) = z;
+    if constexpr (XALL) {
+      for (int i = tid; i < kPairBytes / 16; i += NT)
+        *reinterpret_cast<u32x4*>(xl + L.zimg * kPairBytes + 16 * i) = z;
+      if (tid < 16) xsl[L.zxs * 16 + tid] = 0.0f;
+    }
+    for (int i = tid; i < WGC * 4; i += NT) sbl[(i >> 2) * L.sbs + G + (i & 3)] = 0u;
+  }
+  sb_load(0);
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    if constexpr (!XALL)
+      if (d % KC == 0) stage_load(d / KC, d / KC, 0);
+    load(d, st[d]);
+  }
+  if constexpr (XALL) {
+    for (int base = 0; base < cblocks; base += BPT * NT) {
+      stage_load(0, 0, base);
+      stage_store(0, 0, base);
+    }
+  }
+  sb_store(0);
+  for (int round = 1; round * SBU * NT < sb_units; ++round) {  // only for very wide tables
+    sb_load(round);
+    sb_store(round);
+  }
+  if constexpr (!XALL) stage_store(0, 0, 0);
+  __syncthreads();
+
+  // ---- main loop: straight-line body, D steps per iteration.
+  const int steps = (S + D - 1) / D * D;
+  for (int qb = 0; qb < steps; qb += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int q = qb + d;
+      compute(q, st[d], XALL ? 0 : (q / KC) & 1);
+      load(q + D, st[d]);
+      if constexpr (!XALL) {
+        if (d % KC == 0) stage_load((q + D) / KC, d / KC, 0);
+        if (d % KC == KC - 1) {
+          stage_store(((d + 1) / KC) % NS, ((q + 1) / KC) & 1, 0);
+          __syncthreads();
+        }
+      }
     }
   }
 
-  // Reduce: the two row-split halves (lanes l and l^32), then the WK waves.
-  __shared__ float red[WK][R][TILES][8][16];
+  // ---- reduce: the two row-split halves (lanes l and l^32), then the WK
+  // ranges in order, through LDS (reused once every wave is past the loop).
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);        // [WK][WN][R][TILES][8][16]
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -306,48 +504,97 @@ __global__ __launch_bounds__(64 * WK) void qgemm_rowsplit(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float v = acc[r][tt][e] + __shfl_xor(acc[r][tt][e], 32);
-        if (lane < 32) red[wave][r][tt][4 * (lane >> 4) + e][j] = v;
+        if (lane < 32)
+          red[((((wk * WN + wn) * R + r) * TILES + tt) * 8 + 4 * (lane >> 4) + e) * 16 + j] = v;
       }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < R * 8 * COLS; idx += 64 * WK) {
-    const int r = idx / (8 * COLS);
-    const int rem = idx - r * 8 * COLS;
-    const int m = rem / COLS;
-    const int c = rem - m * COLS;
+  constexpr int OUTS = WN * R * TILES * 128;
+  for (int idx = tid; idx < OUTS; idx += NT) {
     float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < WK; ++w) s += red[w][r][c >> 4][m][c & 15];
-    const int mg = 8 * r + m;
-    if (mg < M && c < ncols) y[(size_t)mg * N + col0 + c] = s;
+    for (int k2 = 0; k2 < WK; ++k2) s += red[k2 * OUTS + idx];
+    const int jj = idx & 15;
+    const int m8 = (idx >> 4) & 7;
+    const int rest = idx >> 7;                       // (wn * R + r) * TILES + tt
+    const int tt = rest % TILES;
+    const int r = (rest / TILES) % R;
+    const int wn2 = rest / (TILES * R);
+    const int m = 8 * r + m8;
+    const int c = wn2 * WCOLS + 16 * tt + jj;
+    if (m < M && c < wgcols) y[(size_t)m * N + wg0 + c] = s;
   }
 }
 
-template <int ACT, int R, int TILES, int WK>
-hipError_t launch_rowsplit(const void* x, const uint8_t* wq, const uint16_t* scales,
-                           const uint16_t* biases, float* y, int M, int K, int N,
-                           hipStream_t stream) {
-  const int cols = 16 * TILES;
+constexpr int kLdsLimit = 160 * 1024;
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  return cus;
+}
+
+template <int ACT, int R, int TILES, int WN, int WK, int D, int KC, bool XALL>
+int lds_bytes_for(int K) {
+  constexpr int WGC = 16 * TILES * WN;
+  const LdsLayout L = lds_layout<R, ActTraits<ACT>::parts, WK, KC, WGC, XALL>(K >> 6);
+  const int red_bytes = WK * WN * R * TILES * 128 * 4;
+  return L.total > red_bytes ? L.total : red_bytes;
+}
+
+template <int ACT, int R, int TILES, int WN, int WK, int D, int KC, bool XALL>
+hipError_t launch_w4(const void* x, const uint8_t* wq, const uint16_t* scales,
+                     const uint16_t* biases, float* y, int M, int K, int N, int cols,
+                     hipStream_t stream) {
+  const int lds_bytes = lds_bytes_for<ACT, R, TILES, WN, WK, D, KC, XALL>(K);
+  auto kern = qgemm_w4<ACT, R, TILES, WN, WK, D, KC, XALL>;
+  if (lds_bytes > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             lds_bytes);
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid((N + cols - 1) / cols);
-  if ((K >> 6) & 1)
-    hipLaunchKernelGGL((qgemm_rowsplit<ACT, R, TILES, WK, true>), grid, dim3(64 * WK), 0, stream,
-                       x, wq, scales, biases, y, M, K, N);
-  else
-    hipLaunchKernelGGL((qgemm_rowsplit<ACT, R, TILES, WK, false>), grid, dim3(64 * WK), 0,
-                       stream, x, wq, scales, biases, y, M, K, N);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * WN * WK), lds_bytes, stream, x, wq, scales, biases,
+                     y, M, K, N, cols);
   return hipGetLastError();
 }
 
+// Configuration per problem. M <= 8 (one row set): when the work-group's
+// whole activation range fits in LDS, the barrier-free XALL kernel; narrow N
+// is split into exactly one work-group per CU (columns rounded up to 4, up
+// to five waves of 16), wide N into 64-column groups.
 template <int ACT>
 hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                          const uint16_t* biases, float* y, int M, int K, int N,
                          hipStream_t s) {
-  // fp32 activations carry three operand terms, so they get fewer tiles.
-  constexpr int T4 = ACT == ACT_FP32 ? 2 : 4;
-  constexpr int T2 = ACT == ACT_FP32 ? 1 : 2;
-  if (M <= 8) return launch_rowsplit<ACT, 1, 4, 8>(x, wq, scales, biases, y, M, K, N, s);
-  if (M <= 16) return launch_rowsplit<ACT, 2, T4, 8>(x, wq, scales, biases, y, M, K, N, s);
-  if (M <= 32) return launch_rowsplit<ACT, 4, T2, 8>(x, wq, scales, biases, y, M, K, N, s);
-  return launch_rowsplit<ACT, 8, T2, 8>(x, wq, scales, biases, y, M, K, N, s);
+  if (M <= 8) {
+    const int cus = device_cus();
+    const int share = ((N + cus - 1) / cus + 3) / 4 * 4;
+    if (share > 48 && share <= 80 &&
+        lds_bytes_for<ACT, 1, 1, 5, 2, 8, 1, true>(K) <= kLdsLimit)
+      return launch_w4<ACT, 1, 1, 5, 2, 8, 1, true>(x, wq, scales, biases, y, M, K, N, share, s);
+    if (lds_bytes_for<ACT, 1, 1, 4, 2, 8, 1, true>(K) <= kLdsLimit)
+      return launch_w4<ACT, 1, 1, 4, 2, 8, 1, true>(x, wq, scales, biases, y, M, K, N, 64, s);
+    return launch_w4<ACT, 1, 1, 4, 2, 4, 2, false>(x, wq, scales, biases, y, M, K, N, 64, s);
+  }
+  // Several row sets: chunked staging; the smaller fallback (32 columns,
+  // one K range, one-step chunks) keeps fp32 at large K within LDS.
+  if (M <= 16) {
+    if (lds_bytes_for<ACT, 2, 1, 4, 2, 4, 2, false>(K) <= kLdsLimit)
+      return launch_w4<ACT, 2, 1, 4, 2, 4, 2, false>(x, wq, scales, biases, y, M, K, N, 64, s);
+    return launch_w4<ACT, 2, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, s);
+  }
+  if (M <= 32) {
+    if (lds_bytes_for<ACT, 4, 1, 4, 1, 4, 1, false>(K) <= kLdsLimit)
+      return launch_w4<ACT, 4, 1, 4, 1, 4, 1, false>(x, wq, scales, biases, y, M, K, N, 64, s);
+    return launch_w4<ACT, 4, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, s);
+  }
+  if (lds_bytes_for<ACT, 8, 1, 4, 1, 2, 1, false>(K) <= kLdsLimit)
+    return launch_w4<ACT, 8, 1, 4, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 64, s);
+  return launch_w4<ACT, 8, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, s);
 }
 
 }  // namespace

@@ -55,6 +55,7 @@ vqv_status vqv_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
   if (M < 1 || M > kMaxRows || N < 1 || K < kGroup) return VQV_ERR_ARG;
   if (group != kGroup) return VQV_ERR_UNSUPPORTED;
   if (K % kGroup) return VQV_ERR_ARG;
+  if (K > vqv::kMaxK) return VQV_ERR_UNSUPPORTED;
   const size_t esz = (size_t)act_size(act_dtype);
   const size_t xbytes = (size_t)M * K * esz;
   const size_t wbytes = (size_t)N * (K / 2);

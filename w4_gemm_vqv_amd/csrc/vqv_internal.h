@@ -10,7 +10,10 @@ namespace vqv {
 
 enum ActKind { ACT_BF16 = 0, ACT_FP16 = 1, ACT_FP32 = 2 };
 
-// y[M,N] = x[M,K] . W^T for 1 <= M <= 64, K % 64 == 0, group 64.
+// Largest K: a work-group keeps its columns' scale/bias rows in LDS.
+constexpr int kMaxK = 16384;
+
+// y[M,N] = x[M,K] . W^T for 1 <= M <= 64, 64 <= K <= kMaxK, K % 64 == 0, group 64.
 hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
                         const uint16_t* biases, float* y, int M, int K, int N, int act,
                         hipStream_t stream);
