@@ -9,11 +9,17 @@ seeded synthetic tensors of that shape, resident in HBM before timing. The
 weights rotate through enough copies that every step streams them from HBM
 rather than from the 256 MB Infinity Cache.
 
-Prints one JSON line. `value` is verified rows per second (M rows per step);
-`roofline` reports the QMM kernel's algorithmic bytes per launch divided by
-its mean launch time (HIP events around each launch on the launch stream)
-against the 8 TB/s HBM peak; `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.
+Prints one JSON line. `value` is verified rows per second (M rows per step),
+timed over the K steps captured as one HIP graph, so the host's launch cost
+stays out of the measurement (the eagerly launched rate is reported beside
+it). `roofline` reports the QMM kernel's algorithmic bytes per launch divided
+by its mean launch time (HIP events around a graph of back-to-back QMM
+launches, on the stream they run on) against the 8 TB/s HBM peak;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+
+Two further modes serve rocprofv3 counter runs: `--counter-pass` launches the
+QMM and a copy kernel of known size eagerly, and `--write-traffic` turns a
+FETCH_SIZE run and a WRITE_SIZE run of it into per-launch HBM bytes.
 """
 
 from __future__ import annotations
@@ -33,6 +39,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "verified rows/s + achieved HBM GB/s, W4 M=8 QMM K=5120 N=17408"
 MALL_BYTES = 256 << 20
+COPY_PROBE_BYTES = 1 << 30
+QMM_LAUNCHES = 240
 
 # workload -> (verify block T, sequences B) for the steps that include verify
 VERIFY = {"tiny": (8, 1), "target": (8, 1), "vocab_verify": (8, 1), "batched_vocab": (16, 4)}
@@ -98,6 +106,62 @@ def cpu_baseline(c, M, T, B, budget_s):
             "seconds_per_step": t_q + t_v}
 
 
+def _counter_rows(run_dir):
+    """(kernel name, counter, value) rows of one rocprofv3 --pmc run, from its
+    CSV output or its SQLite database."""
+    import csv
+    import glob
+    import sqlite3
+    rows = []
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    if rows:
+        return rows
+    for path in glob.glob(os.path.join(run_dir, "**", "*_results.db"), recursive=True):
+        db = sqlite3.connect(path)
+        rows += db.execute("select kernel_name, counter_name, value from counters_collection"
+                           ).fetchall()
+    if not rows:
+        raise SystemExit(f"no counter records under {run_dir}")
+    return rows
+
+
+def write_traffic(fetch_dir, write_dir, workload, M):
+    """Per-launch HBM bytes of the QMM from a FETCH_SIZE pass and a WRITE_SIZE
+    pass of `bench.py --counter-pass`, each scaled by what the same counter
+    reads for the copy kernel (COPY_PROBE_BYTES read and written per launch)."""
+    out = {}
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        q, cp = [], []
+        for kname, cname, v in _counter_rows(run_dir):
+            if cname != counter:
+                continue
+            if "qgemm_w4" in kname:
+                q.append(v)
+            elif "neg" in kname.lower():
+                cp.append(v)
+        if not q or not cp:
+            raise SystemExit(f"{counter}: no QMM or copy dispatches under {run_dir}")
+        half = len(q) // 2  # the second sweep over the weight copies
+        q_kib = statistics.fmean(q[half:])
+        per_byte = statistics.fmean(cp) * 1024 / COPY_PROBE_BYTES
+        key = "fetch" if counter == "FETCH_SIZE" else "write"
+        out[f"{key}_bytes"] = q_kib * 1024 / per_byte
+        out[f"{key}_counter_kib"] = q_kib
+        out[f"{key}_copy_calibration"] = per_byte
+        out[f"{key}_dispatches"] = len(q) - half
+    path = os.path.join(ROOT, "profiles", "qgemm_traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    src = open(os.path.join(ROOT, "w4_gemm_vqv_amd", "csrc", "qgemm.hip"), "rb").read()
+    sha = hashlib.sha256(src).hexdigest()
+    if rec.get("qgemm_hip_sha256") != sha:
+        rec = {"qgemm_hip_sha256": sha, "workloads": {}}
+    rec["workloads"][f"{workload}:M={M}"] = out
+    json.dump(rec, open(path, "w"), indent=1, sort_keys=True)
+    print(json.dumps({f"{workload}:M={M}": out}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,7 +174,16 @@ def main():
     ap.add_argument("--rotate", type=int, default=None, help="weight copies cycled per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="eager QMM launches + a copy kernel, for one rocprofv3 --pmc pass")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarize two --counter-pass runs into profiles/qgemm_traffic.json")
     args = ap.parse_args()
+    if args.write_traffic:
+        import gen
+        write_traffic(*args.write_traffic, args.workload,
+                      args.m or gen.CONFIGS[args.workload]["M"])
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -164,41 +237,88 @@ def main():
                           device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i, evs=None):
+    def qmm(i, st):
         xc, wc, sc, bc = copies[i % R]
-        if evs:
-            evs[0].record(stream)
-        vqv.vqv_qgemm(xc, wc, sc, bc, y=y, stream=stream)
-        if evs:
-            evs[1].record(stream)
+        vqv.vqv_qgemm(xc, wc, sc, bc, y=y, stream=st)
+
+    def ver(st):
+        vqv.vqv_verify(y, draft if T > 1 else None, B, T, argmax=am, accept_len=al,
+                       workspace=vws, stream=st)
+
+    def step(i, st):
+        qmm(i, st)
         if T:
-            vqv.vqv_verify(y, draft if T > 1 else None, B, T, argmax=am, accept_len=al,
-                           workspace=vws, stream=stream)
-            if evs:
-                evs[2].record(stream)
+            ver(st)
+
+    if args.counter_pass:
+        # Eager launches for rocprofv3 --pmc (one counter pass per run): the
+        # QMM over every weight copy twice, then a plain copy kernel of known
+        # size whose counter reading calibrates bytes per counted unit.
+        for i in range(2 * R):
+            qmm(i, stream)
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"counter pass done: {2 * R} QMM launches, 3 copy launches of "
+            f"{COPY_PROBE_BYTES} bytes each way")
+        return
+
+    def graph_of(fn, n):
+        """HIP graph of n launches of fn(i, stream); launch overhead of the
+        Python binding stays out of the timed region."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream()
+            for i in range(n):
+                fn(i, cs)
+        return g
+
+    def timed(g, reps=1):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
 
     for i in range(args.warmup):
-        step(i)
+        step(i, stream)
     torch.cuda.synchronize()
 
-    # Whole-step throughput: K steps between two events, nothing else queued.
+    # Whole-step throughput: the K steps as one graph, replayed once untimed
+    # (upload) and once timed, with nothing else queued.
+    g_steps = graph_of(step, args.steps)
+    g_steps.replay()
+    ms_step = timed(g_steps) / args.steps
+
+    # The same K steps launched one by one from Python, for reference.
+    torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for i in range(args.steps):
-        step(i)
+        step(i, stream)
     t1.record(stream)
     torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
+    ms_eager = t0.elapsed_time(t1) / args.steps
 
-    # Per-launch durations: events around each launch, on the launch stream.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    q_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
-    v_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs] if T else [0.0]
-    q_mean = statistics.fmean(q_us)
+    # Per-launch durations: back-to-back launches of one kernel in a graph,
+    # HIP events around the replays on the stream the kernels run on.
+    nq = R * max(1, math.ceil(QMM_LAUNCHES / R))
+    g_q = graph_of(qmm, nq)
+    g_q.replay()
+    q_runs = [timed(g_q) * 1e3 / nq for _ in range(5)]
+    q_mean = statistics.fmean(q_runs)
+    v_runs = [0.0]
+    if T:
+        g_v = graph_of(lambda i, st: ver(st), QMM_LAUNCHES)
+        g_v.replay()
+        v_runs = [timed(g_v) * 1e3 / QMM_LAUNCHES for _ in range(5)]
 
     qb = qgemm_bytes(M, K, N, esz)
     achieved = qb / (q_mean * 1e-6) / 1e9
@@ -219,9 +339,10 @@ def main():
                                + (f"+ greedy verify B={B} T={T}" if T else "(no verify)"),
                    "M": M, "K": K, "N": N, "group": 64, "act": act, "verify_B": B,
                    "verify_T": T, "weight_copies": R},
+        "eager_ms_per_step": ms_eager,
         "qgemm_us_mean": q_mean,
-        "qgemm_us_median": statistics.median(q_us),
-        "verify_us_mean": statistics.fmean(v_us),
+        "qgemm_us_runs": q_runs,
+        "verify_us_mean": statistics.fmean(v_runs),
         "step_hbm_gbs": (qb + (4 * M * N if T else 0)) / (ms_step * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_record(args.workload, M),
