@@ -55,6 +55,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -525,6 +527,390 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
   }
 }
 
+
+// s_waitcnt immediate that waits until at most `vm` vector memory loads are
+// outstanding and leaves the other counters alone (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8).
+constexpr int vmcnt_wait(int vm) {
+  return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+// LDS of qgemm_w4_m8: GP activation images and one zero image, the row sums
+// (16 floats per image), the (s, b) table (G + 4 dwords per column), then the
+// partial-sum slots, two 8x16 tiles per wave, then each run's first and last
+// tile.
+struct M8Layout {
+  int xs, sb, sbs, red, runs, total;
+};
+
+__host__ __device__ inline M8Layout m8_layout(int G, int WGC, int NW) {
+  const int GP = (G + 1) >> 1;
+  M8Layout L{};
+  L.xs = (GP + 1) * kPairBytes;
+  L.sb = L.xs + (GP + 1) * 16 * 4;
+  L.sbs = G + 4;
+  L.red = L.sb + WGC * L.sbs * 4;
+  L.runs = L.red + NW * 2 * 128 * 4;
+  L.total = L.runs + NW * 2 * 4;
+  return L;
+}
+
+// Sum of the eight 16-bit activations held in one 16-byte block.
+template <int ACT>
+__device__ __forceinline__ float block_sum(const u32x4& v) {
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const unsigned w = v[e];  // a scalar copy: bit_cast must not see the vector element
+    if constexpr (ACT == ACT_FP16)
+      s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w),
+                                 __builtin_bit_cast(f16x2, 0x3C003C00u), s, false);
+    else
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                          __builtin_bit_cast(bf16x2, 0x3F803F80u), s, false);
+  }
+  return s;
+}
+
+// Sum over the eight lanes 8i..8i+7 (DPP: swap neighbours, swap pairs, then
+// mirror within the half row).
+__device__ __forceinline__ float sum8_lanes(float s) {
+  s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                     0, __builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
+  s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                     0, __builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, false));
+  s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                     0, __builtin_bit_cast(int, s), 0x141, 0xF, 0xF, false));
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// One row set (M <= 8), 16-bit activations, the work-group's whole K range in
+// LDS. Same per-step arithmetic as qgemm_w4 with R = 1; the work split and
+// the schedule differ:
+//  * Work is cut into blocks of DB consecutive group pairs of one column
+//    tile; the work-group's blocks, tile-major, are dealt to its NW waves as
+//    contiguous runs of equal length (+-1), so every SIMD carries the same
+//    load whatever the tile count. Addresses are set once per block; the
+//    steps of a block use immediate offsets. A run spans at most two tiles:
+//    a wave flushes its partial sums to LDS when its tile changes, and the
+//    final reduction adds the flushed tiles in wave order (a fixed order:
+//    results are deterministic).
+//  * The weight ring holds RB blocks (D = RB*DB steps). The activation and
+//    scale/bias loads go out first with D0 ring steps; the wave waits for
+//    the first two only (loads retire in order), stages them into LDS, and
+//    only then issues the other ring steps: a full ring of weight requests
+//    would queue ahead of the activation and table reads in the memory
+//    system, and a wave that issues more loads than the memory queue holds
+//    stalls until they drain.
+//  * Staging needs no division: lane (e = lane%8, row = lane/8) of wave w
+//    moves the 8 values k = 64g + 8e.. of group g = w + NW*i; the row sums
+//    come from dot products with ones and three DPP adds.
+//  * In the loop the LDS operands of step q+1 are read while step q runs,
+//    and step q's epilogue waits until step q+1's MFMAs are issued.
+//  * A missing odd last group reads whatever codes follow (or zeros past
+//    the buffer): its activations, row sum, scale and bias are all zero, so
+//    it adds exactly nothing. Columns past the work-group's read zeros and
+//    are never stored.
+template <int ACT, int NW, int TW, int DB, int RB, int D0, int XB>
+__global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
+    const void* __restrict__ x, const uint8_t* __restrict__ wq,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
+    float* __restrict__ y, int M, int K, int N, int cols) {
+  using TR = ActTraits<ACT>;
+  static_assert(TR::parts == 1, "16-bit activations only");
+  static_assert(TW <= NW, "a run must span at most two tiles");
+  constexpr int D = DB * RB;
+  static_assert(D0 >= 0 && D0 <= D, "prologue ring depth");
+  constexpr int NT = 64 * NW;
+  constexpr int WGC = 16 * TW;
+  constexpr int SBU = 2;                            // table units per thread per round
+  constexpr unsigned kSkip = 0x7FF00000u;           // scalar offset that reads as zero
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15;
+  const int h = lane >> 4;
+  const int half = h >> 1;
+  const int G = K >> 6;
+  const int GP = (G + 1) >> 1;                       // a multiple of DB (host)
+  const int bpt = GP / DB;                           // blocks per tile
+  const unsigned rowbytes = (unsigned)K >> 1;
+  const M8Layout L = m8_layout(G, WGC, NW);
+  unsigned char* xl = lds;
+  float* xsl = reinterpret_cast<float*>(lds + L.xs);
+  unsigned* sbl = reinterpret_cast<unsigned*>(lds + L.sb);
+  float* red = reinterpret_cast<float*>(lds + L.red);
+  int* run_tiles = reinterpret_cast<int*>(lds + L.runs);
+
+  const int wg0 = blockIdx.x * cols;
+  const int wgcols = min(cols, N - wg0);
+  const int tiles = (wgcols + 15) >> 4;
+  const int nblk = tiles * bpt;
+  const int b0 = (wave * nblk) / NW;
+  const int nb = ((wave + 1) * nblk) / NW - b0;
+  const int tfirst = b0 / bpt;
+
+  unsigned magic;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(TR::magic));
+
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(wq) + (size_t)wg0 * rowbytes, (short)0, wgcols * rowbytes,
+      kBufferFlags);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(scales) + (size_t)wg0 * G, (short)0, wgcols * G * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(biases) + (size_t)wg0 * G, (short)0, wgcols * G * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(x), (short)0, M * K * 2, kBufferFlags);
+
+  const unsigned woff = (unsigned)j * rowbytes + 16u * h;
+  const bool a_lane = ((j < 8) == (h < 2));
+  const int aslot = a_lane ? (h * 8 + (j & 7)) : 32;
+
+  // ---- activation staging, batch by batch (one batch up to K = 64*NW*XB).
+  const int ngrp = 2 * GP;                           // groups incl. a missing odd one
+  const int rounds = (ngrp + NW - 1) / NW;
+  const int e8 = lane & 7;                           // 8-value block within the group
+  const int mm = lane >> 3;                          // activation row
+  u32x4 xv[XB];
+  auto x_load = [&](int bb) {
+#pragma unroll
+    for (int i = 0; i < XB; ++i) {
+      const int g = wave + NW * (bb + i);
+      const int k = 64 * g + 8 * e8;
+      const bool ok = bb + i < rounds && g < ngrp && mm < M && k < K;
+      xv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          xr, ok ? (unsigned)((mm * K + k) * 2) : kOutOfRange, 0, 0);
+    }
+  };
+  auto x_store = [&](int bb) {
+#pragma unroll
+    for (int i = 0; i < XB; ++i) {
+      const int g = wave + NW * (bb + i);
+      const float s8 = sum8_lanes(block_sum<ACT>(xv[i]));
+      if (bb + i < rounds && g < ngrp) {
+        const int p = g >> 1, hf = g & 1;
+        const int slot = (hf * 2 + (e8 >> 2)) * 8 + mm;
+        *reinterpret_cast<u32x4*>(xl + p * kPairBytes + (e8 & 3) * kTRowBytes +
+                                  slot * kSlotBytes) = permute_pairs(xv[i]);
+        if (e8 == 0) xsl[g * 8 + mm] = s8;
+      }
+    }
+  };
+
+  // ---- scale/bias table (as in qgemm_w4).
+  const bool sb_vec = (G % 8) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
+                                        reinterpret_cast<uintptr_t>(biases)) & 15) == 0;
+  const int sb_units = sb_vec ? wgcols * G / 8 : wgcols * G;
+  u32x4 sbs[SBU], sbb[SBU];
+  auto sb_load = [&](int round) {
+#pragma unroll
+    for (int u = 0; u < SBU; ++u) {
+      const int i = (round * SBU + u) * NT + tid;
+      if (sb_vec) {
+        const unsigned off = i < sb_units ? 16u * i : kOutOfRange;
+        sbs[u] = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
+        sbb[u] = __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0);
+      } else {
+        const unsigned off = i < sb_units ? 2u * i : kOutOfRange;
+        sbs[u].x = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
+        sbb[u].x = __builtin_amdgcn_raw_buffer_load_b16(br, off, 0, 0);
+      }
+    }
+  };
+  auto sb_store = [&](int round) {
+#pragma unroll
+    for (int u = 0; u < SBU; ++u) {
+      const int i = (round * SBU + u) * NT + tid;
+      if (i < sb_units) {
+        if (sb_vec) {
+          const int e0 = 8 * i;
+          const int n = e0 / G, g = e0 - n * G;
+          u32x4 lo, hi;
+          lo.x = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x05040100u);
+          lo.y = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x07060302u);
+          lo.z = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x05040100u);
+          lo.w = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x07060302u);
+          hi.x = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x05040100u);
+          hi.y = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x07060302u);
+          hi.z = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x05040100u);
+          hi.w = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x07060302u);
+          *reinterpret_cast<u32x4*>(&sbl[n * L.sbs + g]) = lo;
+          *reinterpret_cast<u32x4*>(&sbl[n * L.sbs + g + 4]) = hi;
+        } else {
+          const int n = i / G, g = i - n * G;
+          sbl[n * L.sbs + g] = (sbs[u].x & 0xFFFFu) | (sbb[u].x << 16);
+        }
+      }
+    }
+  };
+
+  // ---- blocks of the run. Block i of this wave (0 <= i < nb) is block
+  // b0 + i of the work-group: tile t, pairs p .. p + DB - 1. Blocks are
+  // walked incrementally (no division in the loop).
+  struct Blk {
+    int t, p, left;                                  // left: blocks of the run from here on
+  };
+  const Blk kfirst = {tfirst, (b0 - tfirst * bpt) * DB, nb};
+  auto next = [&](Blk k) {
+    k.p += DB;
+    k.t += k.p == GP;
+    k.p = k.p == GP ? 0 : k.p;
+    k.left -= 1;
+    return k;
+  };
+  u32x4 st[D];
+  // Step d of block k into ring slot `slot` (16 code bytes of this lane).
+  auto load = [&](const Blk& k, int d, u32x4& w) {
+    const unsigned so = k.left > 0 ? (unsigned)k.t * 16u * rowbytes + 64u * (unsigned)k.p : kSkip;
+    w = __builtin_amdgcn_raw_buffer_load_b128(wr, woff + 64u * d, so, 0);
+  };
+
+  // ---- prologue.
+  Blk kl = kfirst;                                    // the next block to load
+  x_load(0);
+  sb_load(0);
+#pragma unroll
+  for (int d = 0; d < D0; ++d) {
+    load(kl, d % DB, st[d]);
+    if (d % DB == DB - 1) kl = next(kl);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(D0));
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < GP * 4; i += NT)
+      *reinterpret_cast<u32x4*>(xl + (i >> 2) * kPairBytes + (i & 3) * kTRowBytes +
+                                32 * kSlotBytes) = z;
+    for (int i = tid; i < kPairBytes / 16; i += NT)
+      *reinterpret_cast<u32x4*>(xl + GP * kPairBytes + 16 * i) = z;
+    if (tid < 16) xsl[GP * 16 + tid] = 0.0f;
+    for (int i = tid; i < WGC * 4; i += NT) sbl[(i >> 2) * L.sbs + G + (i & 3)] = 0u;
+  }
+  x_store(0);
+  sb_store(0);
+  for (int bb = XB; bb < rounds; bb += XB) {          // K above 64*NW*XB only
+    x_load(bb);
+    x_store(bb);
+  }
+  for (int round = 1; round * SBU * NT < sb_units; ++round) {
+    sb_load(round);
+    sb_store(round);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int d = D0; d < D; ++d) {
+    load(kl, d % DB, st[d]);
+    if (d % DB == DB - 1) kl = next(kl);
+  }
+  if (lane == 0) {                                    // this run's tiles, for the reduction
+    run_tiles[2 * wave] = nb > 0 ? tfirst : 1 << 30;
+    run_tiles[2 * wave + 1] = nb > 0 ? (b0 + nb - 1) / bpt : -1;
+  }
+  __syncthreads();
+
+  // ---- main loop.
+  const unsigned char* abase = xl + aslot * kSlotBytes;
+  const float* xsbase = xsl + half * 8 + 4 * (h & 1);
+  const unsigned* sbbase = sbl + j * L.sbs + half;
+  struct Ops { u32x4 A[4]; f32x4 xs; unsigned sb; };
+  // Operands of step d of block k (the zero image and pad past the run).
+  auto fetch = [&](const Blk& k, int d, Ops& o) {
+    const bool in = k.left > 0;                      // uniform
+    const int img = in ? k.p + d : GP;
+    const unsigned char* ab = abase + img * kPairBytes;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o.A[t] = *reinterpret_cast<const u32x4*>(ab + t * kTRowBytes);
+    o.xs = *reinterpret_cast<const f32x4*>(xsbase + img * 16);
+    o.sb = sbbase[in ? k.t * 16 * L.sbs + 2 * (k.p + d) : G + 2];
+  };
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int acc_tile = tfirst;
+  auto flush = [&](int seg) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = acc[e] + __shfl_xor(acc[e], 32);
+      if (lane < 32) red[((wave * 2 + seg) * 8 + 4 * (lane >> 4) + e) * 16 + j] = v;
+      acc[e] = 0.0f;
+    }
+  };
+  auto epilogue = [&](const f32x4& C, const Ops& o) {
+    const float sv = half_lo(o.sb);
+    const float bb = fmaf(-TR::c0, sv, half_hi(o.sb));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(sv, C[e], fmaf(bb, o.xs[e], acc[e]));
+  };
+
+  Ops cur, prev;
+  f32x4 Cprev = {0.0f, 0.0f, 0.0f, 0.0f};
+  prev.sb = 0u;                                       // step -1 adds exactly nothing
+  prev.xs = Cprev;
+  int prev_tile = tfirst;
+  Blk kc = kfirst;                                    // the block being computed
+  fetch(kc, 0, cur);
+  // One block: its DB steps from ring slots r*DB.., loading block kl into
+  // them when `reload`.
+  auto run_block = [&](int r, bool reload) {
+    const Blk kn = next(kc);                          // the next block (LDS prefetch)
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      u32x4 bq[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bq[t] = unpack_codes(st[r * DB + d][t], magic);
+      f32x4 C = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) C = mfma16x16x32<TR::f16>(cur.A[t], bq[t], C);
+      Ops nxt;
+      if (d + 1 < DB) fetch(kc, d + 1, nxt);
+      else fetch(kn, 0, nxt);
+      if (d == 0 && kc.t != prev_tile) {              // uniform: the last step ended a tile
+        epilogue(Cprev, prev);
+        flush(0);
+        acc_tile = kc.t;
+        prev_tile = kc.t;
+      } else {
+        epilogue(Cprev, prev);
+      }
+      if (reload) load(kl, d, st[r * DB + d]);
+      Cprev = C;
+      prev = cur;
+      cur = nxt;
+    }
+    if (reload) kl = next(kl);
+    kc = kn;
+  };
+  int i = 0;
+  for (; i + RB <= nb; i += RB) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) run_block(r, true);
+  }
+#pragma unroll
+  for (int r = 0; r < RB - 1; ++r)                    // the last nb % RB blocks
+    if (i + r < nb) run_block(r, false);
+  epilogue(Cprev, prev);
+  flush(acc_tile > tfirst ? 1 : 0);
+
+  // ---- reduce: each output tile adds the flushed partials of the runs that
+  // cover it, in wave order.
+  __syncthreads();
+  for (int idx = tid; idx < tiles * 128; idx += NT) {
+    const int t = idx >> 7;
+    const int within = idx & 127;                     // row * 16 + column
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int tb = run_tiles[2 * w], te = run_tiles[2 * w + 1];
+      if (t >= tb && t <= te) s += red[((w * 2 + (t - tb)) * 128) + within];
+    }
+    const int m = within >> 4;
+    const int c = t * 16 + (within & 15);
+    if (m < M && c < wgcols) y[(size_t)m * N + wg0 + c] = s;
+  }
+}
+
 constexpr int kLdsLimit = 160 * 1024;
 
 int device_cus() {
@@ -562,6 +948,39 @@ hipError_t launch_w4(const void* x, const uint8_t* wq, const uint16_t* scales,
   return hipGetLastError();
 }
 
+template <int ACT, int NW, int DB, int RB, int D0 = 2>
+hipError_t launch_m8(const void* x, const uint8_t* wq, const uint16_t* scales,
+                     const uint16_t* biases, float* y, int M, int K, int N, int cols,
+                     hipStream_t stream) {
+  constexpr int TW = 5;
+  constexpr int XB = (5120 / 64 + NW - 1) / NW;      // one staging batch up to K = 5120
+  const M8Layout L = m8_layout(K >> 6, 16 * TW, NW);
+  auto kern = qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB>;
+  if (L.total > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             L.total);
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((N + cols - 1) / cols);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * NW), L.total, stream, x, wq, scales, biases, y, M,
+                     K, N, cols);
+  return hipGetLastError();
+}
+
+// Block length of qgemm_w4_m8: the largest of 5, 4, 2, 1 that divides the
+// group-pair count; the ring holds two blocks (four of one pair).
+template <int ACT>
+hipError_t launch_m8_blocks(const void* x, const uint8_t* wq, const uint16_t* scales,
+                            const uint16_t* biases, float* y, int M, int K, int N, int cols,
+                            hipStream_t s) {
+  const int GP = ((K >> 6) + 1) >> 1;
+  if (GP % 5 == 0) return launch_m8<ACT, 8, 5, 2>(x, wq, scales, biases, y, M, K, N, cols, s);
+  if (GP % 4 == 0) return launch_m8<ACT, 8, 4, 2>(x, wq, scales, biases, y, M, K, N, cols, s);
+  if (GP % 2 == 0) return launch_m8<ACT, 8, 2, 4>(x, wq, scales, biases, y, M, K, N, cols, s);
+  return launch_m8<ACT, 8, 1, 8>(x, wq, scales, biases, y, M, K, N, cols, s);
+}
+
 // Configuration per problem. M <= 8 (one row set): when the work-group's
 // whole activation range fits in LDS, the barrier-free XALL kernel; narrow N
 // is split into exactly one work-group per CU (columns rounded up to 4, up
@@ -570,6 +989,14 @@ template <int ACT>
 hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                          const uint16_t* biases, float* y, int M, int K, int N,
                          hipStream_t s) {
+  if constexpr (ACT != ACT_FP32) if (M <= 8) {
+    // Columns per work-group: an equal share of the CUs, at most 5 tiles.
+    const int cus = device_cus();
+    const int share = ((N + cus - 1) / cus + 3) / 4 * 4;
+    const int cols = share < 80 ? share : 80;
+    if (m8_layout(K >> 6, 80, 8).total <= kLdsLimit)
+      return launch_m8_blocks<ACT>(x, wq, scales, biases, y, M, K, N, cols, s);
+  }
   if (M <= 8) {
     const int cus = device_cus();
     const int share = ((N + cus - 1) / cus + 3) / 4 * 4;
