@@ -46,6 +46,9 @@ SHAPES = [
     (3, 5120, 200), (9, 256, 70), (16, 640, 300), (17, 128, 64), (32, 256, 96), (33, 384, 50),
     (64, 512, 130), (7, 4096, 64), (8, 8192, 77), (8, 16384, 40), (16, 16320, 33),
     (64, 2560, 96), (5, 5120, 1000),
+    # Work-groups of several column tiles (the column share of a CU spans
+    # 2, 3 and 5 tiles, the last one partial): runs that cross a tile.
+    (8, 512, 5000), (8, 1280, 12000), (5, 640, 17000), (8, 2560, 17408),
 ]
 
 

@@ -535,19 +535,22 @@ constexpr int vmcnt_wait(int vm) {
   return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 }
 
-// LDS of qgemm_w4_m8: GP activation images and one zero image, the row sums
-// (16 floats per image), the (s, b) table (G + 4 dwords per column), then the
-// partial-sum slots, two 8x16 tiles per wave, then each run's first and last
-// tile.
+// LDS of qgemm_w4_m8: GP activation images and one zero image (more when the
+// staging rounds are padded), the row sums (16 floats per image), the (s, b)
+// table (G + 4 dwords per column), the partial-sum slots (two 8x16 tiles per
+// wave), then each run's first and last tile.
 struct M8Layout {
   int xs, sb, sbs, red, runs, total;
 };
 
-__host__ __device__ inline M8Layout m8_layout(int G, int WGC, int NW) {
+__host__ __device__ inline M8Layout m8_layout(int G, int WGC, int NW, int XB) {
   const int GP = (G + 1) >> 1;
+  const int rounds = (2 * GP + NW - 1) / NW;             // staging rounds per wave
+  const int padded = (rounds + XB - 1) / XB * XB * NW;   // groups the staging writes
+  const int nimg = GP + 1 > padded / 2 ? GP + 1 : padded / 2;
   M8Layout L{};
-  L.xs = (GP + 1) * kPairBytes;
-  L.sb = L.xs + (GP + 1) * 16 * 4;
+  L.xs = nimg * kPairBytes;
+  L.sb = L.xs + nimg * 16 * 4;
   L.sbs = G + 4;
   L.red = L.sb + WGC * L.sbs * 4;
   L.runs = L.red + NW * 2 * 128 * 4;
@@ -620,6 +623,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
   using TR = ActTraits<ACT>;
   static_assert(TR::parts == 1, "16-bit activations only");
   static_assert(TW <= NW, "a run must span at most two tiles");
+  static_assert(NW >= 8, "the partial-sum slots double as an 8 KB write sink");
   constexpr int D = DB * RB;
   static_assert(D0 >= 0 && D0 <= D, "prologue ring depth");
   constexpr int NT = 64 * NW;
@@ -639,7 +643,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
   const int GP = (G + 1) >> 1;                       // a multiple of DB (host)
   const int bpt = GP / DB;                           // blocks per tile
   const unsigned rowbytes = (unsigned)K >> 1;
-  const M8Layout L = m8_layout(G, WGC, NW);
+  const M8Layout L = m8_layout(G, WGC, NW, XB);
   unsigned char* xl = lds;
   float* xsl = reinterpret_cast<float*>(lds + L.xs);
   unsigned* sbl = reinterpret_cast<unsigned*>(lds + L.sb);
@@ -682,23 +686,24 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
     for (int i = 0; i < XB; ++i) {
       const int g = wave + NW * (bb + i);
       const int k = 64 * g + 8 * e8;
-      const bool ok = bb + i < rounds && g < ngrp && mm < M && k < K;
+      const bool ok = mm < M && k < K;
       xv[i] = __builtin_amdgcn_raw_buffer_load_b128(
           xr, ok ? (unsigned)((mm * K + k) * 2) : kOutOfRange, 0, 0);
     }
   };
+  const unsigned xl_lane = (e8 & 3) * kTRowBytes + ((e8 >> 2) * 8 + mm) * kSlotBytes;
+  // The image area is padded (m8_layout) so that every round of every batch
+  // has a slot: rounds past the last group stage zeros (their loads read
+  // past K) into images that are never read, or into the zero image.
   auto x_store = [&](int bb) {
 #pragma unroll
     for (int i = 0; i < XB; ++i) {
-      const int g = wave + NW * (bb + i);
+      const int g = wave + NW * (bb + i);             // uniform
+      // Sum of the row's 64 values: the eight lanes of (row, group) all hold it.
       const float s8 = sum8_lanes(block_sum<ACT>(xv[i]));
-      if (bb + i < rounds && g < ngrp) {
-        const int p = g >> 1, hf = g & 1;
-        const int slot = (hf * 2 + (e8 >> 2)) * 8 + mm;
-        *reinterpret_cast<u32x4*>(xl + p * kPairBytes + (e8 & 3) * kTRowBytes +
-                                  slot * kSlotBytes) = permute_pairs(xv[i]);
-        if (e8 == 0) xsl[g * 8 + mm] = s8;
-      }
+      *reinterpret_cast<u32x4*>(xl + (g >> 1) * kPairBytes + (g & 1) * 16 * kSlotBytes +
+                                xl_lane) = permute_pairs(xv[i]);
+      xsl[g * 8 + mm] = s8;
     }
   };
 
@@ -722,29 +727,36 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
       }
     }
   };
+  // n = e / G as a high product with ceil(2^32 / G) (exact for e < 2^32 / G);
+  // G = 1 has no 32-bit reciprocal and is handled directly.
+  const unsigned g_recip = 0xFFFFFFFFu / (unsigned)G + 1u;
+  auto div_g = [&](unsigned e) { return G == 1 ? e : __umulhi(e, g_recip); };
   auto sb_store = [&](int round) {
 #pragma unroll
     for (int u = 0; u < SBU; ++u) {
       const int i = (round * SBU + u) * NT + tid;
-      if (i < sb_units) {
-        if (sb_vec) {
-          const int e0 = 8 * i;
-          const int n = e0 / G, g = e0 - n * G;
-          u32x4 lo, hi;
-          lo.x = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x05040100u);
-          lo.y = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x07060302u);
-          lo.z = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x05040100u);
-          lo.w = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x07060302u);
-          hi.x = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x05040100u);
-          hi.y = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x07060302u);
-          hi.z = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x05040100u);
-          hi.w = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x07060302u);
-          *reinterpret_cast<u32x4*>(&sbl[n * L.sbs + g]) = lo;
-          *reinterpret_cast<u32x4*>(&sbl[n * L.sbs + g + 4]) = hi;
-        } else {
-          const int n = i / G, g = i - n * G;
-          sbl[n * L.sbs + g] = (sbs[u].x & 0xFFFFu) | (sbb[u].x << 16);
-        }
+      const bool ok = i < sb_units;
+      if (sb_vec) {
+        const unsigned e0 = 8u * (unsigned)i;         // first element of the unit
+        const unsigned n = div_g(e0), g = e0 - n * (unsigned)G;
+        u32x4 lo, hi;                                 // (s_g | b_g << 16) for g .. g+7
+        lo.x = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x05040100u);
+        lo.y = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x07060302u);
+        lo.z = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x05040100u);
+        lo.w = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x07060302u);
+        hi.x = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x05040100u);
+        hi.y = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x07060302u);
+        hi.z = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x05040100u);
+        hi.w = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x07060302u);
+        // Units past the table write into the partial-sum slots (8 KB, not
+        // read before the end of the loop).
+        const unsigned o = ok ? (unsigned)L.sb + 4u * (n * (unsigned)L.sbs + g)
+                              : (unsigned)L.red + 32u * ((unsigned)tid & 255u);
+        *reinterpret_cast<u32x4*>(lds + o) = lo;
+        *reinterpret_cast<u32x4*>(lds + o + 16) = hi;
+      } else if (ok) {
+        const unsigned n = div_g((unsigned)i), g = (unsigned)i - n * (unsigned)G;
+        sbl[n * L.sbs + g] = (sbs[u].x & 0xFFFFu) | (sbb[u].x << 16);
       }
     }
   };
@@ -764,9 +776,12 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
     return k;
   };
   u32x4 st[D];
-  // Step d of block k into ring slot `slot` (16 code bytes of this lane).
-  auto load = [&](const Blk& k, int d, u32x4& w) {
-    const unsigned so = k.left > 0 ? (unsigned)k.t * 16u * rowbytes + 64u * (unsigned)k.p : kSkip;
+  // Scalar offset of block k's codes (past the run: an offset that reads zeros).
+  auto codes_at = [&](const Blk& k) {
+    return k.left > 0 ? (unsigned)k.t * 16u * rowbytes + 64u * (unsigned)k.p : kSkip;
+  };
+  // Step d of the block at scalar offset `so` into a ring slot.
+  auto load = [&](unsigned so, int d, u32x4& w) {
     w = __builtin_amdgcn_raw_buffer_load_b128(wr, woff + 64u * d, so, 0);
   };
 
@@ -776,7 +791,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
   sb_load(0);
 #pragma unroll
   for (int d = 0; d < D0; ++d) {
-    load(kl, d % DB, st[d]);
+    load(codes_at(kl), d % DB, st[d]);
     if (d % DB == DB - 1) kl = next(kl);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(D0));
@@ -803,7 +818,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int d = D0; d < D; ++d) {
-    load(kl, d % DB, st[d]);
+    load(codes_at(kl), d % DB, st[d]);
     if (d % DB == DB - 1) kl = next(kl);
   }
   if (lane == 0) {                                    // this run's tiles, for the reduction
@@ -817,15 +832,28 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
   const float* xsbase = xsl + half * 8 + 4 * (h & 1);
   const unsigned* sbbase = sbl + j * L.sbs + half;
   struct Ops { u32x4 A[4]; f32x4 xs; unsigned sb; };
-  // Operands of step d of block k (the zero image and pad past the run).
-  auto fetch = [&](const Blk& k, int d, Ops& o) {
+  // LDS bases of block k (the zero image and pad past the run); step d of a
+  // block reads at immediate offsets from them.
+  struct Base {
+    const unsigned char* a;
+    const float* xs;
+    const unsigned* sb;
+  };
+  auto base_of = [&](const Blk& k) {
     const bool in = k.left > 0;                      // uniform
-    const int img = in ? k.p + d : GP;
-    const unsigned char* ab = abase + img * kPairBytes;
+    const int img = in ? k.p : GP;
+    Base b;
+    b.a = abase + img * kPairBytes;
+    b.xs = xsbase + img * 16;
+    b.sb = sbbase + (in ? k.t * 16 * L.sbs + 2 * k.p : G + 2);
+    return b;
+  };
+  auto fetch = [&](const Base& b, int d, Ops& o) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) o.A[t] = *reinterpret_cast<const u32x4*>(ab + t * kTRowBytes);
-    o.xs = *reinterpret_cast<const f32x4*>(xsbase + img * 16);
-    o.sb = sbbase[in ? k.t * 16 * L.sbs + 2 * (k.p + d) : G + 2];
+    for (int t = 0; t < 4; ++t)
+      o.A[t] = *reinterpret_cast<const u32x4*>(b.a + d * kPairBytes + t * kTRowBytes);
+    o.xs = *reinterpret_cast<const f32x4*>(b.xs + d * 16);
+    o.sb = b.sb[2 * d];
   };
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   int acc_tile = tfirst;
@@ -850,11 +878,14 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
   prev.xs = Cprev;
   int prev_tile = tfirst;
   Blk kc = kfirst;                                    // the block being computed
-  fetch(kc, 0, cur);
+  Base bc = base_of(kc);
+  fetch(bc, 0, cur);
   // One block: its DB steps from ring slots r*DB.., loading block kl into
   // them when `reload`.
   auto run_block = [&](int r, bool reload) {
     const Blk kn = next(kc);                          // the next block (LDS prefetch)
+    const Base bn = base_of(kn);
+    const unsigned so = codes_at(kl);
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
       u32x4 bq[4];
@@ -864,8 +895,8 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
 #pragma unroll
       for (int t = 0; t < 4; ++t) C = mfma16x16x32<TR::f16>(cur.A[t], bq[t], C);
       Ops nxt;
-      if (d + 1 < DB) fetch(kc, d + 1, nxt);
-      else fetch(kn, 0, nxt);
+      if (d + 1 < DB) fetch(bc, d + 1, nxt);
+      else fetch(bn, 0, nxt);
       if (d == 0 && kc.t != prev_tile) {              // uniform: the last step ended a tile
         epilogue(Cprev, prev);
         flush(0);
@@ -874,13 +905,14 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
       } else {
         epilogue(Cprev, prev);
       }
-      if (reload) load(kl, d, st[r * DB + d]);
+      if (reload) load(so, d, st[r * DB + d]);
       Cprev = C;
       prev = cur;
       cur = nxt;
     }
     if (reload) kl = next(kl);
     kc = kn;
+    bc = bn;
   };
   int i = 0;
   for (; i + RB <= nb; i += RB) {
@@ -948,13 +980,12 @@ hipError_t launch_w4(const void* x, const uint8_t* wq, const uint16_t* scales,
   return hipGetLastError();
 }
 
-template <int ACT, int NW, int DB, int RB, int D0 = 2>
+template <int ACT, int NW, int DB, int RB, int XB, int D0 = 2>
 hipError_t launch_m8(const void* x, const uint8_t* wq, const uint16_t* scales,
                      const uint16_t* biases, float* y, int M, int K, int N, int cols,
                      hipStream_t stream) {
   constexpr int TW = 5;
-  constexpr int XB = (5120 / 64 + NW - 1) / NW;      // one staging batch up to K = 5120
-  const M8Layout L = m8_layout(K >> 6, 16 * TW, NW);
+  const M8Layout L = m8_layout(K >> 6, 16 * TW, NW, XB);
   auto kern = qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB>;
   if (L.total > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -968,17 +999,21 @@ hipError_t launch_m8(const void* x, const uint8_t* wq, const uint16_t* scales,
   return hipGetLastError();
 }
 
+// Staging rounds per batch: 5 up to K = 2560, else 10 (8 waves; one batch up
+// to K = 5120).
+constexpr int m8_xb(int K) { return K <= 2560 ? 5 : 10; }
+
 // Block length of qgemm_w4_m8: the largest of 5, 4, 2, 1 that divides the
 // group-pair count; the ring holds two blocks (four of one pair).
-template <int ACT>
+template <int ACT, int XB>
 hipError_t launch_m8_blocks(const void* x, const uint8_t* wq, const uint16_t* scales,
                             const uint16_t* biases, float* y, int M, int K, int N, int cols,
                             hipStream_t s) {
   const int GP = ((K >> 6) + 1) >> 1;
-  if (GP % 5 == 0) return launch_m8<ACT, 8, 5, 2>(x, wq, scales, biases, y, M, K, N, cols, s);
-  if (GP % 4 == 0) return launch_m8<ACT, 8, 4, 2>(x, wq, scales, biases, y, M, K, N, cols, s);
-  if (GP % 2 == 0) return launch_m8<ACT, 8, 2, 4>(x, wq, scales, biases, y, M, K, N, cols, s);
-  return launch_m8<ACT, 8, 1, 8>(x, wq, scales, biases, y, M, K, N, cols, s);
+  if (GP % 5 == 0) return launch_m8<ACT, 8, 5, 2, XB>(x, wq, scales, biases, y, M, K, N, cols, s);
+  if (GP % 4 == 0) return launch_m8<ACT, 8, 4, 2, XB>(x, wq, scales, biases, y, M, K, N, cols, s);
+  if (GP % 2 == 0) return launch_m8<ACT, 8, 2, 4, XB>(x, wq, scales, biases, y, M, K, N, cols, s);
+  return launch_m8<ACT, 8, 1, 8, XB>(x, wq, scales, biases, y, M, K, N, cols, s);
 }
 
 // Configuration per problem. M <= 8 (one row set): when the work-group's
@@ -994,8 +1029,11 @@ hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scale
     const int cus = device_cus();
     const int share = ((N + cus - 1) / cus + 3) / 4 * 4;
     const int cols = share < 80 ? share : 80;
-    if (m8_layout(K >> 6, 80, 8).total <= kLdsLimit)
-      return launch_m8_blocks<ACT>(x, wq, scales, biases, y, M, K, N, cols, s);
+    if (m8_layout(K >> 6, 80, 8, m8_xb(K)).total <= kLdsLimit) {
+      if (m8_xb(K) == 5)
+        return launch_m8_blocks<ACT, 5>(x, wq, scales, biases, y, M, K, N, cols, s);
+      return launch_m8_blocks<ACT, 10>(x, wq, scales, biases, y, M, K, N, cols, s);
+    }
   }
   if (M <= 8) {
     const int cus = device_cus();
