@@ -346,7 +346,7 @@ def main():
         "step_hbm_gbs": (qb + (4 * M * N if T else 0)) / (ms_step * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_record(args.workload, M),
-                     "kernel": "qgemm_w4", "bytes_per_launch": qb},
+                     "kernel": "qgemm_w4_m8" if M <= 8 and act != "fp32" else "qgemm_w4", "bytes_per_launch": qb},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -600,12 +600,12 @@ __device__ __forceinline__ float sum8_lanes(float s) {
 //    final reduction adds the flushed tiles in wave order (a fixed order:
 //    results are deterministic).
 //  * The weight ring holds RB blocks (D = RB*DB steps). The activation and
-//    scale/bias loads go out first with D0 ring steps; the wave waits for
-//    the first two only (loads retire in order), stages them into LDS, and
-//    only then issues the other ring steps: a full ring of weight requests
-//    would queue ahead of the activation and table reads in the memory
-//    system, and a wave that issues more loads than the memory queue holds
-//    stalls until they drain.
+//    scale/bias loads go out first with D0 ring steps; the other ring steps
+//    are issued one per staging round. Loads retire in order, so staging
+//    waits for the activations only; a full ring issued up front would queue
+//    ahead of the activation and table reads in the memory system, and a
+//    wave that issues more loads than the memory queue holds stalls until
+//    they drain, which would hold up its staging.
 //  * Staging needs no division: lane (e = lane%8, row = lane/8) of wave w
 //    moves the 8 values k = 64g + 8e.. of group g = w + NW*i; the row sums
 //    come from dot products with ones and three DPP adds.
@@ -695,16 +695,17 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
   // The image area is padded (m8_layout) so that every round of every batch
   // has a slot: rounds past the last group stage zeros (their loads read
   // past K) into images that are never read, or into the zero image.
+  auto x_store_round = [&](int bb, int i) {
+    const int g = wave + NW * (bb + i);               // uniform
+    // Sum of the row's 64 values: the eight lanes of (row, group) all hold it.
+    const float s8 = sum8_lanes(block_sum<ACT>(xv[i]));
+    *reinterpret_cast<u32x4*>(xl + (g >> 1) * kPairBytes + (g & 1) * 16 * kSlotBytes +
+                              xl_lane) = permute_pairs(xv[i]);
+    xsl[g * 8 + mm] = s8;
+  };
   auto x_store = [&](int bb) {
 #pragma unroll
-    for (int i = 0; i < XB; ++i) {
-      const int g = wave + NW * (bb + i);             // uniform
-      // Sum of the row's 64 values: the eight lanes of (row, group) all hold it.
-      const float s8 = sum8_lanes(block_sum<ACT>(xv[i]));
-      *reinterpret_cast<u32x4*>(xl + (g >> 1) * kPairBytes + (g & 1) * 16 * kSlotBytes +
-                                xl_lane) = permute_pairs(xv[i]);
-      xsl[g * 8 + mm] = s8;
-    }
+    for (int i = 0; i < XB; ++i) x_store_round(bb, i);
   };
 
   // ---- scale/bias table (as in qgemm_w4).
@@ -787,14 +788,14 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
 
   // ---- prologue.
   Blk kl = kfirst;                                    // the next block to load
+  auto ring_load = [&](int d) {                       // ring slot d, in slot order
+    load(codes_at(kl), d % DB, st[d]);
+    if (d % DB == DB - 1) kl = next(kl);
+  };
   x_load(0);
   sb_load(0);
 #pragma unroll
-  for (int d = 0; d < D0; ++d) {
-    load(codes_at(kl), d % DB, st[d]);
-    if (d % DB == DB - 1) kl = next(kl);
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_wait(D0));
+  for (int d = 0; d < D0; ++d) ring_load(d);
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int i = tid; i < GP * 4; i += NT)
@@ -805,7 +806,13 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
     if (tid < 16) xsl[GP * 16 + tid] = 0.0f;
     for (int i = tid; i < WGC * 4; i += NT) sbl[(i >> 2) * L.sbs + G + (i & 3)] = 0u;
   }
-  x_store(0);
+  // The first batch is staged round by round, one more ring slot issued
+  // before each round, so the weight stream starts while staging runs.
+#pragma unroll
+  for (int i = 0; i < XB; ++i) {
+    if (D0 + i < D) ring_load(D0 + i);
+    x_store_round(0, i);
+  }
   sb_store(0);
   for (int bb = XB; bb < rounds; bb += XB) {          // K above 64*NW*XB only
     x_load(bb);
@@ -815,12 +822,8 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
     sb_load(round);
     sb_store(round);
   }
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int d = D0; d < D; ++d) {
-    load(codes_at(kl), d % DB, st[d]);
-    if (d % DB == DB - 1) kl = next(kl);
-  }
+  for (int d = D0 + XB; d < D; ++d) ring_load(d);
   if (lane == 0) {                                    // this run's tiles, for the reduction
     run_tiles[2 * wave] = nb > 0 ? tfirst : 1 << 30;
     run_tiles[2 * wave + 1] = nb > 0 ? (b0 + nb - 1) / bpt : -1;
@@ -1004,13 +1007,14 @@ hipError_t launch_m8(const void* x, const uint8_t* wq, const uint16_t* scales,
 constexpr int m8_xb(int K) { return K <= 2560 ? 5 : 10; }
 
 // Block length of qgemm_w4_m8: the largest of 5, 4, 2, 1 that divides the
-// group-pair count; the ring holds two blocks (four of one pair).
+// group-pair count; the ring holds one block of 5, two of 4, four of 2 or
+// eight of 1 (deeper rings delay the staging reads, measured at K = 5120).
 template <int ACT, int XB>
 hipError_t launch_m8_blocks(const void* x, const uint8_t* wq, const uint16_t* scales,
                             const uint16_t* biases, float* y, int M, int K, int N, int cols,
                             hipStream_t s) {
   const int GP = ((K >> 6) + 1) >> 1;
-  if (GP % 5 == 0) return launch_m8<ACT, 8, 5, 2, XB>(x, wq, scales, biases, y, M, K, N, cols, s);
+  if (GP % 5 == 0) return launch_m8<ACT, 8, 5, 1, XB>(x, wq, scales, biases, y, M, K, N, cols, s);
   if (GP % 4 == 0) return launch_m8<ACT, 8, 4, 2, XB>(x, wq, scales, biases, y, M, K, N, cols, s);
   if (GP % 2 == 0) return launch_m8<ACT, 8, 2, 4, XB>(x, wq, scales, biases, y, M, K, N, cols, s);
   return launch_m8<ACT, 8, 1, 8, XB>(x, wq, scales, biases, y, M, K, N, cols, s);
