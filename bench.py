@@ -54,7 +54,7 @@ def qgemm_bytes(M, K, N, esz):
     return K * N // 2 + 4 * N * (K // 64) + M * K * esz + 4 * M * N
 
 
-def traffic_record(workload, M):
+def traffic_record(workload, M, fused=False):
     """Measured HBM bytes per launch from committed rocprofv3 counter runs,
     valid only while the kernel source is unchanged."""
     path = os.path.join(ROOT, "profiles", "qgemm_traffic.json")
@@ -62,7 +62,7 @@ def traffic_record(workload, M):
         return None
     rec = json.load(open(path))
     src = open(os.path.join(ROOT, "w4_gemm_vqv_amd", "csrc", "qgemm.hip"), "rb").read()
-    entry = rec.get("workloads", {}).get(f"{workload}:M={M}")
+    entry = rec.get("workloads", {}).get(f"{workload}:M={M}" + (":fused" if fused else ""))
     if not entry or rec.get("qgemm_hip_sha256") != hashlib.sha256(src).hexdigest():
         return None
     return entry["fetch_bytes"] + entry["write_bytes"]
@@ -127,7 +127,7 @@ def _counter_rows(run_dir):
     return rows
 
 
-def write_traffic(fetch_dir, write_dir, workload, M):
+def write_traffic(fetch_dir, write_dir, workload, M, fused):
     """Per-launch HBM bytes of the QMM from a FETCH_SIZE pass and a WRITE_SIZE
     pass of `bench.py --counter-pass`, each scaled by what the same counter
     reads for the copy kernel (COPY_PROBE_BYTES read and written per launch)."""
@@ -137,7 +137,7 @@ def write_traffic(fetch_dir, write_dir, workload, M):
         for kname, cname, v in _counter_rows(run_dir):
             if cname != counter:
                 continue
-            if "qgemm_w4" in kname:
+            if "qgemm_w4" in kname and (", true>" in kname) == fused:
                 q.append(v)
             elif "neg" in kname.lower():
                 cp.append(v)
@@ -157,9 +157,10 @@ def write_traffic(fetch_dir, write_dir, workload, M):
     sha = hashlib.sha256(src).hexdigest()
     if rec.get("qgemm_hip_sha256") != sha:
         rec = {"qgemm_hip_sha256": sha, "workloads": {}}
-    rec["workloads"][f"{workload}:M={M}"] = out
+    key = f"{workload}:M={M}" + (":fused" if fused else "")
+    rec["workloads"][key] = out
     json.dump(rec, open(path, "w"), indent=1, sort_keys=True)
-    print(json.dumps({f"{workload}:M={M}": out}))
+    print(json.dumps({key: out}))
 
 
 def main():
@@ -174,6 +175,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=None, help="weight copies cycled per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=["fused", "separate"], default="fused",
+                    help="one step: the projection with the verify fused into its epilogue, "
+                         "or the two calls back to back")
     ap.add_argument("--counter-pass", action="store_true",
                     help="eager QMM launches + a copy kernel, for one rocprofv3 --pmc pass")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -182,7 +186,8 @@ def main():
     if args.write_traffic:
         import gen
         write_traffic(*args.write_traffic, args.workload,
-                      args.m or gen.CONFIGS[args.workload]["M"])
+                      args.m or gen.CONFIGS[args.workload]["M"],
+                      args.path == "fused" and args.workload in VERIFY)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -205,6 +210,7 @@ def main():
     M = args.m or c["M"]
     K, N, act = c["K"], c["N"], c["act"]
     esz = 4 if act == "fp32" else 2
+    vqv_act = {"bf16": 0, "fp16": 1, "fp32": 2}[act]
     T, B = VERIFY.get(args.workload, (0, 0))
     if T:
         if B == 1:
@@ -236,6 +242,11 @@ def main():
         vws = torch.empty(max(vqv.vqv_verify_workspace_bytes(B, T, N), 8), dtype=torch.uint8,
                           device=dev)
     stream = torch.cuda.current_stream()
+    fused_ok = T > 0 and vqv.vqv_qgemm_verify_workspace_bytes(M, K, N, 64, vqv_act) > 0
+    if fused_ok:
+        fws = torch.zeros(vqv.vqv_qgemm_verify_workspace_bytes(M, K, N, 64, vqv_act),
+                          dtype=torch.uint8, device=dev)
+    use_fused = fused_ok and args.path == "fused"
 
     def qmm(i, st):
         xc, wc, sc, bc = copies[i % R]
@@ -245,7 +256,15 @@ def main():
         vqv.vqv_verify(y, draft if T > 1 else None, B, T, argmax=am, accept_len=al,
                        workspace=vws, stream=st)
 
+    def fused(i, st):
+        xc, wc, sc, bc = copies[i % R]
+        vqv.vqv_qgemm_verify(xc, wc, sc, bc, draft if T > 1 else None, B, T, y=y, argmax=am,
+                             accept_len=al, workspace=fws, stream=st)
+
     def step(i, st):
+        if use_fused:
+            fused(i, st)
+            return
         qmm(i, st)
         if T:
             ver(st)
@@ -255,13 +274,13 @@ def main():
         # QMM over every weight copy twice, then a plain copy kernel of known
         # size whose counter reading calibrates bytes per counted unit.
         for i in range(2 * R):
-            qmm(i, stream)
+            (fused if use_fused else qmm)(i, stream)
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        log(f"counter pass done: {2 * R} QMM launches, 3 copy launches of "
+        log(f"counter pass done: {2 * R} {'fused ' if use_fused else ''}QMM launches, 3 copy launches of "
             f"{COPY_PROBE_BYTES} bytes each way")
         return
 
@@ -319,9 +338,19 @@ def main():
         g_v = graph_of(lambda i, st: ver(st), QMM_LAUNCHES)
         g_v.replay()
         v_runs = [timed(g_v) * 1e3 / QMM_LAUNCHES for _ in range(5)]
+    f_runs = None
+    if use_fused:
+        g_f = graph_of(fused, nq)
+        g_f.replay()
+        f_runs = [timed(g_f) * 1e3 / nq for _ in range(5)]
 
     qb = qgemm_bytes(M, K, N, esz)
-    achieved = qb / (q_mean * 1e-6) / 1e9
+    # The dominant kernel: the step's projection kernel (with the fused verify
+    # when the step uses it; its extra traffic is 8 bytes per row and group).
+    k_us = statistics.fmean(f_runs) if use_fused else q_mean
+    achieved = qb / (k_us * 1e-6) / 1e9
+    kname = ("qgemm_w4_m8 (fused verify)" if use_fused else
+             "qgemm_w4_m8" if M <= 8 and act != "fp32" else "qgemm_w4")
     out = {
         "metric": METRIC,
         "value": M / (ms_step * 1e-3),
@@ -336,17 +365,20 @@ def main():
         "dtype": act,
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: W4 group-64 QMM M={M} K={K} N={N} {act} "
-                               + (f"+ greedy verify B={B} T={T}" if T else "(no verify)"),
+                               + (f"+ greedy verify B={B} T={T}" if T else "(no verify)")
+                               + (" (verify fused into the QMM epilogue)" if use_fused else ""),
                    "M": M, "K": K, "N": N, "group": 64, "act": act, "verify_B": B,
                    "verify_T": T, "weight_copies": R},
         "eager_ms_per_step": ms_eager,
         "qgemm_us_mean": q_mean,
         "qgemm_us_runs": q_runs,
         "verify_us_mean": statistics.fmean(v_runs),
+        "fused_us_mean": statistics.fmean(f_runs) if f_runs else None,
+        "step_path": "fused" if use_fused else "separate",
         "step_hbm_gbs": (qb + (4 * M * N if T else 0)) / (ms_step * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_record(args.workload, M),
-                     "kernel": "qgemm_w4_m8" if M <= 8 and act != "fp32" else "qgemm_w4", "bytes_per_launch": qb},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_record(args.workload, M, use_fused),
+                     "kernel": kname, "bytes_per_launch": qb, "us_per_launch": k_us},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

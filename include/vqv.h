@@ -126,6 +126,39 @@ vqv_status vqv_verify(const float* logits, const int32_t* draft, int B, int T, i
                       int32_t* argmax, int32_t* accept_len, void* workspace,
                       size_t workspace_bytes, void* hip_stream);
 
+/*
+ * Projection and greedy verify in one call: y = x . W^T as vqv_qgemm, then
+ * argmax and accept_len of y as vqv_verify with B*T == M. Where it applies
+ * (M <= 8, bf16/fp16 activations, K within the single-row-set kernel's LDS
+ * budget: K <= 5120 for every N), the argmax is fused into the projection's
+ * epilogue, so the logits are never read back ("dspark: fold first-token
+ * forward into verify + bit-exact M5 Metal decode wins", first commit: the
+ * fused argmax of the CUDA path and the single accept loop; "perf: tune
+ * DFlash2 M=8 verification for M1 and M2", PR description: the verify
+ * projection at M=8). Elsewhere the two operations run back to back.
+ *
+ * Arguments
+ *   x, wq, scales, biases, M, K, N, group, act_dtype
+ *              as vqv_qgemm.
+ *   y          [M, N] fp32 logits, written; may be NULL when they are not
+ *              needed. 16-byte aligned.
+ *   draft, B, T, argmax, accept_len
+ *              as vqv_verify, with B*T == M (else VQV_ERR_ARG).
+ *   workspace  at least vqv_qgemm_verify_workspace_bytes(M, K, N, group,
+ *              act_dtype) bytes, 256-byte aligned. Calls that share a
+ *              workspace must not overlap in time (same stream, or
+ *              synchronized).
+ * The results are bit-identical to vqv_qgemm followed by vqv_verify on the
+ * same inputs.
+ */
+size_t vqv_qgemm_verify_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype);
+
+vqv_status vqv_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* scales,
+                            const uint16_t* biases, float* y, int M, int K, int N, int group,
+                            vqv_dtype act_dtype, const int32_t* draft, int B, int T,
+                            int32_t* argmax, int32_t* accept_len, void* workspace,
+                            size_t workspace_bytes, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

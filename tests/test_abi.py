@@ -36,7 +36,8 @@ def declared_functions():
 def test_header_declares_the_calls():
     assert declared_functions() == sorted(
         ["vqv_abi_version", "vqv_status_string", "vqv_qgemm_workspace_bytes", "vqv_qgemm",
-         "vqv_verify_workspace_bytes", "vqv_verify"])
+         "vqv_verify_workspace_bytes", "vqv_verify", "vqv_qgemm_verify_workspace_bytes",
+         "vqv_qgemm_verify"])
 
 
 def test_exports_every_declared_symbol(L):
@@ -63,6 +64,17 @@ def test_workspace_queries(L):
     assert L.vqv_verify_workspace_bytes(4, 16, 151936) == 64 * 38 * 8
     assert L.vqv_verify_workspace_bytes(1, 1, 1) == 8
     assert L.vqv_verify_workspace_bytes(0, 8, 10) == 0
+
+
+def test_fused_workspace_queries(L):
+    head = 256
+    fused = L.vqv_qgemm_verify_workspace_bytes(8, 5120, 17408, 64, BF16)
+    assert head < fused <= head + 64 * 1024  # per-group partials only
+    fallback = L.vqv_qgemm_verify_workspace_bytes(16, 512, 1000, 64, BF16)
+    assert fallback >= head + 16 * 1000 * 4  # room for the logits
+    assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 64, FP32) >= head + 8 * 1000 * 4
+    assert L.vqv_qgemm_verify_workspace_bytes(0, 512, 1000, 64, BF16) == 0
+    assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 32, BF16) == 0
 
 
 # Fabricated, well-aligned and non-overlapping device addresses.
@@ -97,6 +109,25 @@ def test_verify_rejects(L, kw, status):
     a.update(kw)
     assert L.vqv_verify(a["logits"], a["draft"], a["B"], a["T"], a["N"], a["argmax"], a["acc"],
                         a["ws"], a["wsb"], None) == status
+
+
+DR, AM, AC = 0x70000000, 0x80000000, 0x90000000
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), ARG), (dict(am=None), ARG), (dict(ac=None), ARG), (dict(dr=None), ARG),
+    (dict(B=2), ARG), (dict(T=4), ARG), (dict(M=65, B=65, T=1), ARG), (dict(group=128), UNSUP),
+    (dict(K=100), ARG), (dict(y=Y + 4), ALIGN), (dict(am=AM + 2), ALIGN), (dict(ws=None), WS),
+    (dict(wsb=8), WS), (dict(ws=WSP + 16), WS), (dict(am=X), ARG), (dict(ws=W), ARG),
+    (dict(y=DR), ARG), (dict(ac=AM + 16), ARG), (dict(K=16384 + 64), UNSUP),
+])
+def test_fused_rejects(L, kw, status):
+    a = dict(x=X, wq=W, s=S, b=B_, y=Y, M=8, K=512, N=1024, group=64, act=BF16, dr=DR, B=1, T=8,
+             am=AM, ac=AC, ws=WSP, wsb=1 << 20)
+    a.update(kw)
+    assert L.vqv_qgemm_verify(a["x"], a["wq"], a["s"], a["b"], a["y"], a["M"], a["K"], a["N"],
+                              a["group"], a["act"], a["dr"], a["B"], a["T"], a["am"], a["ac"],
+                              a["ws"], a["wsb"], None) == status
 
 
 def test_python_binding_raises_with_status(L):

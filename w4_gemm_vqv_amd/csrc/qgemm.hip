@@ -48,6 +48,7 @@
 // with the weights of its first step so that storing it never drains the
 // ring.
 
+#include "argmax.h"
 #include "vqv_internal.h"
 
 namespace vqv {
@@ -528,13 +529,6 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
 }
 
 
-// s_waitcnt immediate that waits until at most `vm` vector memory loads are
-// outstanding and leaves the other counters alone (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8).
-constexpr int vmcnt_wait(int vm) {
-  return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-}
-
 // LDS of qgemm_w4_m8: GP activation images and one zero image (more when the
 // staging rounds are padded), the row sums (16 floats per image), the (s, b)
 // table (G + 4 dwords per column), the partial-sum slots (two 8x16 tiles per
@@ -589,7 +583,7 @@ __device__ __forceinline__ float sum8_lanes(float s) {
 
 // ---------------------------------------------------------------------------
 // One row set (M <= 8), 16-bit activations, the work-group's whole K range in
-// LDS. Same per-step arithmetic as qgemm_w4 with R = 1; the work split and
+// LDS. With FUSED the greedy verify runs in the epilogue (VerifyArgs). Same per-step arithmetic as qgemm_w4 with R = 1; the work split and
 // the schedule differ:
 //  * Work is cut into blocks of DB consecutive group pairs of one column
 //    tile; the work-group's blocks, tile-major, are dealt to its NW waves as
@@ -615,11 +609,11 @@ __device__ __forceinline__ float sum8_lanes(float s) {
 //    the buffer): its activations, row sum, scale and bias are all zero, so
 //    it adds exactly nothing. Columns past the work-group's read zeros and
 //    are never stored.
-template <int ACT, int NW, int TW, int DB, int RB, int D0, int XB>
+template <int ACT, int NW, int TW, int DB, int RB, int D0, int XB, bool FUSED>
 __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
-    float* __restrict__ y, int M, int K, int N, int cols) {
+    float* __restrict__ y, int M, int K, int N, int cols, VerifyArgs va) {
   using TR = ActTraits<ACT>;
   static_assert(TR::parts == 1, "16-bit activations only");
   static_assert(TW <= NW, "a run must span at most two tiles");
@@ -929,8 +923,13 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
   flush(acc_tile > tfirst ? 1 : 0);
 
   // ---- reduce: each output tile adds the flushed partials of the runs that
-  // cover it, in wave order.
+  // cover it, in wave order. With the fused verify each thread also keeps the
+  // best (key, index) of the row its outputs belong to: output idx is row
+  // (idx >> 4) & 7, and NT is a multiple of 128, so that row is fixed per
+  // thread, (tid >> 4) & 7.
   __syncthreads();
+  unsigned bk = 0u;
+  int bi = INT_MAX;
   for (int idx = tid; idx < tiles * 128; idx += NT) {
     const int t = idx >> 7;
     const int within = idx & 127;                     // row * 16 + column
@@ -942,7 +941,32 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
     }
     const int m = within >> 4;
     const int c = t * 16 + (within & 15);
-    if (m < M && c < wgcols) y[(size_t)m * N + wg0 + c] = s;
+    if (m < M && c < wgcols) {
+      if (!FUSED || y) y[(size_t)m * N + wg0 + c] = s;
+      if (FUSED) take_better(bk, bi, order_key(s), wg0 + c);
+    }
+  }
+  if constexpr (!FUSED) return;
+
+  // ---- fused greedy verify, first half. The 16 lanes of one row in a wave
+  // reduce their bests; a work-group's row best combines its waves in wave
+  // order and is written as this group's partial for the finishing kernel.
+  static_assert(NT % 128 == 0 && NW % 2 == 0, "one row per thread in the epilogue");
+  best16(bk, bi);
+  unsigned* cand = reinterpret_cast<unsigned*>(lds);  // [NW][4] x (key, index)
+  if ((lane & 15) == 0) {
+    cand[(wave * 4 + (lane >> 4)) * 2] = bk;
+    cand[(wave * 4 + (lane >> 4)) * 2 + 1] = (unsigned)bi;
+  }
+  __syncthreads();
+  // Lane m < M of wave 0: row m is held by the waves of parity m / 4, in
+  // their quarter m % 4.
+  if (wave == 0 && lane < M) {
+    unsigned k = 0u;
+    int ix = INT_MAX;
+    for (int w = lane >> 2; w < NW; w += 2)
+      take_better(k, ix, cand[(w * 4 + (lane & 3)) * 2], (int)cand[(w * 4 + (lane & 3)) * 2 + 1]);
+    va.partials[(size_t)blockIdx.x * 8 + lane] = make_uint2(k, (unsigned)ix);
   }
 }
 
@@ -986,10 +1010,11 @@ hipError_t launch_w4(const void* x, const uint8_t* wq, const uint16_t* scales,
 template <int ACT, int NW, int DB, int RB, int XB, int D0 = 2>
 hipError_t launch_m8(const void* x, const uint8_t* wq, const uint16_t* scales,
                      const uint16_t* biases, float* y, int M, int K, int N, int cols,
-                     hipStream_t stream) {
+                     const VerifyArgs& va, hipStream_t stream) {
   constexpr int TW = 5;
   const M8Layout L = m8_layout(K >> 6, 16 * TW, NW, XB);
-  auto kern = qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB>;
+  auto kern = va.argmax ? qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, true>
+                        : qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, false>;
   if (L.total > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -998,7 +1023,7 @@ hipError_t launch_m8(const void* x, const uint8_t* wq, const uint16_t* scales,
   }
   const dim3 grid((N + cols - 1) / cols);
   hipLaunchKernelGGL(kern, grid, dim3(64 * NW), L.total, stream, x, wq, scales, biases, y, M,
-                     K, N, cols);
+                     K, N, cols, va);
   return hipGetLastError();
 }
 
@@ -1012,12 +1037,34 @@ constexpr int m8_xb(int K) { return K <= 2560 ? 5 : 10; }
 template <int ACT, int XB>
 hipError_t launch_m8_blocks(const void* x, const uint8_t* wq, const uint16_t* scales,
                             const uint16_t* biases, float* y, int M, int K, int N, int cols,
-                            hipStream_t s) {
+                            const VerifyArgs& va, hipStream_t s) {
   const int GP = ((K >> 6) + 1) >> 1;
-  if (GP % 5 == 0) return launch_m8<ACT, 8, 5, 1, XB>(x, wq, scales, biases, y, M, K, N, cols, s);
-  if (GP % 4 == 0) return launch_m8<ACT, 8, 4, 2, XB>(x, wq, scales, biases, y, M, K, N, cols, s);
-  if (GP % 2 == 0) return launch_m8<ACT, 8, 2, 4, XB>(x, wq, scales, biases, y, M, K, N, cols, s);
-  return launch_m8<ACT, 8, 1, 8, XB>(x, wq, scales, biases, y, M, K, N, cols, s);
+  if (GP % 5 == 0)
+    return launch_m8<ACT, 8, 5, 1, XB>(x, wq, scales, biases, y, M, K, N, cols, va, s);
+  if (GP % 4 == 0)
+    return launch_m8<ACT, 8, 4, 2, XB>(x, wq, scales, biases, y, M, K, N, cols, va, s);
+  if (GP % 2 == 0)
+    return launch_m8<ACT, 8, 2, 4, XB>(x, wq, scales, biases, y, M, K, N, cols, va, s);
+  return launch_m8<ACT, 8, 1, 8, XB>(x, wq, scales, biases, y, M, K, N, cols, va, s);
+}
+
+// Columns per work-group of qgemm_w4_m8 (an equal share of the CUs, at most
+// five tiles) and whether its LDS image fits.
+int m8_cols(int N) {
+  const int cus = device_cus();
+  const int share = ((N + cus - 1) / cus + 3) / 4 * 4;
+  return share < 80 ? share : 80;
+}
+bool m8_fits(int K) { return m8_layout(K >> 6, 80, 8, m8_xb(K)).total <= kLdsLimit; }
+
+template <int ACT>
+hipError_t launch_m8_any(const void* x, const uint8_t* wq, const uint16_t* scales,
+                         const uint16_t* biases, float* y, int M, int K, int N,
+                         const VerifyArgs& va, hipStream_t s) {
+  const int cols = m8_cols(N);
+  if (m8_xb(K) == 5)
+    return launch_m8_blocks<ACT, 5>(x, wq, scales, biases, y, M, K, N, cols, va, s);
+  return launch_m8_blocks<ACT, 10>(x, wq, scales, biases, y, M, K, N, cols, va, s);
 }
 
 // Configuration per problem. M <= 8 (one row set): when the work-group's
@@ -1028,16 +1075,9 @@ template <int ACT>
 hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                          const uint16_t* biases, float* y, int M, int K, int N,
                          hipStream_t s) {
-  if constexpr (ACT != ACT_FP32) if (M <= 8) {
-    // Columns per work-group: an equal share of the CUs, at most 5 tiles.
-    const int cus = device_cus();
-    const int share = ((N + cus - 1) / cus + 3) / 4 * 4;
-    const int cols = share < 80 ? share : 80;
-    if (m8_layout(K >> 6, 80, 8, m8_xb(K)).total <= kLdsLimit) {
-      if (m8_xb(K) == 5)
-        return launch_m8_blocks<ACT, 5>(x, wq, scales, biases, y, M, K, N, cols, s);
-      return launch_m8_blocks<ACT, 10>(x, wq, scales, biases, y, M, K, N, cols, s);
-    }
+  if constexpr (ACT != ACT_FP32) if (M <= 8 && m8_fits(K)) {
+    const VerifyArgs none{};
+    return launch_m8_any<ACT>(x, wq, scales, biases, y, M, K, N, none, s);
   }
   if (M <= 8) {
     const int cus = device_cus();
@@ -1077,6 +1117,25 @@ hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales
     case ACT_FP32: return dispatch_rows<ACT_FP32>(x, wq, scales, biases, y, M, K, N, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+int qgemm_verify_groups(int M, int K, int N, int act) {
+  // The projection kernel of the fused path writes one partial per
+  // work-group and row; verify_finish (verify.hip) reduces them.
+  if (M > 8 || act == ACT_FP32 || !m8_fits(K)) return 0;
+  const int cols = m8_cols(N);
+  return (N + cols - 1) / cols;
+}
+
+hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* scales,
+                               const uint16_t* biases, float* y, int M, int K, int N, int act,
+                               const VerifyArgs& va, hipStream_t stream) {
+  hipError_t e = hipErrorInvalidValue;
+  if (act == ACT_BF16) e = launch_m8_any<ACT_BF16>(x, wq, scales, biases, y, M, K, N, va, stream);
+  if (act == ACT_FP16) e = launch_m8_any<ACT_FP16>(x, wq, scales, biases, y, M, K, N, va, stream);
+  if (e != hipSuccess) return e;
+  return launch_verify_finish(va.partials, qgemm_verify_groups(M, K, N, act), va.draft, va.B,
+                              va.T, va.argmax, va.accept_len, stream);
 }
 
 }  // namespace vqv

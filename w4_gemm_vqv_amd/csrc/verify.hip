@@ -8,33 +8,19 @@
 // DFlash", commit message).
 //
 // Stage 1: one 256-thread work-group per (row, chunk of kVerifyChunk logits)
-// scans with 16-byte loads and reduces (key, index) pairs by wave shuffles,
-// then across the four waves in LDS. The key orders floats as unsigned ints
-// with every NaN above +inf and -0 folded onto +0; among equal keys the lower
-// index wins. That makes the result unique, so the reduction order cannot
-// change it.
+// scans with 16-byte loads and reduces (key, index) pairs (argmax.h) by wave
+// shuffles, then across the four waves in LDS.
 // Stage 2: one wave per sequence. Lane i reduces row i's chunk partials in
 // order, writes argmax, compares with draft i, and a ballot's count of
 // trailing ones is the accept length.
 
 #include <limits.h>
 
+#include "argmax.h"
 #include "vqv_internal.h"
 
 namespace vqv {
 namespace {
-
-__device__ __forceinline__ unsigned order_key(float v) {
-  unsigned u = __float_as_uint(v);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0xFFFFFFFFu;  // any NaN: above all
-  if (u == 0x80000000u) u = 0u;                              // -0 ties with +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Real values map to keys >= 0x007FFFFF, so (0, INT_MAX) is "no candidate".
-__device__ __forceinline__ void take_better(unsigned& k, int& i, unsigned k2, int i2) {
-  if (k2 > k || (k2 == k && i2 < i)) { k = k2; i = i2; }
-}
 
 template <bool VEC4>
 __global__ __launch_bounds__(256) void verify_stage1(const float* __restrict__ logits, int N,
@@ -60,12 +46,7 @@ __global__ __launch_bounds__(256) void verify_stage1(const float* __restrict__ l
     for (int c = beg + threadIdx.x; c < end; c += 256) take_better(bk, bi, order_key(rp[c]), c);
   }
 
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const unsigned k2 = __shfl_xor(bk, off);
-    const int i2 = __shfl_xor(bi, off);
-    take_better(bk, bi, k2, i2);
-  }
+  wave_best(bk, bi);
   __shared__ unsigned sk[4];
   __shared__ int si[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -101,7 +82,45 @@ __global__ __launch_bounds__(64) void verify_stage2(const uint2* __restrict__ pa
   if (lane == 0) accept_len[b] = __builtin_ctzll(miss);
 }
 
+// The fused projection's second half: wave m reduces row m's per-group
+// partials (lanes stride over the groups, then a fixed-order lane tree), and
+// wave 0 walks every sequence.
+__global__ __launch_bounds__(512) void verify_finish(const uint2* __restrict__ part, int groups,
+                                                     const int32_t* __restrict__ draft, int B,
+                                                     int T, int32_t* __restrict__ argmax,
+                                                     int32_t* __restrict__ accept_len) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rows = B * T;
+  const int d = wave == 0 ? draft_of_row(draft, B, T) : -1;
+  __shared__ int best[8];
+  if (wave < rows) {
+    unsigned k = 0u;
+    int ix = INT_MAX;
+    for (int g = lane; g < groups; g += 64) {
+      const uint2 v = part[(size_t)g * 8 + wave];
+      take_better(k, ix, v.x, (int)v.y);
+    }
+    best64(k, ix);
+    if (lane == 0) {
+      argmax[wave] = ix;
+      best[wave] = ix;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int len = accept_lengths_of(lane < rows ? best[lane] : -1, d, B, T);
+    if (lane < B) accept_len[lane] = len;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_verify_finish(const uint2* partials, int groups, const int32_t* draft, int B,
+                                int T, int32_t* argmax, int32_t* accept_len, hipStream_t stream) {
+  hipLaunchKernelGGL(verify_finish, dim3(1), dim3(512), 0, stream, partials, groups, draft, B, T,
+                     argmax, accept_len);
+  return hipGetLastError();
+}
 
 hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int T, int N,
                          int32_t* argmax, int32_t* accept_len, void* partials,

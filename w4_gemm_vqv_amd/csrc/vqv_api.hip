@@ -77,6 +77,77 @@ vqv_status vqv_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
   return e == hipSuccess ? VQV_OK : VQV_ERR_HIP;
 }
 
+// Fused projection + verify: a 256-byte head (unused), then either the fused
+// kernel's per-group partials or, where the fused kernel does not apply,
+// room for the logits and the two-stage verify's partials.
+constexpr size_t kHead = 256;
+
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t vqv_qgemm_verify_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype) {
+  if (M < 1 || M > kMaxRows || N < 1 || K < kGroup || group != kGroup) return 0;
+  const int groups = vqv::qgemm_verify_groups(M, K, N, (int)act_dtype);
+  if (groups > 0) return kHead + (size_t)groups * 8 * 8;
+  return kHead + align256((size_t)M * N * 4) + (size_t)M * vqv::verify_chunks(N) * 8;
+}
+
+vqv_status vqv_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* scales,
+                            const uint16_t* biases, float* y, int M, int K, int N, int group,
+                            vqv_dtype act_dtype, const int32_t* draft, int B, int T,
+                            int32_t* argmax, int32_t* accept_len, void* workspace,
+                            size_t workspace_bytes, void* hip_stream) {
+  if (!x || !wq || !scales || !biases || !argmax || !accept_len) return VQV_ERR_ARG;
+  if (act_dtype != VQV_BF16 && act_dtype != VQV_FP16 && act_dtype != VQV_FP32)
+    return VQV_ERR_ARG;
+  if (M < 1 || M > kMaxRows || N < 1 || K < kGroup) return VQV_ERR_ARG;
+  if (B < 1 || T < 1 || T > kMaxBlock || (long long)B * T != M) return VQV_ERR_ARG;
+  if (T > 1 && !draft) return VQV_ERR_ARG;
+  if (group != kGroup) return VQV_ERR_UNSUPPORTED;
+  if (K % kGroup) return VQV_ERR_ARG;
+  if (K > vqv::kMaxK) return VQV_ERR_UNSUPPORTED;
+  const size_t esz = (size_t)act_size(act_dtype);
+  const size_t xbytes = (size_t)M * K * esz;
+  const size_t wbytes = (size_t)N * (K / 2);
+  const size_t sbytes = (size_t)N * (K / kGroup) * 2;
+  const size_t ybytes = (size_t)M * N * 4;
+  if (xbytes >= (1ull << 31) || wbytes >= (1ull << 32) || (size_t)N * (K / kGroup) >= (1ull << 31) ||
+      ybytes >= (1ull << 31))
+    return VQV_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(scales, 2) || !aligned(biases, 2) ||
+      (y && !aligned(y, 16)) || !aligned(argmax, 4) || !aligned(accept_len, 4) ||
+      (draft && !aligned(draft, 4)))
+    return VQV_ERR_ALIGN;
+  const size_t need = vqv_qgemm_verify_workspace_bytes(M, K, N, group, act_dtype);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return VQV_ERR_WORKSPACE;
+  const size_t dbytes = draft ? (size_t)B * (T - 1) * 4 : 0;
+  const void* ins[4] = {x, wq, scales, biases};
+  const size_t insz[4] = {xbytes, wbytes, sbytes, sbytes};
+  void* outs[4] = {y, argmax, accept_len, workspace};
+  const size_t outsz[4] = {y ? ybytes : 0, (size_t)M * 4, (size_t)B * 4, need};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 4; ++i)
+      if (overlaps(outs[o], outsz[o], ins[i], insz[i])) return VQV_ERR_ARG;
+    if (overlaps(outs[o], outsz[o], draft, dbytes)) return VQV_ERR_ARG;
+    for (int o2 = o + 1; o2 < 4; ++o2)
+      if (overlaps(outs[o], outsz[o], outs[o2], outsz[o2])) return VQV_ERR_ARG;
+  }
+  (void)hipGetLastError();
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  hipError_t e;
+  if (vqv::qgemm_verify_groups(M, K, N, (int)act_dtype) > 0) {
+    vqv::VerifyArgs va{draft, B, T, argmax, accept_len, reinterpret_cast<uint2*>(ws + kHead)};
+    e = vqv::launch_qgemm_verify(x, wq, scales, biases, y, M, K, N, (int)act_dtype, va, st);
+  } else {
+    float* logits = y ? y : reinterpret_cast<float*>(ws + kHead);
+    void* part = ws + kHead + align256(ybytes);
+    e = vqv::launch_qgemm(x, wq, scales, biases, logits, M, K, N, (int)act_dtype, st);
+    if (e == hipSuccess)
+      e = vqv::launch_verify(logits, draft, B, T, N, argmax, accept_len, part, st);
+  }
+  return e == hipSuccess ? VQV_OK : VQV_ERR_HIP;
+}
+
 size_t vqv_verify_workspace_bytes(int B, int T, int N) {
   if (B < 1 || T < 1 || N < 1) return 0;
   return (size_t)B * T * vqv::verify_chunks(N) * 8;

@@ -18,6 +18,32 @@ hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales
                         const uint16_t* biases, float* y, int M, int K, int N, int act,
                         hipStream_t stream);
 
+// Greedy verify fused into the projection's epilogue (M = B*T <= 8, 16-bit
+// activations, K within the single-row-set kernel's LDS budget): each
+// work-group reduces its columns to one (key, index) partial per row, and a
+// one-work-group kernel then reduces the partials, writes argmax and the
+// accept lengths.
+struct VerifyArgs {
+  const int32_t* draft;   // [B, T-1]
+  int B, T;
+  int32_t* argmax;        // [B*T]
+  int32_t* accept_len;    // [B]
+  uint2* partials;        // [work-groups][8]: (key, index)
+};
+
+// Reduces `groups` partials per row ([groups][8], rows 0..B*T-1 <= 8) to the
+// argmax of each row, then the accept walk of each sequence.
+hipError_t launch_verify_finish(const uint2* partials, int groups, const int32_t* draft, int B,
+                                int T, int32_t* argmax, int32_t* accept_len, hipStream_t stream);
+
+// The number of work-groups the fused projection launches, or 0 when the
+// fused path does not take this problem.
+int qgemm_verify_groups(int M, int K, int N, int act);
+
+hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* scales,
+                               const uint16_t* biases, float* y, int M, int K, int N, int act,
+                               const VerifyArgs& va, hipStream_t stream);
+
 // Logits per verify work-group (one row, one chunk of columns).
 constexpr int kVerifyChunk = 4096;
 
