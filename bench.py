@@ -2,12 +2,14 @@
 """Throughput of the W4 verify projection + greedy verify on one MI355X.
 
 One step is the whole hot path over one verify block: the W4 group-64 QMM
-y[M,N] = x[M,K] . W^T (vqv_qgemm), then the per-row argmax and accept walk
-over y (vqv_verify). The default workload is the target projection M=8,
-K=5120, N=17408 with bf16 activations and a verify block of T=8. Inputs are
-seeded synthetic tensors of that shape, resident in HBM before timing. The
-weights rotate through enough copies that every step streams them from HBM
-rather than from the 256 MB Infinity Cache.
+y[M,N] = x[M,K] . W^T, then the per-row argmax and accept walk over y. By
+default a step is one vqv_qgemm_verify call (the argmax fused into the QMM
+epilogue, a one-work-group kernel finishing the rows and the walk); with
+--path separate it is vqv_qgemm followed by vqv_verify. The default workload
+is the target projection M=8, K=5120, N=17408 with bf16 activations and a
+verify block of T=8. Inputs are seeded synthetic tensors of that shape,
+resident in HBM before timing. The weights rotate through enough copies that
+every step streams them from HBM rather than from the 256 MB Infinity Cache.
 
 Prints one JSON line. `value` is verified rows per second (M rows per step),
 timed over the K steps captured as one HIP graph, so the host's launch cost
@@ -54,7 +56,7 @@ def qgemm_bytes(M, K, N, esz):
     return K * N // 2 + 4 * N * (K // 64) + M * K * esz + 4 * M * N
 
 
-def traffic_record(workload, M, fused=False):
+def traffic_record(workload, M):
     """Measured HBM bytes per launch from committed rocprofv3 counter runs,
     valid only while the kernel source is unchanged."""
     path = os.path.join(ROOT, "profiles", "qgemm_traffic.json")
@@ -62,7 +64,7 @@ def traffic_record(workload, M, fused=False):
         return None
     rec = json.load(open(path))
     src = open(os.path.join(ROOT, "w4_gemm_vqv_amd", "csrc", "qgemm.hip"), "rb").read()
-    entry = rec.get("workloads", {}).get(f"{workload}:M={M}" + (":fused" if fused else ""))
+    entry = rec.get("workloads", {}).get(f"{workload}:M={M}")
     if not entry or rec.get("qgemm_hip_sha256") != hashlib.sha256(src).hexdigest():
         return None
     return entry["fetch_bytes"] + entry["write_bytes"]
@@ -127,7 +129,7 @@ def _counter_rows(run_dir):
     return rows
 
 
-def write_traffic(fetch_dir, write_dir, workload, M, fused):
+def write_traffic(fetch_dir, write_dir, workload, M):
     """Per-launch HBM bytes of the QMM from a FETCH_SIZE pass and a WRITE_SIZE
     pass of `bench.py --counter-pass`, each scaled by what the same counter
     reads for the copy kernel (COPY_PROBE_BYTES read and written per launch)."""
@@ -137,7 +139,7 @@ def write_traffic(fetch_dir, write_dir, workload, M, fused):
         for kname, cname, v in _counter_rows(run_dir):
             if cname != counter:
                 continue
-            if "qgemm_w4" in kname and (", true>" in kname) == fused:
+            if "qgemm_w4" in kname and ", true>" not in kname:
                 q.append(v)
             elif "neg" in kname.lower():
                 cp.append(v)
@@ -157,7 +159,7 @@ def write_traffic(fetch_dir, write_dir, workload, M, fused):
     sha = hashlib.sha256(src).hexdigest()
     if rec.get("qgemm_hip_sha256") != sha:
         rec = {"qgemm_hip_sha256": sha, "workloads": {}}
-    key = f"{workload}:M={M}" + (":fused" if fused else "")
+    key = f"{workload}:M={M}"
     rec["workloads"][key] = out
     json.dump(rec, open(path, "w"), indent=1, sort_keys=True)
     print(json.dumps({key: out}))
@@ -186,8 +188,7 @@ def main():
     if args.write_traffic:
         import gen
         write_traffic(*args.write_traffic, args.workload,
-                      args.m or gen.CONFIGS[args.workload]["M"],
-                      args.path == "fused" and args.workload in VERIFY)
+                      args.m or gen.CONFIGS[args.workload]["M"])
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -274,13 +275,13 @@ def main():
         # QMM over every weight copy twice, then a plain copy kernel of known
         # size whose counter reading calibrates bytes per counted unit.
         for i in range(2 * R):
-            (fused if use_fused else qmm)(i, stream)
+            qmm(i, stream)
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        log(f"counter pass done: {2 * R} {'fused ' if use_fused else ''}QMM launches, 3 copy launches of "
+        log(f"counter pass done: {2 * R} QMM launches, 3 copy launches of "
             f"{COPY_PROBE_BYTES} bytes each way")
         return
 
@@ -345,12 +346,13 @@ def main():
         f_runs = [timed(g_f) * 1e3 / nq for _ in range(5)]
 
     qb = qgemm_bytes(M, K, N, esz)
-    # The dominant kernel: the step's projection kernel (with the fused verify
-    # when the step uses it; its extra traffic is 8 bytes per row and group).
-    k_us = statistics.fmean(f_runs) if use_fused else q_mean
+    # The dominant kernel is the projection. Its launches are timed in a graph
+    # of their own (the fused step's instance adds only the per-group argmax
+    # epilogue, 8 bytes per row and work-group, and is timed with the finish
+    # kernel in fused_us_mean).
+    k_us = q_mean
     achieved = qb / (k_us * 1e-6) / 1e9
-    kname = ("qgemm_w4_m8 (fused verify)" if use_fused else
-             "qgemm_w4_m8" if M <= 8 and act != "fp32" else "qgemm_w4")
+    kname = "qgemm_w4_m8" if M <= 8 and act != "fp32" else "qgemm_w4"
     out = {
         "metric": METRIC,
         "value": M / (ms_step * 1e-3),
@@ -377,7 +379,7 @@ def main():
         "step_path": "fused" if use_fused else "separate",
         "step_hbm_gbs": (qb + (4 * M * N if T else 0)) / (ms_step * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_record(args.workload, M, use_fused),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_record(args.workload, M),
                      "kernel": kname, "bytes_per_launch": qb, "us_per_launch": k_us},
         "cpu_baseline": None,
     }
