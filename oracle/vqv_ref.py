@@ -13,7 +13,9 @@ What it computes, step by step, is the plain definition of the operation:
 4. ``argmax_ref``: per row, the lowest index holding the maximum; -0 and +0
    are equal; any NaN wins and the first NaN is taken.
 5. ``accept_walk_ref`` and ``verify_ref``: per sequence, the number of
-   leading drafts equal to the target's argmax of the row before them.
+   leading drafts equal to the target's argmax of the row before them,
+   optionally capped by the sequence's count of valid drafts.
+6. ``margin_ref``: per row, top-1 minus top-2 in fp32.
 
 Sources on the pages:
 
@@ -117,17 +119,52 @@ def argmax_ref(v: np.ndarray) -> int:
     return int(np.flatnonzero(v == top)[0])
 
 
-def accept_walk_ref(row_argmax: np.ndarray, draft: np.ndarray, T: int) -> int:
+def margin_ref(v: np.ndarray) -> np.float32:
+    """Top-1 minus top-2 of one fp32 row, in fp32.
+
+    The margin the verifier's gate compares with a bar ("dspark: fold
+    first-token forward into verify + bit-exact M5 Metal decode wins", first
+    commit: the target's top-1 minus top-2 logit margin gate). Top-2 is the
+    largest value at any index other than the argmax, so a tied maximum gives
+    0 (-0 and +0 tie; so do two +inf or two -inf). A row holding a NaN gives
+    NaN; a row of one value gives +inf (no competitor). Otherwise the
+    difference is rounded to fp32, as the GPU computes it.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    if np.isnan(v).any():
+        return np.float32(np.nan)
+    if v.size == 1:
+        return np.float32(np.inf)
+    i = argmax_ref(v)
+    top = v[i]
+    second = np.delete(v, i).max()
+    if second == top:
+        return np.float32(0.0)
+    return np.float32(top) - np.float32(second)
+
+
+def accept_walk_ref(row_argmax: np.ndarray, draft: np.ndarray, T: int,
+                    draft_len: int | None = None) -> int:
     """Accepted drafts of one sequence: leading i < T-1 with
-    argmax[i] == draft[i]. Row i's prediction checks the token fed at row i+1."""
+    argmax[i] == draft[i]. Row i's prediction checks the token fed at row i+1.
+
+    With draft_len, only drafts i < draft_len are walked; it is clamped to
+    0..T-1. A sequence's block may hold fewer valid drafts than T-1: the
+    batched loop's rows have different live lengths ("perf(speculative):
+    commit per-row accepts in batched DFlash", commit message), and a block
+    can end in a partial tail ("perf: tune DFlash2 M=8 verification for M1
+    and M2", Validation).
+    """
+    limit = T - 1 if draft_len is None else min(max(int(draft_len), 0), T - 1)
     L = 0
-    while L < T - 1 and int(row_argmax[L]) == int(draft[L]):
+    while L < limit and int(row_argmax[L]) == int(draft[L]):
         L += 1
     return L
 
 
-def verify_ref(logits: np.ndarray, draft, B: int, T: int):
-    """logits [B*T, N] -> (argmax [B*T] int32, accept_len [B] int32)."""
+def verify_ref(logits: np.ndarray, draft, B: int, T: int, draft_len=None, margin=False):
+    """logits [B*T, N] -> (argmax [B*T] int32, accept_len [B] int32), and the
+    margins [B*T] fp32 when margin=True. draft_len [B] limits each walk."""
     logits = np.asarray(logits)
     if logits.shape[0] != B * T:
         raise ValueError("logits must have B*T rows")
@@ -136,6 +173,10 @@ def verify_ref(logits: np.ndarray, draft, B: int, T: int):
         d = np.asarray(draft).reshape(B, T - 1)
     else:
         d = np.zeros((B, 0), dtype=np.int32)
-    acc = np.array([accept_walk_ref(a[b * T:(b + 1) * T], d[b], T) for b in range(B)],
+    lens = [None] * B if draft_len is None else [int(v) for v in np.asarray(draft_len)]
+    acc = np.array([accept_walk_ref(a[b * T:(b + 1) * T], d[b], T, lens[b]) for b in range(B)],
                    dtype=np.int32)
+    if margin:
+        m = np.array([margin_ref(logits[r]) for r in range(B * T)], dtype=np.float32)
+        return a, acc, m
     return a, acc

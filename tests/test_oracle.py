@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import gen
-from oracle import (accept_walk_ref, argmax_ref, decode_act, dequantize, qgemm_ref,
+from oracle import (margin_ref, accept_walk_ref, argmax_ref, decode_act, dequantize, qgemm_ref,
                     unpack_codes, verify_ref)
 
 # ---------------------------------------------------------------- brute force
@@ -349,3 +349,69 @@ def test_drafts_builder_realises_accept_lengths():
     for L0 in range(T):
         d = gen.make_drafts(a, B, T, N, seed=1, accept=np.full(B, L0))
         assert all(accept_walk_ref(a[b * T:(b + 1) * T], d[b], T) == L0 for b in range(B))
+
+
+# ---------------------------------------------------------------- margin
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_margin_matches_sorted_top_two(seed):
+    """Rows with distinct values: the two largest from a library sort."""
+    rng = np.random.default_rng(seed)
+    for n in (2, 3, 17, 1000):
+        v = rng.standard_normal(n).astype(np.float32)
+        v = np.unique(v)  # distinct values (sorted); shuffle them back
+        rng.shuffle(v)
+        srt = np.sort(v)
+        assert margin_ref(v) == np.float32(srt[-1]) - np.float32(srt[-2])
+
+
+def test_margin_hand_cases():
+    f = np.float32
+    assert margin_ref(np.array([1, 3, 2], f)) == f(1.0)
+    assert margin_ref(np.array([3, 3, 1], f)) == f(0.0)            # tied maximum
+    assert margin_ref(np.array([-0.0, 0.0], f)) == f(0.0)          # signed zeros tie
+    assert margin_ref(np.array([np.inf, np.inf, 1], f)) == f(0.0)  # tied +inf
+    assert margin_ref(np.array([-np.inf, -np.inf], f)) == f(0.0)   # tied -inf
+    assert margin_ref(np.array([np.inf, 1], f)) == f(np.inf)
+    assert margin_ref(np.array([2, -np.inf], f)) == f(np.inf)
+    assert margin_ref(np.array([5], f)) == f(np.inf)                # no competitor
+    assert np.isnan(margin_ref(np.array([1, np.nan, 3], f)))
+    assert margin_ref(np.array([-1, -4, -2], f)) == f(1.0)
+    # fp32 rounding of the difference: 1 - 2^-30 is not representable
+    assert margin_ref(np.array([1.0, 2.0 ** -30], f)) == f(1.0)
+
+
+def test_margin_through_verify():
+    rng = np.random.default_rng(3)
+    lg = rng.standard_normal((6, 50)).astype(np.float32)
+    a, acc, m = verify_ref(lg, np.zeros((2, 2), np.int32), 2, 3, margin=True)
+    for r in range(6):
+        top = np.sort(lg[r])[-2:]
+        assert m[r] == np.float32(top[1]) - np.float32(top[0])
+
+
+# ---------------------------------------------------------------- valid draft length
+
+
+def test_walk_draft_len_caps_the_walk():
+    a = np.array([5, 6, 7, 8, 9])
+    d = np.array([5, 6, 7, 8])       # every draft matches: natural walk 4 (T=5)
+    assert accept_walk_ref(a, d, 5) == 4
+    assert [accept_walk_ref(a, d, 5, L) for L in range(6)] == [0, 1, 2, 3, 4, 4]
+    assert accept_walk_ref(a, d, 5, -3) == 0      # clamped to 0
+    assert accept_walk_ref(a, d, 5, 99) == 4      # clamped to T-1
+    d2 = np.array([5, 0, 7, 8])      # miss at 1: the cap never extends a walk
+    assert [accept_walk_ref(a, d2, 5, L) for L in range(5)] == [0, 1, 1, 1, 1]
+
+
+def test_verify_draft_len_per_sequence():
+    rng = np.random.default_rng(9)
+    B, T, N = 3, 6, 40
+    lg = rng.standard_normal((B * T, N)).astype(np.float32)
+    a = np.array([int(np.argmax(r)) for r in lg])
+    draft = np.stack([a[b * T:b * T + T - 1] for b in range(B)])  # full accept
+    _, acc = verify_ref(lg, draft, B, T)
+    assert acc.tolist() == [T - 1] * B
+    _, acc = verify_ref(lg, draft, B, T, draft_len=np.array([0, 3, 5]))
+    assert acc.tolist() == [0, 3, 5]

@@ -26,11 +26,22 @@ MUTANTS = {
                         "return int(np.flatnonzero(v == top)[-1])"),
     "nan_ignored": ("if nan.any():\n        return int(np.flatnonzero(nan)[0])",
                     "if False:\n        pass\n    v = np.where(nan, -np.inf, v)"),
-    "walk_off_by_one": ("while L < T - 1 and int(row_argmax[L]) == int(draft[L]):",
-                        "while L < T - 1 and int(row_argmax[L + 1]) == int(draft[L]):"),
+    "walk_off_by_one": ("while L < limit and int(row_argmax[L]) == int(draft[L]):",
+                        "while L < limit and int(row_argmax[L + 1]) == int(draft[L]):"),
     "walk_counts_all_matches": (
-        "while L < T - 1 and int(row_argmax[L]) == int(draft[L]):\n        L += 1",
-        "for i in range(T - 1):\n        L += int(int(row_argmax[i]) == int(draft[i]))"),
+        "while L < limit and int(row_argmax[L]) == int(draft[L]):\n        L += 1",
+        "for i in range(limit):\n        L += int(int(row_argmax[i]) == int(draft[i]))"),
+    "walk_ignores_draft_len": ("limit = T - 1 if draft_len is None else min(max(int(draft_len), 0), T - 1)",
+                               "limit = T - 1"),
+    "walk_draft_len_off_by_one": (
+        "limit = T - 1 if draft_len is None else min(max(int(draft_len), 0), T - 1)",
+        "limit = T - 1 if draft_len is None else min(max(int(draft_len) + 1, 0), T - 1)"),
+    "margin_distinct_second": ("second = np.delete(v, i).max()",
+                               "second = v[v != top].max() if (v != top).any() else top"),
+    "margin_ignores_nan": ("if np.isnan(v).any():\n        return np.float32(np.nan)",
+                           "if False:\n        pass\n    v = np.where(np.isnan(v), -np.inf, v)"),
+    "margin_sign": ("return np.float32(top) - np.float32(second)",
+                    "return np.float32(second) - np.float32(top)"),
     "bf16_decode_shift": ("u = np.asarray(x, dtype=np.uint16).astype(np.uint32) << 16",
                           "u = np.asarray(x, dtype=np.uint16).astype(np.uint32) << 15"),
     "fp16_scale_as_bf16": (
