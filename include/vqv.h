@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define VQV_ABI_VERSION 1
+#define VQV_ABI_VERSION 2
 
 typedef enum {
   VQV_BF16 = 0, /* bfloat16 activations                                  */
@@ -117,14 +117,46 @@ vqv_status vqv_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
  *               argmax[b*T+i] == draft[b,i] for every i < L. The bonus token
  *               argmax[b*T+L] is implied; tokens committed = L + 1.
  *   B >= 1, 1 <= T <= 64, N >= 1, B*T*N < 2^31.
- *   workspace   at least vqv_verify_workspace_bytes(B, T, N) bytes.
+ *   workspace   at least vqv_verify_workspace_bytes(B, T, N) bytes, 16-byte
+ *               aligned; its contents on entry do not matter.
  * Draft ids are compared as plain int32: ids outside [0, N) never match.
+ * No output may overlap an input, another output or the workspace
+ * (VQV_ERR_ARG).
  */
 size_t vqv_verify_workspace_bytes(int B, int T, int N);
 
 vqv_status vqv_verify(const float* logits, const int32_t* draft, int B, int T, int N,
                       int32_t* argmax, int32_t* accept_len, void* workspace,
                       size_t workspace_bytes, void* hip_stream);
+
+/*
+ * vqv_verify with two optional extras (either may be NULL; with both NULL
+ * the call is vqv_verify):
+ *   draft_len   [B] int32 input: sequence b holds draft_len[b] valid drafts,
+ *               clamped to 0..T-1, and its walk stops there, so accept_len[b]
+ *               <= clamp(draft_len[b]). In a batched round loop the live
+ *               sequences carry blocks of different valid lengths, and a
+ *               block may end in a partial tail ("perf(speculative): commit
+ *               per-row accepts in batched DFlash", commit message: each row
+ *               commits its own count; "perf: tune DFlash2 M=8 verification
+ *               for M1 and M2", Validation: the partial-tail case). Drafts
+ *               past the valid length do not affect the result, but draft
+ *               must still hold all B*(T-1) entries. 4-byte aligned.
+ *   margin      [B*T] fp32 output: top-1 minus top-2 of each row, where top-2
+ *               is the largest value at any index other than the argmax; the
+ *               value a margin gate compares with its bar ("dspark: fold
+ *               first-token forward into verify + bit-exact M5 Metal decode
+ *               wins", first commit: the top-1/top-2 margin gate). A tied
+ *               maximum gives 0 (-0 and +0 tie, as do two infinities of one
+ *               sign), a row holding NaN gives NaN, a row of one value (N == 1)
+ *               gives +inf; otherwise it is the fp32 difference, rounded to
+ *               nearest. 4-byte aligned.
+ * argmax and accept_len are as in vqv_verify; the workspace is the same.
+ */
+vqv_status vqv_verify_ex(const float* logits, const int32_t* draft, const int32_t* draft_len,
+                         int B, int T, int N, int32_t* argmax, int32_t* accept_len,
+                         float* margin, void* workspace, size_t workspace_bytes,
+                         void* hip_stream);
 
 /*
  * Projection and greedy verify in one call: y = x . W^T as vqv_qgemm, then
@@ -158,6 +190,20 @@ vqv_status vqv_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* sc
                             vqv_dtype act_dtype, const int32_t* draft, int B, int T,
                             int32_t* argmax, int32_t* accept_len, void* workspace,
                             size_t workspace_bytes, void* hip_stream);
+
+/*
+ * vqv_qgemm_verify with vqv_verify_ex's two optional extras: draft_len [B]
+ * (the valid drafts of each sequence) and margin [B*T] (top-1 minus top-2 of
+ * each logits row). On the fused path the projection's epilogue keeps each
+ * row's two best keys, so the margin costs no extra read of the logits. The
+ * results are bit-identical to vqv_qgemm followed by vqv_verify_ex.
+ */
+vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t* scales,
+                               const uint16_t* biases, float* y, int M, int K, int N, int group,
+                               vqv_dtype act_dtype, const int32_t* draft,
+                               const int32_t* draft_len, int B, int T, int32_t* argmax,
+                               int32_t* accept_len, float* margin, void* workspace,
+                               size_t workspace_bytes, void* hip_stream);
 
 #ifdef __cplusplus
 }

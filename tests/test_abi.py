@@ -36,8 +36,8 @@ def declared_functions():
 def test_header_declares_the_calls():
     assert declared_functions() == sorted(
         ["vqv_abi_version", "vqv_status_string", "vqv_qgemm_workspace_bytes", "vqv_qgemm",
-         "vqv_verify_workspace_bytes", "vqv_verify", "vqv_qgemm_verify_workspace_bytes",
-         "vqv_qgemm_verify"])
+         "vqv_verify_workspace_bytes", "vqv_verify", "vqv_verify_ex",
+         "vqv_qgemm_verify_workspace_bytes", "vqv_qgemm_verify", "vqv_qgemm_verify_ex"])
 
 
 def test_exports_every_declared_symbol(L):
@@ -52,7 +52,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.vqv_abi_version() == 1
+    assert L.vqv_abi_version() == 2
     for s in range(6):
         assert L.vqv_status_string(s)
     assert L.vqv_status_string(99) == b"unknown status"
@@ -60,16 +60,17 @@ def test_version_and_strings(L):
 
 def test_workspace_queries(L):
     assert L.vqv_qgemm_workspace_bytes(8, 5120, 17408, 64, BF16) == 0
-    assert L.vqv_verify_workspace_bytes(1, 8, 17408) == 8 * 5 * 8
-    assert L.vqv_verify_workspace_bytes(4, 16, 151936) == 64 * 38 * 8
-    assert L.vqv_verify_workspace_bytes(1, 1, 1) == 8
+    # one 16-byte top-two partial per (row, chunk of 4096 logits)
+    assert L.vqv_verify_workspace_bytes(1, 8, 17408) == 8 * 5 * 16
+    assert L.vqv_verify_workspace_bytes(4, 16, 151936) == 64 * 38 * 16
+    assert L.vqv_verify_workspace_bytes(1, 1, 1) == 16
     assert L.vqv_verify_workspace_bytes(0, 8, 10) == 0
 
 
 def test_fused_workspace_queries(L):
     head = 256
     fused = L.vqv_qgemm_verify_workspace_bytes(8, 5120, 17408, 64, BF16)
-    assert head < fused <= head + 64 * 1024  # per-group partials only
+    assert head < fused <= head + 128 * 1024  # per-group partials only
     fallback = L.vqv_qgemm_verify_workspace_bytes(16, 512, 1000, 64, BF16)
     assert fallback >= head + 16 * 1000 * 4  # room for the logits
     assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 64, FP32) >= head + 8 * 1000 * 4
@@ -102,6 +103,7 @@ def test_qgemm_rejects(L, kw, status):
     (dict(B=0), ARG), (dict(T=0), ARG), (dict(T=65), ARG), (dict(N=0), ARG),
     (dict(draft=None), ARG), (dict(B=2 ** 20, T=64, N=64), ARG), (dict(logits=X + 4), ALIGN),
     (dict(argmax=Y + 2), ALIGN), (dict(ws=None), WS), (dict(wsb=8), WS), (dict(ws=WSP + 4), WS),
+    (dict(ws=WSP + 8), WS),
     (dict(argmax=X + 64), ARG), (dict(acc=X), ARG), (dict(ws=X), ARG),
 ])
 def test_verify_rejects(L, kw, status):
@@ -128,6 +130,36 @@ def test_fused_rejects(L, kw, status):
     assert L.vqv_qgemm_verify(a["x"], a["wq"], a["s"], a["b"], a["y"], a["M"], a["K"], a["N"],
                               a["group"], a["act"], a["dr"], a["B"], a["T"], a["am"], a["ac"],
                               a["ws"], a["wsb"], None) == status
+
+
+LEN, MG = 0xA0000000, 0xB0000000
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dl=LEN + 2), ALIGN), (dict(mg=MG + 2), ALIGN), (dict(mg=Y), ARG), (dict(mg=S), ARG),
+    (dict(mg=X + 64), ARG), (dict(mg=WSP), ARG), (dict(dl=Y), ARG), (dict(dl=S), ARG),
+    (dict(dl=WSP + 32), ARG), (dict(mg=MG + 8, B=2, T=4, dl=MG + 16), ARG), (dict(mg=LEN), ARG),
+])
+def test_verify_ex_rejects(L, kw, status):
+    a = dict(logits=X, draft=W, dl=LEN, B=1, T=8, N=1024, argmax=Y, acc=S, mg=MG, ws=WSP,
+             wsb=1 << 20)
+    a.update(kw)
+    assert L.vqv_verify_ex(a["logits"], a["draft"], a["dl"], a["B"], a["T"], a["N"], a["argmax"],
+                           a["acc"], a["mg"], a["ws"], a["wsb"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dl=LEN + 2), ALIGN), (dict(mg=MG + 2), ALIGN), (dict(mg=AM), ARG), (dict(mg=Y), ARG),
+    (dict(mg=X), ARG), (dict(mg=WSP + 64), ARG), (dict(dl=AM), ARG), (dict(dl=AC), ARG),
+    (dict(dl=Y + 128), ARG), (dict(dl=WSP), ARG), (dict(mg=LEN), ARG), (dict(x=None), ARG),
+])
+def test_fused_ex_rejects(L, kw, status):
+    a = dict(x=X, wq=W, s=S, b=B_, y=Y, M=8, K=512, N=1024, group=64, act=BF16, dr=DR, dl=LEN,
+             B=1, T=8, am=AM, ac=AC, mg=MG, ws=WSP, wsb=1 << 20)
+    a.update(kw)
+    assert L.vqv_qgemm_verify_ex(a["x"], a["wq"], a["s"], a["b"], a["y"], a["M"], a["K"], a["N"],
+                                 a["group"], a["act"], a["dr"], a["dl"], a["B"], a["T"], a["am"],
+                                 a["ac"], a["mg"], a["ws"], a["wsb"], None) == status
 
 
 def test_python_binding_raises_with_status(L):

@@ -924,12 +924,11 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
 
   // ---- reduce: each output tile adds the flushed partials of the runs that
   // cover it, in wave order. With the fused verify each thread also keeps the
-  // best (key, index) of the row its outputs belong to: output idx is row
-  // (idx >> 4) & 7, and NT is a multiple of 128, so that row is fixed per
-  // thread, (tid >> 4) & 7.
+  // top two keys (and the best's index) of the row its outputs belong to:
+  // output idx is row (idx >> 4) & 7, and NT is a multiple of 128, so that row
+  // is fixed per thread, (tid >> 4) & 7.
   __syncthreads();
-  unsigned bk = 0u;
-  int bi = INT_MAX;
+  Top2 best = top2_none();
   for (int idx = tid; idx < tiles * 128; idx += NT) {
     const int t = idx >> 7;
     const int within = idx & 127;                     // row * 16 + column
@@ -943,30 +942,35 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
     const int c = t * 16 + (within & 15);
     if (m < M && c < wgcols) {
       if (!FUSED || y) y[(size_t)m * N + wg0 + c] = s;
-      if (FUSED) take_better(bk, bi, order_key(s), wg0 + c);
+      if (FUSED) top2_add(best, s, wg0 + c);
     }
   }
   if constexpr (!FUSED) return;
 
   // ---- fused greedy verify, first half. The 16 lanes of one row in a wave
-  // reduce their bests; a work-group's row best combines its waves in wave
-  // order and is written as this group's partial for the finishing kernel.
+  // reduce their top two; a work-group's row result combines its waves in
+  // wave order and is written as this group's partial for the finishing
+  // kernel. The candidates overlay the activation image, which the reduction
+  // above no longer reads.
   static_assert(NT % 128 == 0 && NW % 2 == 0, "one row per thread in the epilogue");
-  best16(bk, bi);
-  unsigned* cand = reinterpret_cast<unsigned*>(lds);  // [NW][4] x (key, index)
+  top2_best16(best);
+  unsigned* cand = reinterpret_cast<unsigned*>(lds);  // [NW][4] x (k1, i1, k2)
   if ((lane & 15) == 0) {
-    cand[(wave * 4 + (lane >> 4)) * 2] = bk;
-    cand[(wave * 4 + (lane >> 4)) * 2 + 1] = (unsigned)bi;
+    unsigned* p = cand + (wave * 4 + (lane >> 4)) * 3;
+    p[0] = best.k1;
+    p[1] = (unsigned)best.i1;
+    p[2] = best.k2;
   }
   __syncthreads();
   // Lane m < M of wave 0: row m is held by the waves of parity m / 4, in
   // their quarter m % 4.
   if (wave == 0 && lane < M) {
-    unsigned k = 0u;
-    int ix = INT_MAX;
-    for (int w = lane >> 2; w < NW; w += 2)
-      take_better(k, ix, cand[(w * 4 + (lane & 3)) * 2], (int)cand[(w * 4 + (lane & 3)) * 2 + 1]);
-    va.partials[(size_t)blockIdx.x * 8 + lane] = make_uint2(k, (unsigned)ix);
+    Top2 r = top2_none();
+    for (int w = lane >> 2; w < NW; w += 2) {
+      const unsigned* p = cand + (w * 4 + (lane & 3)) * 3;
+      top2_merge(r, p[0], (int)p[1], p[2]);
+    }
+    va.partials[(size_t)blockIdx.x * 8 + lane] = top2_pack(r);
   }
 }
 
@@ -1134,8 +1138,7 @@ hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t*
   if (act == ACT_BF16) e = launch_m8_any<ACT_BF16>(x, wq, scales, biases, y, M, K, N, va, stream);
   if (act == ACT_FP16) e = launch_m8_any<ACT_FP16>(x, wq, scales, biases, y, M, K, N, va, stream);
   if (e != hipSuccess) return e;
-  return launch_verify_finish(va.partials, qgemm_verify_groups(M, K, N, act), va.draft, va.B,
-                              va.T, va.argmax, va.accept_len, stream);
+  return launch_verify_finish(va.partials, qgemm_verify_groups(M, K, N, act), va, stream);
 }
 
 }  // namespace vqv

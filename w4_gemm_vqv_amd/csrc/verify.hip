@@ -8,11 +8,15 @@
 // DFlash", commit message).
 //
 // Stage 1: one 256-thread work-group per (row, chunk of kVerifyChunk logits)
-// scans with 16-byte loads and reduces (key, index) pairs (argmax.h) by wave
-// shuffles, then across the four waves in LDS.
-// Stage 2: one wave per sequence. Lane i reduces row i's chunk partials in
-// order, writes argmax, compares with draft i, and a ballot's count of
-// trailing ones is the accept length.
+// scans with 16-byte loads and reduces top-two partials (argmax.h: best key,
+// its lowest index, best other key) across lanes by DPP and across the four
+// waves in LDS.
+// Stage 2: one work-group per sequence. A wave reduces one row's chunk
+// partials at a time (lanes over chunks, all loads in flight), writes argmax
+// (and the top-1 minus top-2 margin when asked); then wave 0 compares each
+// row's argmax with its draft, and a ballot's count of trailing ones is the
+// accept length. A sequence with fewer valid drafts (draft_len) stops its
+// walk there.
 
 #include <limits.h>
 
@@ -24,118 +28,139 @@ namespace {
 
 template <bool VEC4>
 __global__ __launch_bounds__(256) void verify_stage1(const float* __restrict__ logits, int N,
-                                                     int nchunks, uint2* __restrict__ part) {
+                                                     int nchunks, uint4* __restrict__ part) {
   const int row = blockIdx.x / nchunks;
   const int chunk = blockIdx.x - row * nchunks;
   const float* rp = logits + (size_t)row * N;
   const int beg = chunk * kVerifyChunk;
   const int end = min(N, beg + kVerifyChunk);
 
-  unsigned bk = 0u;
-  int bi = INT_MAX;
+  // Every load of the chunk goes out before the first compare.
+  Top2 t = top2_none();
   if constexpr (VEC4) {
+    constexpr int kPer = kVerifyChunk / (4 * 256);
     const float4* rp4 = reinterpret_cast<const float4*>(rp);
-    for (int q = (beg >> 2) + threadIdx.x; q < (end >> 2); q += 256) {
-      const float4 v = rp4[q];
-      take_better(bk, bi, order_key(v.x), 4 * q);
-      take_better(bk, bi, order_key(v.y), 4 * q + 1);
-      take_better(bk, bi, order_key(v.z), 4 * q + 2);
-      take_better(bk, bi, order_key(v.w), 4 * q + 3);
+    float4 v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int q = (beg >> 2) + threadIdx.x + 256 * j;
+      const float ninf = -__builtin_inff();
+      v[j] = q < (end >> 2) ? rp4[q] : make_float4(ninf, ninf, ninf, ninf);
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int q = (beg >> 2) + threadIdx.x + 256 * j;
+      if (q < (end >> 2)) {
+        top2_add(t, v[j].x, 4 * q);
+        top2_add(t, v[j].y, 4 * q + 1);
+        top2_add(t, v[j].z, 4 * q + 2);
+        top2_add(t, v[j].w, 4 * q + 3);
+      }
     }
   } else {
-    for (int c = beg + threadIdx.x; c < end; c += 256) take_better(bk, bi, order_key(rp[c]), c);
+    constexpr int kPer = kVerifyChunk / 256;
+    float v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int c = beg + threadIdx.x + 256 * j;
+      v[j] = c < end ? rp[c] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int c = beg + threadIdx.x + 256 * j;
+      if (c < end) top2_add(t, v[j], c);
+    }
   }
 
-  wave_best(bk, bi);
-  __shared__ unsigned sk[4];
-  __shared__ int si[4];
+  t = top2_best64(t);
+  __shared__ uint4 sw[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) { sk[wave] = bk; si[wave] = bi; }
+  if (lane == 0) sw[wave] = top2_pack(t);
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w) take_better(bk, bi, sk[w], si[w]);
-    part[(size_t)row * nchunks + chunk] = make_uint2(bk, (unsigned)bi);
+    for (int w = 1; w < 4; ++w) top2_merge(t, sw[w]);
+    part[(size_t)row * nchunks + chunk] = top2_pack(t);
   }
 }
 
-__global__ __launch_bounds__(64) void verify_stage2(const uint2* __restrict__ part, int nchunks,
-                                                    const int32_t* __restrict__ draft, int T,
-                                                    int32_t* __restrict__ argmax,
-                                                    int32_t* __restrict__ accept_len) {
+// One work-group per sequence: wave w reduces the chunk partials of rows w,
+// w+8, ... (lanes over chunks), then wave 0 walks the sequence.
+__global__ __launch_bounds__(512) void verify_stage2(const uint4* __restrict__ part, int nchunks,
+                                                     VerifyArgs va) {
   const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  int a = -1;
-  if (lane < T) {
-    const size_t row = (size_t)b * T + lane;
-    const uint2* pr = part + row * nchunks;
-    unsigned bk = 0u;
-    int bi = INT_MAX;
-    for (int c = 0; c < nchunks; ++c) {
-      const uint2 v = pr[c];
-      take_better(bk, bi, v.x, (int)v.y);
-    }
-    a = bi;
-    argmax[row] = a;
-  }
-  const bool hit = (lane < T - 1) && (a == draft[(size_t)b * (T - 1) + lane]);
-  const unsigned long long miss = ~__ballot(hit);  // lane T-1 never hits, so miss != 0
-  if (lane == 0) accept_len[b] = __builtin_ctzll(miss);
-}
-
-// The fused projection's second half: wave m reduces row m's per-group
-// partials (lanes stride over the groups, then a fixed-order lane tree), and
-// wave 0 walks every sequence.
-__global__ __launch_bounds__(512) void verify_finish(const uint2* __restrict__ part, int groups,
-                                                     const int32_t* __restrict__ draft, int B,
-                                                     int T, int32_t* __restrict__ argmax,
-                                                     int32_t* __restrict__ accept_len) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rows = B * T;
-  const int d = wave == 0 ? draft_of_row(draft, B, T) : -1;
-  __shared__ int best[8];
-  if (wave < rows) {
-    unsigned k = 0u;
-    int ix = INT_MAX;
-    for (int g = lane; g < groups; g += 64) {
-      const uint2 v = part[(size_t)g * 8 + wave];
-      take_better(k, ix, v.x, (int)v.y);
-    }
-    best64(k, ix);
+  const int T = va.T;
+  int d = -1, limit = T - 1;  // limit: raw valid-draft count, clamped at the walk
+  if (wave == 0) {
+    d = draft_of_row(va.draft + (size_t)b * (T - 1), 1, T);
+    limit = draft_len_of_row(va.draft_len ? va.draft_len + b : nullptr, 1, T);
+  }
+  __shared__ int best[64];
+  for (int i = wave; i < T; i += 8) {
+    const size_t row = (size_t)b * T + i;
+    const Top2 t = top2_reduce_strided(part + row * nchunks, nchunks, 1);
     if (lane == 0) {
-      argmax[wave] = ix;
-      best[wave] = ix;
+      va.argmax[row] = t.i1;
+      if (va.margin) va.margin[row] = top2_margin(t);
+      best[i] = t.i1;
     }
   }
   __syncthreads();
   if (wave == 0) {
-    const int len = accept_lengths_of(lane < rows ? best[lane] : -1, d, B, T);
-    if (lane < B) accept_len[lane] = len;
+    const int len =
+        accept_lengths_of(lane < T ? best[lane] : -1, d, clamp_limit(limit, T), 1, T);
+    if (lane == 0) va.accept_len[b] = len;
+  }
+}
+
+// The fused projection's second half: wave m reduces row m's per-group
+// partials, and wave 0 walks every sequence.
+__global__ __launch_bounds__(512) void verify_finish(const uint4* __restrict__ part, int groups,
+                                                     VerifyArgs va) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int B = va.B, T = va.T, rows = B * T;
+  int d = -1, limit = T - 1;  // limit: raw valid-draft count, clamped at the walk
+  if (wave == 0) {
+    d = draft_of_row(va.draft, B, T);
+    limit = draft_len_of_row(va.draft_len, B, T);
+  }
+  __shared__ int best[8];
+  if (wave < rows) {
+    const Top2 t = top2_reduce_strided(part + wave, groups, 8);
+    if (lane == 0) {
+      va.argmax[wave] = t.i1;
+      if (va.margin) va.margin[wave] = top2_margin(t);
+      best[wave] = t.i1;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int len =
+        accept_lengths_of(lane < rows ? best[lane] : -1, d, clamp_limit(limit, T), B, T);
+    if (lane < B) va.accept_len[lane] = len;
   }
 }
 
 }  // namespace
 
-hipError_t launch_verify_finish(const uint2* partials, int groups, const int32_t* draft, int B,
-                                int T, int32_t* argmax, int32_t* accept_len, hipStream_t stream) {
-  hipLaunchKernelGGL(verify_finish, dim3(1), dim3(512), 0, stream, partials, groups, draft, B, T,
-                     argmax, accept_len);
+hipError_t launch_verify_finish(const uint4* partials, int groups, const VerifyArgs& va,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(verify_finish, dim3(1), dim3(512), 0, stream, partials, groups, va);
   return hipGetLastError();
 }
 
-hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int T, int N,
-                         int32_t* argmax, int32_t* accept_len, void* partials,
-                         hipStream_t stream) {
+hipError_t launch_verify(const float* logits, int N, const VerifyArgs& va, hipStream_t stream) {
   const int nchunks = verify_chunks(N);
-  const dim3 g1(nchunks * B * T);  // B*T*N < 2^31 keeps this below 2^31 / kVerifyChunk
-  uint2* part = static_cast<uint2*>(partials);
+  const dim3 g1(nchunks * va.B * va.T);  // B*T*N < 2^31 keeps this below 2^31 / kVerifyChunk
   if ((N & 3) == 0)
-    hipLaunchKernelGGL(verify_stage1<true>, g1, dim3(256), 0, stream, logits, N, nchunks, part);
+    hipLaunchKernelGGL(verify_stage1<true>, g1, dim3(256), 0, stream, logits, N, nchunks,
+                       va.partials);
   else
-    hipLaunchKernelGGL(verify_stage1<false>, g1, dim3(256), 0, stream, logits, N, nchunks, part);
+    hipLaunchKernelGGL(verify_stage1<false>, g1, dim3(256), 0, stream, logits, N, nchunks,
+                       va.partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_stage2, dim3(B), dim3(64), 0, stream, part, nchunks, draft, T,
-                     argmax, accept_len);
+  hipLaunchKernelGGL(verify_stage2, dim3(va.B), dim3(512), 0, stream, va.partials, nchunks, va);
   return hipGetLastError();
 }
 

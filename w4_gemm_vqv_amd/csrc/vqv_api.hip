@@ -87,8 +87,8 @@ static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 size_t vqv_qgemm_verify_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype) {
   if (M < 1 || M > kMaxRows || N < 1 || K < kGroup || group != kGroup) return 0;
   const int groups = vqv::qgemm_verify_groups(M, K, N, (int)act_dtype);
-  if (groups > 0) return kHead + (size_t)groups * 8 * 8;
-  return kHead + align256((size_t)M * N * 4) + (size_t)M * vqv::verify_chunks(N) * 8;
+  if (groups > 0) return kHead + (size_t)groups * 8 * 16;
+  return kHead + align256((size_t)M * N * 4) + (size_t)M * vqv::verify_chunks(N) * 16;
 }
 
 vqv_status vqv_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* scales,
@@ -96,6 +96,17 @@ vqv_status vqv_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* sc
                             vqv_dtype act_dtype, const int32_t* draft, int B, int T,
                             int32_t* argmax, int32_t* accept_len, void* workspace,
                             size_t workspace_bytes, void* hip_stream) {
+  return vqv_qgemm_verify_ex(x, wq, scales, biases, y, M, K, N, group, act_dtype, draft,
+                             nullptr, B, T, argmax, accept_len, nullptr, workspace,
+                             workspace_bytes, hip_stream);
+}
+
+vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t* scales,
+                               const uint16_t* biases, float* y, int M, int K, int N, int group,
+                               vqv_dtype act_dtype, const int32_t* draft,
+                               const int32_t* draft_len, int B, int T, int32_t* argmax,
+                               int32_t* accept_len, float* margin, void* workspace,
+                               size_t workspace_bytes, void* hip_stream) {
   if (!x || !wq || !scales || !biases || !argmax || !accept_len) return VQV_ERR_ARG;
   if (act_dtype != VQV_BF16 && act_dtype != VQV_FP16 && act_dtype != VQV_FP32)
     return VQV_ERR_ARG;
@@ -115,69 +126,82 @@ vqv_status vqv_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* sc
     return VQV_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(scales, 2) || !aligned(biases, 2) ||
       (y && !aligned(y, 16)) || !aligned(argmax, 4) || !aligned(accept_len, 4) ||
-      (draft && !aligned(draft, 4)))
+      (draft && !aligned(draft, 4)) || (draft_len && !aligned(draft_len, 4)) ||
+      (margin && !aligned(margin, 4)))
     return VQV_ERR_ALIGN;
   const size_t need = vqv_qgemm_verify_workspace_bytes(M, K, N, group, act_dtype);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return VQV_ERR_WORKSPACE;
-  const size_t dbytes = draft ? (size_t)B * (T - 1) * 4 : 0;
-  const void* ins[4] = {x, wq, scales, biases};
-  const size_t insz[4] = {xbytes, wbytes, sbytes, sbytes};
-  void* outs[4] = {y, argmax, accept_len, workspace};
-  const size_t outsz[4] = {y ? ybytes : 0, (size_t)M * 4, (size_t)B * 4, need};
-  for (int o = 0; o < 4; ++o) {
-    for (int i = 0; i < 4; ++i)
+  const void* ins[6] = {x, wq, scales, biases, draft, draft_len};
+  const size_t insz[6] = {xbytes, wbytes, sbytes, sbytes, draft ? (size_t)B * (T - 1) * 4 : 0,
+                          draft_len ? (size_t)B * 4 : 0};
+  void* outs[5] = {y, argmax, accept_len, margin, workspace};
+  const size_t outsz[5] = {y ? ybytes : 0, (size_t)M * 4, (size_t)B * 4,
+                           margin ? (size_t)M * 4 : 0, need};
+  for (int o = 0; o < 5; ++o) {
+    for (int i = 0; i < 6; ++i)
       if (overlaps(outs[o], outsz[o], ins[i], insz[i])) return VQV_ERR_ARG;
-    if (overlaps(outs[o], outsz[o], draft, dbytes)) return VQV_ERR_ARG;
-    for (int o2 = o + 1; o2 < 4; ++o2)
+    for (int o2 = o + 1; o2 < 5; ++o2)
       if (overlaps(outs[o], outsz[o], outs[o2], outsz[o2])) return VQV_ERR_ARG;
   }
   (void)hipGetLastError();
   const hipStream_t st = static_cast<hipStream_t>(hip_stream);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
+  vqv::VerifyArgs va{draft, draft_len, B, T, argmax, accept_len, margin,
+                     reinterpret_cast<uint4*>(ws + kHead)};
   hipError_t e;
   if (vqv::qgemm_verify_groups(M, K, N, (int)act_dtype) > 0) {
-    vqv::VerifyArgs va{draft, B, T, argmax, accept_len, reinterpret_cast<uint2*>(ws + kHead)};
     e = vqv::launch_qgemm_verify(x, wq, scales, biases, y, M, K, N, (int)act_dtype, va, st);
   } else {
     float* logits = y ? y : reinterpret_cast<float*>(ws + kHead);
-    void* part = ws + kHead + align256(ybytes);
+    va.partials = reinterpret_cast<uint4*>(ws + kHead + align256(ybytes));
     e = vqv::launch_qgemm(x, wq, scales, biases, logits, M, K, N, (int)act_dtype, st);
-    if (e == hipSuccess)
-      e = vqv::launch_verify(logits, draft, B, T, N, argmax, accept_len, part, st);
+    if (e == hipSuccess) e = vqv::launch_verify(logits, N, va, st);
   }
   return e == hipSuccess ? VQV_OK : VQV_ERR_HIP;
 }
 
 size_t vqv_verify_workspace_bytes(int B, int T, int N) {
   if (B < 1 || T < 1 || N < 1) return 0;
-  return (size_t)B * T * vqv::verify_chunks(N) * 8;
+  return (size_t)B * T * vqv::verify_chunks(N) * 16;
 }
 
 vqv_status vqv_verify(const float* logits, const int32_t* draft, int B, int T, int N,
                       int32_t* argmax, int32_t* accept_len, void* workspace,
                       size_t workspace_bytes, void* hip_stream) {
+  return vqv_verify_ex(logits, draft, nullptr, B, T, N, argmax, accept_len, nullptr, workspace,
+                       workspace_bytes, hip_stream);
+}
+
+vqv_status vqv_verify_ex(const float* logits, const int32_t* draft, const int32_t* draft_len,
+                         int B, int T, int N, int32_t* argmax, int32_t* accept_len,
+                         float* margin, void* workspace, size_t workspace_bytes,
+                         void* hip_stream) {
   if (!logits || !argmax || !accept_len) return VQV_ERR_ARG;
   if (B < 1 || T < 1 || T > kMaxBlock || N < 1) return VQV_ERR_ARG;
   if (T > 1 && !draft) return VQV_ERR_ARG;
   const size_t rows = (size_t)B * T;
   if (rows * (size_t)N >= (1ull << 31)) return VQV_ERR_ARG;
   if (!aligned(logits, 16) || !aligned(argmax, 4) || !aligned(accept_len, 4) ||
-      (draft && !aligned(draft, 4)))
+      (draft && !aligned(draft, 4)) || (draft_len && !aligned(draft_len, 4)) ||
+      (margin && !aligned(margin, 4)))
     return VQV_ERR_ALIGN;
-  const size_t lbytes = rows * N * 4;
-  if (overlaps(argmax, rows * 4, logits, lbytes) || overlaps(accept_len, (size_t)B * 4, logits, lbytes) ||
-      overlaps(argmax, rows * 4, accept_len, (size_t)B * 4) ||
-      (draft && (overlaps(argmax, rows * 4, draft, (size_t)B * (T - 1) * 4) ||
-                 overlaps(accept_len, (size_t)B * 4, draft, (size_t)B * (T - 1) * 4))))
-    return VQV_ERR_ARG;
   const size_t need = vqv_verify_workspace_bytes(B, T, N);
-  if (!workspace || workspace_bytes < need || !aligned(workspace, 8)) return VQV_ERR_WORKSPACE;
-  if (overlaps(workspace, need, logits, lbytes) || overlaps(workspace, need, argmax, rows * 4) ||
-      overlaps(workspace, need, accept_len, (size_t)B * 4))
-    return VQV_ERR_ARG;
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return VQV_ERR_WORKSPACE;
+  const void* ins[3] = {logits, draft, draft_len};
+  const size_t insz[3] = {rows * N * 4, draft ? (size_t)B * (T - 1) * 4 : 0,
+                          draft_len ? (size_t)B * 4 : 0};
+  void* outs[4] = {argmax, accept_len, margin, workspace};
+  const size_t outsz[4] = {rows * 4, (size_t)B * 4, margin ? rows * 4 : 0, need};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 3; ++i)
+      if (overlaps(outs[o], outsz[o], ins[i], insz[i])) return VQV_ERR_ARG;
+    for (int o2 = o + 1; o2 < 4; ++o2)
+      if (overlaps(outs[o], outsz[o], outs[o2], outsz[o2])) return VQV_ERR_ARG;
+  }
   (void)hipGetLastError();
-  const hipError_t e = vqv::launch_verify(logits, draft, B, T, N, argmax, accept_len, workspace,
-                                          static_cast<hipStream_t>(hip_stream));
+  const vqv::VerifyArgs va{draft, draft_len, B, T, argmax, accept_len, margin,
+                           static_cast<uint4*>(workspace)};
+  const hipError_t e = vqv::launch_verify(logits, N, va, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? VQV_OK : VQV_ERR_HIP;
 }
 

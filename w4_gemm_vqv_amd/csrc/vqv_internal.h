@@ -20,21 +20,23 @@ hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales
 
 // Greedy verify fused into the projection's epilogue (M = B*T <= 8, 16-bit
 // activations, K within the single-row-set kernel's LDS budget): each
-// work-group reduces its columns to one (key, index) partial per row, and a
-// one-work-group kernel then reduces the partials, writes argmax and the
-// accept lengths.
+// work-group reduces its columns to one top-two partial per row, and a
+// one-work-group kernel then reduces the partials, writes argmax, the margins
+// (when asked) and the accept lengths.
 struct VerifyArgs {
-  const int32_t* draft;   // [B, T-1]
+  const int32_t* draft;      // [B, T-1]
+  const int32_t* draft_len;  // [B] valid drafts per sequence, or NULL for T-1
   int B, T;
-  int32_t* argmax;        // [B*T]
-  int32_t* accept_len;    // [B]
-  uint2* partials;        // [work-groups][8]: (key, index)
+  int32_t* argmax;           // [B*T]
+  int32_t* accept_len;       // [B]
+  float* margin;             // [B*T] or NULL
+  uint4* partials;           // [work-groups][8]: (k1, i1, k2, -)
 };
 
 // Reduces `groups` partials per row ([groups][8], rows 0..B*T-1 <= 8) to the
-// argmax of each row, then the accept walk of each sequence.
-hipError_t launch_verify_finish(const uint2* partials, int groups, const int32_t* draft, int B,
-                                int T, int32_t* argmax, int32_t* accept_len, hipStream_t stream);
+// argmax (and margin) of each row, then the accept walk of each sequence.
+hipError_t launch_verify_finish(const uint4* partials, int groups, const VerifyArgs& va,
+                                hipStream_t stream);
 
 // The number of work-groups the fused projection launches, or 0 when the
 // fused path does not take this problem.
@@ -49,9 +51,8 @@ constexpr int kVerifyChunk = 4096;
 
 inline int verify_chunks(int N) { return (N + kVerifyChunk - 1) / kVerifyChunk; }
 
-// Two-stage greedy verify; `partials` holds B*T*verify_chunks(N) 8-byte slots.
-hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int T, int N,
-                         int32_t* argmax, int32_t* accept_len, void* partials,
-                         hipStream_t stream);
+// Two-stage greedy verify over fp32 logits [B*T, N]; `va.partials` holds
+// B*T*verify_chunks(N) 16-byte slots.
+hipError_t launch_verify(const float* logits, int N, const VerifyArgs& va, hipStream_t stream);
 
 }  // namespace vqv

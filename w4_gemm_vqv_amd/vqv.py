@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libvqv.so")
 VQV_BF16, VQV_FP16, VQV_FP32 = 0, 1, 2
 VQV_OK, VQV_ERR_ARG, VQV_ERR_UNSUPPORTED, VQV_ERR_ALIGN, VQV_ERR_WORKSPACE, VQV_ERR_HIP = range(6)
 EXPORTS = ("vqv_abi_version", "vqv_status_string", "vqv_qgemm_workspace_bytes", "vqv_qgemm",
-           "vqv_verify_workspace_bytes", "vqv_verify", "vqv_qgemm_verify_workspace_bytes",
-           "vqv_qgemm_verify")
+           "vqv_verify_workspace_bytes", "vqv_verify", "vqv_verify_ex",
+           "vqv_qgemm_verify_workspace_bytes", "vqv_qgemm_verify", "vqv_qgemm_verify_ex")
 
 _DTYPES = {torch.bfloat16: VQV_BF16, torch.float16: VQV_FP16, torch.float32: VQV_FP32}
 _lib = None
@@ -58,6 +58,11 @@ def lib() -> ctypes.CDLL:
         L.vqv_qgemm_verify.restype = i
         L.vqv_qgemm_verify.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, i, i, vp, vp, vp, sz,
                                        vp]
+        L.vqv_verify_ex.restype = i
+        L.vqv_verify_ex.argtypes = [vp, vp, vp, i, i, i, vp, vp, vp, vp, sz, vp]
+        L.vqv_qgemm_verify_ex.restype = i
+        L.vqv_qgemm_verify_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, i, i, vp, vp,
+                                          vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -133,7 +138,7 @@ def vqv_verify(logits: torch.Tensor, draft: torch.Tensor | None, B: int, T: int,
     if accept_len is None:
         accept_len = torch.empty(B, dtype=torch.int32, device=dev)
     if workspace is None:
-        workspace = torch.empty(max(vqv_verify_workspace_bytes(B, T, N), 8), dtype=torch.uint8,
+        workspace = torch.empty(max(vqv_verify_workspace_bytes(B, T, N), 16), dtype=torch.uint8,
                                 device=dev)
     dptr = _dev(draft, "draft") if (draft is not None and draft.numel()) else None
     _check(lib().vqv_verify(_dev(logits, "logits"), dptr, B, T, N, _dev(argmax, "argmax"),
@@ -141,6 +146,36 @@ def vqv_verify(logits: torch.Tensor, draft: torch.Tensor | None, B: int, T: int,
                             workspace.numel() * workspace.element_size(),
                             _stream_handle(stream)))
     return argmax, accept_len
+
+
+def vqv_verify_ex(logits: torch.Tensor, draft: torch.Tensor | None, B: int, T: int,
+                  draft_len: torch.Tensor | None = None, want_margin: bool = True,
+                  argmax: torch.Tensor | None = None, accept_len: torch.Tensor | None = None,
+                  margin: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  stream=None):
+    """(argmax [B*T] int32, accept_len [B] int32, margin [B*T] fp32 or None):
+    vqv_verify with per-sequence valid draft counts (int32 [B], or None) and
+    the top-1 minus top-2 margin of each row."""
+    N = logits.shape[-1]
+    dev = logits.device
+    if argmax is None:
+        argmax = torch.empty(B * T, dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if margin is None and want_margin:
+        margin = torch.empty(B * T, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(vqv_verify_workspace_bytes(B, T, N), 16), dtype=torch.uint8,
+                                device=dev)
+    dptr = _dev(draft, "draft") if (draft is not None and draft.numel()) else None
+    lptr = _dev(draft_len, "draft_len") if draft_len is not None else None
+    mptr = _dev(margin, "margin") if margin is not None else None
+    _check(lib().vqv_verify_ex(_dev(logits, "logits"), dptr, lptr, B, T, N,
+                               _dev(argmax, "argmax"), _dev(accept_len, "accept_len"), mptr,
+                               _dev(workspace, "workspace"),
+                               workspace.numel() * workspace.element_size(),
+                               _stream_handle(stream)))
+    return argmax, accept_len, margin
 
 
 def vqv_qgemm_verify_workspace_bytes(M: int, K: int, N: int, group: int = 64,
@@ -178,3 +213,42 @@ def vqv_qgemm_verify(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor,
                                   workspace.numel() * workspace.element_size(),
                                   _stream_handle(stream)))
     return y, argmax, accept_len
+
+
+def vqv_qgemm_verify_ex(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor,
+                        biases: torch.Tensor, draft: torch.Tensor | None, B: int, T: int,
+                        draft_len: torch.Tensor | None = None, want_margin: bool = True,
+                        y: torch.Tensor | None = None, want_y: bool = True,
+                        argmax: torch.Tensor | None = None,
+                        accept_len: torch.Tensor | None = None,
+                        margin: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, group: int = 64, stream=None):
+    """(y or None, argmax, accept_len, margin or None): vqv_qgemm_verify with
+    vqv_verify_ex's valid draft counts and margins."""
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported activation dtype {x.dtype}")
+    M, K = x.shape
+    N = wq.shape[0]
+    dev = x.device
+    act = _DTYPES[x.dtype]
+    if y is None and want_y:
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    if argmax is None:
+        argmax = torch.empty(B * T, dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if margin is None and want_margin:
+        margin = torch.empty(B * T, dtype=torch.float32, device=dev)
+    if workspace is None:
+        need = vqv_qgemm_verify_workspace_bytes(M, K, N, group, act)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    dptr = _dev(draft, "draft") if (draft is not None and draft.numel()) else None
+    lptr = _dev(draft_len, "draft_len") if draft_len is not None else None
+    mptr = _dev(margin, "margin") if margin is not None else None
+    _check(lib().vqv_qgemm_verify_ex(
+        _dev(x, "x"), _dev(wq, "wq"), _dev(scales, "scales"), _dev(biases, "biases"),
+        _dev(y, "y") if y is not None else None, M, K, N, group, act, dptr, lptr, B, T,
+        _dev(argmax, "argmax"), _dev(accept_len, "accept_len"), mptr,
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream)))
+    return y, argmax, accept_len, margin
