@@ -16,6 +16,8 @@ What it computes, step by step, is the plain definition of the operation:
    leading drafts equal to the target's argmax of the row before them,
    optionally capped by the sequence's count of valid drafts.
 6. ``margin_ref``: per row, top-1 minus top-2 in fp32.
+7. ``silu_ref``, ``swiglu_ref`` and ``qgemm_swiglu_ref``: the gated
+   activation over a gate/up projection, h = silu(gate) * up in float64.
 
 Sources on the pages:
 
@@ -180,3 +182,47 @@ def verify_ref(logits: np.ndarray, draft, B: int, T: int, draft_len=None, margin
         m = np.array([margin_ref(logits[r]) for r in range(B * T)], dtype=np.float32)
         return a, acc, m
     return a, acc
+
+
+def silu_ref(g):
+    """silu(g) = g * sigmoid(g) = g / (1 + exp(-g)), elementwise in float64.
+
+    For g below about -709 exp(-g) overflows to inf and the quotient is -0,
+    the float64 limit of the exact value.
+    """
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu_ref(y):
+    """Gated activation of a fused gate/up projection output.
+
+    ``y`` is [M, 2*Nh]: columns 0..Nh-1 are the gate, columns Nh..2*Nh-1 the
+    up projection, one matmul over the two weight blocks stacked along N (the
+    M=16 gate/up block of "perf: tune DFlash2 M=8 verification for M1 and
+    M2", Validation; the pages name no activation, and silu-gating is the
+    plainest reading for the Qwen 3.5 targets of "perf(speculative): commit
+    per-row accepts in batched DFlash"). Returns h [M, Nh] = silu(gate) * up
+    in float64.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    if y.shape[-1] % 2:
+        raise ValueError("a gate/up output has an even number of columns")
+    nh = y.shape[-1] // 2
+    return silu_ref(y[..., :nh]) * y[..., nh:]
+
+
+def qgemm_swiglu_ref(x: np.ndarray, act: str, wq: np.ndarray, scales: np.ndarray,
+                     biases: np.ndarray, group: int = GROUP, cols=None) -> np.ndarray:
+    """h = silu(x @ Wg.T) * (x @ Wu.T) in float64, with W = [Wg; Wu] stacked
+    along N (rows 0..Nh-1 gate, Nh..2*Nh-1 up). ``cols`` restricts h to the
+    given columns j, each computed from weight rows j and Nh + j."""
+    N = wq.shape[0]
+    if N % 2:
+        raise ValueError("a gate/up weight has an even number of rows")
+    nh = N // 2
+    idx = np.arange(nh) if cols is None else np.asarray(cols, dtype=np.int64)
+    gate = qgemm_ref(x, act, wq, scales, biases, group, cols=idx)
+    up = qgemm_ref(x, act, wq, scales, biases, group, cols=nh + idx)
+    return swiglu_ref(np.concatenate([gate, up], axis=1))

@@ -16,7 +16,7 @@ import pytest
 
 import gen
 from oracle import (margin_ref, accept_walk_ref, argmax_ref, decode_act, dequantize, qgemm_ref,
-                    unpack_codes, verify_ref)
+                    qgemm_swiglu_ref, silu_ref, swiglu_ref, unpack_codes, verify_ref)
 
 # ---------------------------------------------------------------- brute force
 
@@ -415,3 +415,77 @@ def test_verify_draft_len_per_sequence():
     assert acc.tolist() == [T - 1] * B
     _, acc = verify_ref(lg, draft, B, T, draft_len=np.array([0, 3, 5]))
     assert acc.tolist() == [0, 3, 5]
+
+
+# ---------------------------------------------------------------- gate/up SwiGLU
+
+
+def test_silu_closed_forms():
+    """sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4; silu(0) = 0;
+    silu(g) - silu(-g) = g; silu(g) -> g for large g."""
+    ln3 = np.log(3.0)
+    assert silu_ref(0.0) == 0.0
+    assert abs(silu_ref(ln3) - 0.75 * ln3) <= 1e-15
+    assert abs(silu_ref(-ln3) + 0.25 * ln3) <= 1e-15
+    assert abs(silu_ref(np.log(1.0 / 3.0)) + 0.25 * ln3) <= 1e-15
+    g = np.linspace(-30, 30, 601)
+    np.testing.assert_allclose(silu_ref(g) - silu_ref(-g), g, rtol=0, atol=1e-13)
+    assert silu_ref(60.0) == 60.0            # sigmoid(60) rounds to 1 in float64
+    assert -1e-20 < silu_ref(-60.0) < 0.0    # -60 * e^-60
+
+
+def test_silu_against_library_logistic():
+    """g * expit(g), scipy's logistic routine, on random and large values."""
+    from scipy.special import expit
+    rng = np.random.default_rng(5)
+    g = np.concatenate([rng.standard_normal(1000) * 4, [-700.0, -40.0, 40.0, 700.0]])
+    np.testing.assert_allclose(silu_ref(g), g * expit(g), rtol=1e-14, atol=1e-300)
+
+
+def test_swiglu_halves_are_gate_then_up():
+    """h = silu(gate) * up with the gate in the first half of the columns:
+    an asymmetric hand case that a swapped or interleaved split fails."""
+    y = np.array([[1.0, 2.0, -3.0, 5.0, 7.0, 0.5]])
+    s1, s2 = 1.0 / (1.0 + np.exp(-1.0)), 2.0 / (1.0 + np.exp(-2.0))
+    s3 = -3.0 / (1.0 + np.exp(3.0))
+    np.testing.assert_allclose(swiglu_ref(y), [[s1 * 5.0, s2 * 7.0, s3 * 0.5]], rtol=1e-15)
+    assert swiglu_ref(np.zeros((2, 4))).shape == (2, 2)
+    with pytest.raises(ValueError):
+        swiglu_ref(np.zeros((1, 3)))
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+def test_qgemm_swiglu_brute_force(act):
+    """Exact rational gate and up columns, then silu by math.exp."""
+    import math
+    M, K, NH = 2, 128, 3
+    rng = np.random.default_rng(12)
+    wq, s, b = gen.make_weights(rng, 2 * NH, K)
+    x = gen.make_x(rng, M, K, act)
+    y = _brute_qgemm(x, act, wq, s, b, M, K, 2 * NH)
+    h = qgemm_swiglu_ref(x, act, wq, s, b)
+    for m in range(M):
+        for j in range(NH):
+            g, u = float(y[m][j]), float(y[m][NH + j])
+            e = g / (1.0 + math.exp(-g)) * u
+            assert abs(h[m, j] - e) <= 1e-12 * (1.0 + abs(e)), (m, j, h[m, j], e)
+
+
+def test_qgemm_swiglu_column_subset():
+    x, wq, s, b = _rand(21, M=4, K=192, N=10)
+    full = qgemm_swiglu_ref(x, "bf16", wq, s, b)
+    cols = [4, 0, 3]
+    np.testing.assert_array_equal(qgemm_swiglu_ref(x, "bf16", wq, s, b, cols=cols),
+                                  full[:, cols])
+
+
+def test_qgemm_swiglu_zero_gate_and_zero_up():
+    """Zero codes and zero biases in the gate half give h = 0 whatever the up
+    half is; the same in the up half gives h = 0 too."""
+    x, wq, s, b = _rand(22, M=3, K=128, N=8)
+    for rows in (slice(0, 4), slice(4, 8)):
+        wq2, b2 = wq.copy(), b.copy()
+        wq2[rows] = 0
+        b2[rows] = 0
+        np.testing.assert_array_equal(qgemm_swiglu_ref(x, "bf16", wq2, s, b2),
+                                      np.zeros((3, 4)))

@@ -42,6 +42,14 @@ MUTANTS = {
                            "if False:\n        pass\n    v = np.where(np.isnan(v), -np.inf, v)"),
     "margin_sign": ("return np.float32(top) - np.float32(second)",
                     "return np.float32(second) - np.float32(top)"),
+    "silu_no_gate_factor": ("return g / (1.0 + np.exp(-g))", "return 1.0 / (1.0 + np.exp(-g))"),
+    "silu_exp_sign": ("return g / (1.0 + np.exp(-g))", "return g / (1.0 + np.exp(g))"),
+    "swiglu_halves_swapped": ("return silu_ref(y[..., :nh]) * y[..., nh:]",
+                              "return silu_ref(y[..., nh:]) * y[..., :nh]"),
+    "swiglu_interleaved": ("return silu_ref(y[..., :nh]) * y[..., nh:]",
+                           "return silu_ref(y[..., 0::2]) * y[..., 1::2]"),
+    "swiglu_up_offset": ("up = qgemm_ref(x, act, wq, scales, biases, group, cols=nh + idx)",
+                         "up = qgemm_ref(x, act, wq, scales, biases, group, cols=idx)"),
     "bf16_decode_shift": ("u = np.asarray(x, dtype=np.uint16).astype(np.uint32) << 16",
                           "u = np.asarray(x, dtype=np.uint16).astype(np.uint32) << 15"),
     "fp16_scale_as_bf16": (
