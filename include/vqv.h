@@ -2,7 +2,7 @@
  * vqv.h - C ABI of libvqv: the block-verification projection of DFlash-style
  * speculative decoding on AMD Instinct MI355X (gfx950).
  *
- * Two operations, each an asynchronous launch on the caller's HIP stream:
+ * Two core operations, each an asynchronous launch on the caller's HIP stream:
  *
  *   vqv_qgemm   y[M,N] = x[M,K] . W^T, W[N,K] 4-bit group-quantized (affine,
  *               group 64 along K), fp32 output. This is the quantized linear
@@ -17,6 +17,11 @@
  *               walk count; "dspark: fold first-token forward into verify +
  *               bit-exact M5 Metal decode wins", first commit: the committed
  *               token is verified as row 0 of the block).
+ *
+ * Around them: vqv_qgemm_verify fuses the two, vqv_verify_ex and
+ * vqv_qgemm_verify_ex add per-sequence draft lengths and top-1/top-2 margins,
+ * and vqv_qgemm_swiglu is the projection of a stacked gate/up weight with its
+ * silu-gated activation.
  *
  * Memory and ownership
  *   Every pointer is DEVICE memory owned by the caller; the library never
@@ -42,7 +47,7 @@
 extern "C" {
 #endif
 
-#define VQV_ABI_VERSION 2
+#define VQV_ABI_VERSION 3
 
 typedef enum {
   VQV_BF16 = 0, /* bfloat16 activations                                  */
@@ -204,6 +209,39 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
                                const int32_t* draft_len, int B, int T, int32_t* argmax,
                                int32_t* accept_len, float* margin, void* workspace,
                                size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Gate/up projection with its SwiGLU activation: y = x . W^T as vqv_qgemm over
+ * a stacked weight W [N, K] whose rows 0..N/2-1 are the gate projection and
+ * rows N/2..N-1 the up projection, then
+ *     h[m, j] = silu(y[m, j]) * y[m, N/2 + j],   silu(g) = g / (1 + exp(-g)),
+ * written as h [M, N/2] fp32; y itself is not written. This is the fused
+ * gate/up block of the M=16 verify pass ("perf: tune DFlash2 M=8 verification
+ * for M1 and M2", Validation: the M=16 gate/up block and its 1e-3 bound; the
+ * pages name no activation, and a silu-gated MLP is the reading taken for the
+ * Qwen 3.5 targets of "perf(speculative): commit per-row accepts in batched
+ * DFlash").
+ *
+ * Arguments
+ *   x, wq, scales, biases, M, K, group, act_dtype   as vqv_qgemm, with N the
+ *              row count of the stacked weight: N even, N >= 2.
+ *   h          [M, N/2] fp32, written. 4-byte aligned. Must not overlap an
+ *              input or the workspace.
+ *   workspace  at least vqv_qgemm_swiglu_workspace_bytes(...) bytes,
+ *              256-byte aligned; may be NULL when that is 0. It is 0 where
+ *              the activation is fused into the projection (M <= 16,
+ *              bf16/fp16, K <= 2560); elsewhere the projection's output goes
+ *              there first (M*N fp32).
+ *
+ * Numerics: the gate and up sums are those of vqv_qgemm (fp32); silu uses
+ * the fp32 exponential and an IEEE division.
+ */
+size_t vqv_qgemm_swiglu_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype);
+
+vqv_status vqv_qgemm_swiglu(const void* x, const uint8_t* wq, const uint16_t* scales,
+                            const uint16_t* biases, float* h, int M, int K, int N, int group,
+                            vqv_dtype act_dtype, void* workspace, size_t workspace_bytes,
+                            void* hip_stream);
 
 #ifdef __cplusplus
 }

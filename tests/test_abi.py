@@ -37,7 +37,8 @@ def test_header_declares_the_calls():
     assert declared_functions() == sorted(
         ["vqv_abi_version", "vqv_status_string", "vqv_qgemm_workspace_bytes", "vqv_qgemm",
          "vqv_verify_workspace_bytes", "vqv_verify", "vqv_verify_ex",
-         "vqv_qgemm_verify_workspace_bytes", "vqv_qgemm_verify", "vqv_qgemm_verify_ex"])
+         "vqv_qgemm_verify_workspace_bytes", "vqv_qgemm_verify", "vqv_qgemm_verify_ex",
+         "vqv_qgemm_swiglu_workspace_bytes", "vqv_qgemm_swiglu"])
 
 
 def test_exports_every_declared_symbol(L):
@@ -52,7 +53,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.vqv_abi_version() == 2
+    assert L.vqv_abi_version() == 3
     for s in range(6):
         assert L.vqv_status_string(s)
     assert L.vqv_status_string(99) == b"unknown status"
@@ -160,6 +161,36 @@ def test_fused_ex_rejects(L, kw, status):
     assert L.vqv_qgemm_verify_ex(a["x"], a["wq"], a["s"], a["b"], a["y"], a["M"], a["K"], a["N"],
                                  a["group"], a["act"], a["dr"], a["dl"], a["B"], a["T"], a["am"],
                                  a["ac"], a["mg"], a["ws"], a["wsb"], None) == status
+
+
+def test_swiglu_workspace_queries(L):
+    # fused into the 16-row kernel: no workspace
+    assert L.vqv_qgemm_swiglu_workspace_bytes(16, 2560, 18432, 64, BF16) == 0
+    assert L.vqv_qgemm_swiglu_workspace_bytes(4, 512, 1000, 64, FP16) == 0
+    # fallbacks hold the stacked output
+    assert L.vqv_qgemm_swiglu_workspace_bytes(32, 512, 1000, 64, BF16) >= 32 * 1000 * 4
+    assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1000, 64, FP32) >= 16 * 1000 * 4
+    assert L.vqv_qgemm_swiglu_workspace_bytes(16, 5120, 1000, 64, BF16) >= 16 * 1000 * 4
+    # invalid: odd N, group, M
+    assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1001, 64, BF16) == 0
+    assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1000, 32, BF16) == 0
+    assert L.vqv_qgemm_swiglu_workspace_bytes(0, 512, 1000, 64, BF16) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), ARG), (dict(h=None), ARG), (dict(N=1001), ARG), (dict(N=0), ARG),
+    (dict(M=65), ARG), (dict(K=100), ARG), (dict(group=32), UNSUP), (dict(act=3), ARG),
+    (dict(x=X + 8), ALIGN), (dict(h=Y + 2), ALIGN), (dict(h=X), ARG), (dict(h=W + 64), ARG),
+    (dict(h=S), ARG), (dict(K=16384 + 64), UNSUP),
+    (dict(M=32, ws=None), WS), (dict(M=32, wsb=64), WS), (dict(M=32, ws=WSP + 16), WS),
+    (dict(M=32, ws=X), ARG), (dict(M=32, h=WSP + 256), ARG),
+])
+def test_swiglu_rejects(L, kw, status):
+    a = dict(x=X, wq=W, s=S, b=B_, h=Y, M=16, K=512, N=1000, group=64, act=BF16, ws=WSP,
+             wsb=1 << 20)
+    a.update(kw)
+    assert L.vqv_qgemm_swiglu(a["x"], a["wq"], a["s"], a["b"], a["h"], a["M"], a["K"], a["N"],
+                              a["group"], a["act"], a["ws"], a["wsb"], None) == status
 
 
 def test_python_binding_raises_with_status(L):

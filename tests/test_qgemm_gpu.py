@@ -49,6 +49,10 @@ SHAPES = [
     # Work-groups of several column tiles (the column share of a CU spans
     # 2, 3 and 5 tiles, the last one partial): runs that cross a tile.
     (8, 512, 5000), (8, 1280, 12000), (5, 640, 17000), (8, 2560, 17408),
+    # One row set of 9..16 rows (the 16-row kernel for 16-bit activations):
+    # several tiles per work-group, ragged tails, G = 1 and odd G.
+    (16, 512, 5000), (12, 1280, 12000), (10, 192, 4001), (16, 64, 300), (13, 2560, 17408),
+    (16, 2560, 2000), (11, 448, 777),
 ]
 
 

@@ -1,0 +1,120 @@
+// Helpers shared by the projection kernels (qgemm.hip, qgemm_m16.hip): the
+// 16-bit MFMA wrapper, the exact code unpack and the activation permutation
+// that matches it, activation sums, and launch sizing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vqv_internal.h"
+
+namespace vqv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr unsigned kOutOfRange = 0x80000000u;   // buffer offset that reads as zero
+constexpr int kBufferFlags = 0x00020000;        // raw buffer, 32-bit data format
+
+template <int ACT> struct ActTraits;
+template <> struct ActTraits<ACT_BF16> {
+  static constexpr unsigned magic = 0x43004300u;  // bf16 pair (128, 128)
+  static constexpr float c0 = 128.0f;
+  static constexpr int esz = 2, parts = 1;
+  static constexpr bool f16 = false;
+};
+template <> struct ActTraits<ACT_FP16> {
+  static constexpr unsigned magic = 0x64006400u;  // fp16 pair (1024, 1024)
+  static constexpr float c0 = 1024.0f;
+  static constexpr int esz = 2, parts = 1;
+  static constexpr bool f16 = true;
+};
+template <> struct ActTraits<ACT_FP32> {           // three bf16 terms per value
+  static constexpr unsigned magic = 0x43004300u;
+  static constexpr float c0 = 128.0f;
+  static constexpr int esz = 4, parts = 3;
+  static constexpr bool f16 = false;
+};
+
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 8 codes of one dword -> four 16-bit float pairs (c0+q): (n0,n4) (n1,n5) (n2,n6) (n3,n7).
+__device__ __forceinline__ u32x4 unpack_codes(unsigned d, unsigned magic) {
+  u32x4 q;
+  q.x = (d & 0x000F000Fu) | magic;
+  q.y = ((d >> 4) & 0x000F000Fu) | magic;
+  q.z = ((d >> 8) & 0x000F000Fu) | magic;
+  q.w = ((d >> 12) & 0x000F000Fu) | magic;
+  return q;
+}
+
+// Natural-order 16-bit values (k0,k1)(k2,k3)(k4,k5)(k6,k7) -> unpack order.
+__device__ __forceinline__ u32x4 permute_pairs(u32x4 r) {
+  u32x4 a;
+  a.x = __builtin_amdgcn_perm(r.z, r.x, 0x05040100u);
+  a.y = __builtin_amdgcn_perm(r.z, r.x, 0x07060302u);
+  a.z = __builtin_amdgcn_perm(r.w, r.y, 0x05040100u);
+  a.w = __builtin_amdgcn_perm(r.w, r.y, 0x07060302u);
+  return a;
+}
+
+__device__ __forceinline__ float half_lo(unsigned v) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(unsigned v) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(v >> 16));
+}
+
+// Sum of the eight 16-bit activations held in one 16-byte block.
+template <int ACT>
+__device__ __forceinline__ float block_sum(const u32x4& v) {
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const unsigned w = v[e];  // a scalar copy: bit_cast must not see the vector element
+    if constexpr (ACT == ACT_FP16)
+      s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w),
+                                 __builtin_bit_cast(f16x2, 0x3C003C00u), s, false);
+    else
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                          __builtin_bit_cast(bf16x2, 0x3F803F80u), s, false);
+  }
+  return s;
+}
+
+// Sum over the eight lanes 8i..8i+7 (DPP: swap neighbours, swap pairs, then
+// mirror within the half row).
+__device__ __forceinline__ float sum8_lanes(float s) {
+  s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                     0, __builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
+  s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                     0, __builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, false));
+  s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                     0, __builtin_bit_cast(int, s), 0x141, 0xF, 0xF, false));
+  return s;
+}
+
+constexpr int kLdsLimit = 160 * 1024;
+
+inline int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  return cus;
+}
+
+}  // namespace vqv

@@ -160,6 +160,51 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
   return e == hipSuccess ? VQV_OK : VQV_ERR_HIP;
 }
 
+size_t vqv_qgemm_swiglu_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype) {
+  if (M < 1 || M > kMaxRows || N < 2 || (N & 1) || K < kGroup || group != kGroup) return 0;
+  if (vqv::qgemm_swiglu_fused(M, K, N, (int)act_dtype)) return 0;
+  return align256((size_t)M * N * 4);  // the stacked gate/up output
+}
+
+vqv_status vqv_qgemm_swiglu(const void* x, const uint8_t* wq, const uint16_t* scales,
+                            const uint16_t* biases, float* h, int M, int K, int N, int group,
+                            vqv_dtype act_dtype, void* workspace, size_t workspace_bytes,
+                            void* hip_stream) {
+  if (!x || !wq || !scales || !biases || !h) return VQV_ERR_ARG;
+  if (act_dtype != VQV_BF16 && act_dtype != VQV_FP16 && act_dtype != VQV_FP32)
+    return VQV_ERR_ARG;
+  if (M < 1 || M > kMaxRows || N < 2 || (N & 1) || K < kGroup) return VQV_ERR_ARG;
+  if (group != kGroup) return VQV_ERR_UNSUPPORTED;
+  if (K % kGroup) return VQV_ERR_ARG;
+  if (K > vqv::kMaxK) return VQV_ERR_UNSUPPORTED;
+  const size_t esz = (size_t)act_size(act_dtype);
+  const size_t xbytes = (size_t)M * K * esz;
+  const size_t wbytes = (size_t)N * (K / 2);
+  const size_t sbytes = (size_t)N * (K / kGroup) * 2;
+  const size_t hbytes = (size_t)M * (N / 2) * 4;
+  if (xbytes >= (1ull << 31) || wbytes >= (1ull << 32) || (size_t)N * (K / kGroup) >= (1ull << 31) ||
+      (size_t)M * N * 4 >= (1ull << 31))
+    return VQV_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(scales, 2) || !aligned(biases, 2) ||
+      !aligned(h, 4))
+    return VQV_ERR_ALIGN;
+  const size_t need = vqv_qgemm_swiglu_workspace_bytes(M, K, N, group, act_dtype);
+  if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return VQV_ERR_WORKSPACE;
+  const void* ins[4] = {x, wq, scales, biases};
+  const size_t insz[4] = {xbytes, wbytes, sbytes, sbytes};
+  for (int i = 0; i < 4; ++i) {
+    if (overlaps(h, hbytes, ins[i], insz[i])) return VQV_ERR_ARG;
+    if (need && overlaps(workspace, need, ins[i], insz[i])) return VQV_ERR_ARG;
+  }
+  if (need && overlaps(h, hbytes, workspace, need)) return VQV_ERR_ARG;
+  (void)hipGetLastError();
+  const hipError_t e = vqv::launch_qgemm_swiglu(x, wq, scales, biases, h, M, K, N,
+                                                (int)act_dtype, static_cast<float*>(workspace),
+                                                static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? VQV_OK : VQV_ERR_HIP;
+}
+
 size_t vqv_verify_workspace_bytes(int B, int T, int N) {
   if (B < 1 || T < 1 || N < 1) return 0;
   return (size_t)B * T * vqv::verify_chunks(N) * 16;

@@ -46,6 +46,22 @@ hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t*
                                const uint16_t* biases, float* y, int M, int K, int N, int act,
                                const VerifyArgs& va, hipStream_t stream);
 
+// One row set of 9..16 rows (bf16/fp16, K within the kernel's LDS budget):
+// qgemm_w4_m16 (qgemm_m16.hip). Whether it takes the problem, and the launch.
+bool qgemm_m16_fits(int M, int K, int act);
+hipError_t launch_qgemm_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
+                            const uint16_t* biases, float* y, int M, int K, int N, int act,
+                            hipStream_t stream);
+
+// h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:] of y = x . W^T, W the stacked
+// gate/up weight [N, K]. Fused into the 16-row kernel when
+// qgemm_swiglu_fused(); otherwise the projection writes `scratch_y` [M, N]
+// and an elementwise kernel forms h.
+bool qgemm_swiglu_fused(int M, int K, int N, int act);
+hipError_t launch_qgemm_swiglu(const void* x, const uint8_t* wq, const uint16_t* scales,
+                               const uint16_t* biases, float* h, int M, int K, int N, int act,
+                               float* scratch_y, hipStream_t stream);
+
 // Logits per verify work-group (one row, one chunk of columns).
 constexpr int kVerifyChunk = 4096;
 

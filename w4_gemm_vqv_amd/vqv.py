@@ -20,7 +20,8 @@ VQV_BF16, VQV_FP16, VQV_FP32 = 0, 1, 2
 VQV_OK, VQV_ERR_ARG, VQV_ERR_UNSUPPORTED, VQV_ERR_ALIGN, VQV_ERR_WORKSPACE, VQV_ERR_HIP = range(6)
 EXPORTS = ("vqv_abi_version", "vqv_status_string", "vqv_qgemm_workspace_bytes", "vqv_qgemm",
            "vqv_verify_workspace_bytes", "vqv_verify", "vqv_verify_ex",
-           "vqv_qgemm_verify_workspace_bytes", "vqv_qgemm_verify", "vqv_qgemm_verify_ex")
+           "vqv_qgemm_verify_workspace_bytes", "vqv_qgemm_verify", "vqv_qgemm_verify_ex",
+           "vqv_qgemm_swiglu_workspace_bytes", "vqv_qgemm_swiglu")
 
 _DTYPES = {torch.bfloat16: VQV_BF16, torch.float16: VQV_FP16, torch.float32: VQV_FP32}
 _lib = None
@@ -60,6 +61,10 @@ def lib() -> ctypes.CDLL:
                                        vp]
         L.vqv_verify_ex.restype = i
         L.vqv_verify_ex.argtypes = [vp, vp, vp, i, i, i, vp, vp, vp, vp, sz, vp]
+        L.vqv_qgemm_swiglu_workspace_bytes.restype = sz
+        L.vqv_qgemm_swiglu_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.vqv_qgemm_swiglu.restype = i
+        L.vqv_qgemm_swiglu.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, sz, vp]
         L.vqv_qgemm_verify_ex.restype = i
         L.vqv_qgemm_verify_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, i, i, vp, vp,
                                           vp, vp, sz, vp]
@@ -252,3 +257,31 @@ def vqv_qgemm_verify_ex(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor,
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream_handle(stream)))
     return y, argmax, accept_len, margin
+
+
+def vqv_qgemm_swiglu_workspace_bytes(M: int, K: int, N: int, group: int = 64,
+                                     act_dtype: int = VQV_BF16) -> int:
+    return lib().vqv_qgemm_swiglu_workspace_bytes(M, K, N, group, act_dtype)
+
+
+def vqv_qgemm_swiglu(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor,
+                     biases: torch.Tensor, h: torch.Tensor | None = None, group: int = 64,
+                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """h [M, N/2] fp32 = silu(x . Wg^T) * (x . Wu^T) for a stacked gate/up
+    weight ([N, K/2] codes, gate rows first)."""
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported activation dtype {x.dtype}")
+    M, K = x.shape
+    N = wq.shape[0]
+    act = _DTYPES[x.dtype]
+    if h is None:
+        h = torch.empty((M, N // 2), dtype=torch.float32, device=x.device)
+    need = vqv_qgemm_swiglu_workspace_bytes(M, K, N, group, act)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().vqv_qgemm_swiglu(_dev(x, "x"), _dev(wq, "wq"), _dev(scales, "scales"),
+                                  _dev(biases, "biases"), _dev(h, "h"), M, K, N, group, act,
+                                  ws_ptr, ws_bytes, _stream_handle(stream)))
+    return h
