@@ -5,7 +5,9 @@ One step is the whole hot path over one verify block: the W4 group-64 QMM
 y[M,N] = x[M,K] . W^T, then the per-row argmax and accept walk over y. By
 default a step is one vqv_qgemm_verify call (the argmax fused into the QMM
 epilogue, a one-work-group kernel finishing the rows and the walk); with
---path separate it is vqv_qgemm followed by vqv_verify. The default workload
+--path separate it is vqv_qgemm followed by vqv_verify; with --path swiglu
+(the gate/up workload) it is one vqv_qgemm_swiglu call, the projection of the
+stacked gate/up weight with its silu-gated epilogue. The default workload
 is the target projection M=8, K=5120, N=17408 with bf16 activations and a
 verify block of T=8. Inputs are seeded synthetic tensors of that shape,
 resident in HBM before timing. The weights rotate through enough copies that
@@ -56,6 +58,17 @@ def qgemm_bytes(M, K, N, esz):
     return K * N // 2 + 4 * N * (K // 64) + M * K * esz + 4 * M * N
 
 
+KERNEL_SOURCES = ("qgemm.hip", "qgemm_common.h", "qgemm_m16.hip")
+
+
+def kernel_sha():
+    """sha256 over the projection kernels' sources, in a fixed order."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "w4_gemm_vqv_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_record(workload, M):
     """Measured HBM bytes per launch from committed rocprofv3 counter runs,
     valid only while the kernel source is unchanged."""
@@ -63,9 +76,8 @@ def traffic_record(workload, M):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "w4_gemm_vqv_amd", "csrc", "qgemm.hip"), "rb").read()
     entry = rec.get("workloads", {}).get(f"{workload}:M={M}")
-    if not entry or rec.get("qgemm_hip_sha256") != hashlib.sha256(src).hexdigest():
+    if not entry or rec.get("kernel_sources_sha256") != kernel_sha():
         return None
     return entry["fetch_bytes"] + entry["write_bytes"]
 
@@ -155,10 +167,9 @@ def write_traffic(fetch_dir, write_dir, workload, M):
         out[f"{key}_dispatches"] = len(q) - half
     path = os.path.join(ROOT, "profiles", "qgemm_traffic.json")
     rec = json.load(open(path)) if os.path.exists(path) else {}
-    src = open(os.path.join(ROOT, "w4_gemm_vqv_amd", "csrc", "qgemm.hip"), "rb").read()
-    sha = hashlib.sha256(src).hexdigest()
-    if rec.get("qgemm_hip_sha256") != sha:
-        rec = {"qgemm_hip_sha256": sha, "workloads": {}}
+    sha = kernel_sha()
+    if rec.get("kernel_sources_sha256") != sha:
+        rec = {"kernel_sources_sha256": sha, "workloads": {}}
     key = f"{workload}:M={M}"
     rec["workloads"][key] = out
     json.dump(rec, open(path, "w"), indent=1, sort_keys=True)
@@ -177,9 +188,10 @@ def main():
     ap.add_argument("--rotate", type=int, default=None, help="weight copies cycled per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=["fused", "separate"], default="fused",
+    ap.add_argument("--path", choices=["fused", "separate", "swiglu"], default="fused",
                     help="one step: the projection with the verify fused into its epilogue, "
-                         "or the two calls back to back")
+                         "the two calls back to back, or (gate/up) the projection with its "
+                         "SwiGLU epilogue")
     ap.add_argument("--counter-pass", action="store_true",
                     help="eager QMM launches + a copy kernel, for one rocprofv3 --pmc pass")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -248,6 +260,13 @@ def main():
         fws = torch.zeros(vqv.vqv_qgemm_verify_workspace_bytes(M, K, N, 64, vqv_act),
                           dtype=torch.uint8, device=dev)
     use_fused = fused_ok and args.path == "fused"
+    use_swiglu = args.path == "swiglu"
+    if use_swiglu:
+        if T or N % 2:
+            raise SystemExit("--path swiglu takes a gate/up workload (even N, no verify)")
+        hbuf = torch.empty((M, N // 2), dtype=torch.float32, device=dev)
+        sws_n = vqv.vqv_qgemm_swiglu_workspace_bytes(M, K, N, 64, vqv_act)
+        sws = torch.empty(sws_n, dtype=torch.uint8, device=dev) if sws_n else None
 
     def qmm(i, st):
         xc, wc, sc, bc = copies[i % R]
@@ -262,9 +281,16 @@ def main():
         vqv.vqv_qgemm_verify(xc, wc, sc, bc, draft if T > 1 else None, B, T, y=y, argmax=am,
                              accept_len=al, workspace=fws, stream=st)
 
+    def swiglu(i, st):
+        xc, wc, sc, bc = copies[i % R]
+        vqv.vqv_qgemm_swiglu(xc, wc, sc, bc, h=hbuf, workspace=sws, stream=st)
+
     def step(i, st):
         if use_fused:
             fused(i, st)
+            return
+        if use_swiglu:
+            swiglu(i, st)
             return
         qmm(i, st)
         if T:
@@ -339,6 +365,11 @@ def main():
         g_v = graph_of(lambda i, st: ver(st), QMM_LAUNCHES)
         g_v.replay()
         v_runs = [timed(g_v) * 1e3 / QMM_LAUNCHES for _ in range(5)]
+    s_runs = None
+    if use_swiglu:
+        g_s = graph_of(swiglu, nq)
+        g_s.replay()
+        s_runs = [timed(g_s) * 1e3 / nq for _ in range(5)]
     f_runs = None
     if use_fused:
         g_f = graph_of(fused, nq)
@@ -351,8 +382,22 @@ def main():
     # epilogue, 8 bytes per row and work-group, and is timed with the finish
     # kernel in fused_us_mean).
     k_us = q_mean
+    if act == "fp32":
+        kname = "qgemm_w4"
+    elif M <= 8:
+        kname = "qgemm_w4_m8"
+    elif M <= 16 and K <= 2560:
+        kname = "qgemm_w4_m16"
+    else:
+        kname = "qgemm_w4"
+    if use_swiglu:
+        # The step's kernel is the projection with the SwiGLU epilogue: it
+        # writes h [M, N/2] instead of y [M, N].
+        qb = qb - 4 * M * N + 4 * M * (N // 2)
+        k_us = statistics.fmean(s_runs)
+        if kname == "qgemm_w4_m16":
+            kname = "qgemm_w4_m16 (SwiGLU)"
     achieved = qb / (k_us * 1e-6) / 1e9
-    kname = "qgemm_w4_m8" if M <= 8 and act != "fp32" else "qgemm_w4"
     out = {
         "metric": METRIC,
         "value": M / (ms_step * 1e-3),
@@ -368,7 +413,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: W4 group-64 QMM M={M} K={K} N={N} {act} "
                                + (f"+ greedy verify B={B} T={T}" if T else "(no verify)")
-                               + (" (verify fused into the QMM epilogue)" if use_fused else ""),
+                               + (" (verify fused into the QMM epilogue)" if use_fused else "")
+                               + (" with the SwiGLU epilogue, h[M, N/2]" if use_swiglu else ""),
                    "M": M, "K": K, "N": N, "group": 64, "act": act, "verify_B": B,
                    "verify_T": T, "weight_copies": R},
         "eager_ms_per_step": ms_eager,
@@ -376,10 +422,12 @@ def main():
         "qgemm_us_runs": q_runs,
         "verify_us_mean": statistics.fmean(v_runs),
         "fused_us_mean": statistics.fmean(f_runs) if f_runs else None,
-        "step_path": "fused" if use_fused else "separate",
-        "step_hbm_gbs": (qb + (4 * M * N if T else 0)) / (ms_step * 1e-3) / 1e9,
+        "swiglu_us_mean": statistics.fmean(s_runs) if s_runs else None,
+        "step_path": "fused" if use_fused else ("swiglu" if use_swiglu else "separate"),
+        "step_hbm_gbs": (qb + (4 * M * N if T and not use_fused else 0)) / (ms_step * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_record(args.workload, M),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None if use_swiglu else traffic_record(args.workload, M),
                      "kernel": kname, "bytes_per_launch": qb, "us_per_launch": k_us},
         "cpu_baseline": None,
     }
