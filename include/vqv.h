@@ -229,9 +229,9 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
  *              input or the workspace.
  *   workspace  at least vqv_qgemm_swiglu_workspace_bytes(...) bytes,
  *              256-byte aligned; may be NULL when that is 0. It is 0 where
- *              the activation is fused into the projection (M <= 16,
- *              bf16/fp16, K <= 2560); elsewhere the projection's output goes
- *              there first (M*N fp32).
+ *              the activation is fused into the projection (bf16/fp16
+ *              activations, K <= 2560); elsewhere the projection's output
+ *              goes there first (M*N fp32).
  *
  * Numerics: the gate and up sums are those of vqv_qgemm (fp32); silu uses
  * the fp32 exponential and an IEEE division.

@@ -164,11 +164,12 @@ def test_fused_ex_rejects(L, kw, status):
 
 
 def test_swiglu_workspace_queries(L):
-    # fused into the 16-row kernel: no workspace
+    # fused into the 16-row kernel (row sets of 16): no workspace
     assert L.vqv_qgemm_swiglu_workspace_bytes(16, 2560, 18432, 64, BF16) == 0
     assert L.vqv_qgemm_swiglu_workspace_bytes(4, 512, 1000, 64, FP16) == 0
+    assert L.vqv_qgemm_swiglu_workspace_bytes(64, 512, 1000, 64, BF16) == 0
     # fallbacks hold the stacked output
-    assert L.vqv_qgemm_swiglu_workspace_bytes(32, 512, 1000, 64, BF16) >= 32 * 1000 * 4
+    assert L.vqv_qgemm_swiglu_workspace_bytes(32, 512, 1000, 64, FP32) >= 32 * 1000 * 4
     assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1000, 64, FP32) >= 16 * 1000 * 4
     assert L.vqv_qgemm_swiglu_workspace_bytes(16, 5120, 1000, 64, BF16) >= 16 * 1000 * 4
     # invalid: odd N, group, M
@@ -182,8 +183,9 @@ def test_swiglu_workspace_queries(L):
     (dict(M=65), ARG), (dict(K=100), ARG), (dict(group=32), UNSUP), (dict(act=3), ARG),
     (dict(x=X + 8), ALIGN), (dict(h=Y + 2), ALIGN), (dict(h=X), ARG), (dict(h=W + 64), ARG),
     (dict(h=S), ARG), (dict(K=16384 + 64), UNSUP),
-    (dict(M=32, ws=None), WS), (dict(M=32, wsb=64), WS), (dict(M=32, ws=WSP + 16), WS),
-    (dict(M=32, ws=X), ARG), (dict(M=32, h=WSP + 256), ARG),
+    (dict(act=FP32, ws=None), WS), (dict(act=FP32, wsb=64), WS),
+    (dict(act=FP32, ws=WSP + 16), WS), (dict(act=FP32, ws=X), ARG),
+    (dict(act=FP32, h=WSP + 256), ARG),
 ])
 def test_swiglu_rejects(L, kw, status):
     a = dict(x=X, wq=W, s=S, b=B_, h=Y, M=16, K=512, N=1000, group=64, act=BF16, ws=WSP,

@@ -53,6 +53,9 @@ SHAPES = [
     # several tiles per work-group, ragged tails, G = 1 and odd G.
     (16, 512, 5000), (12, 1280, 12000), (10, 192, 4001), (16, 64, 300), (13, 2560, 17408),
     (16, 2560, 2000), (11, 448, 777),
+    # Row sets of 16 (17..64 rows): several column groups per XCD, ragged
+    # last row set, a padded grid.
+    (64, 2560, 5000), (48, 1280, 3001), (20, 512, 12000), (64, 64, 99), (40, 2560, 17408),
 ]
 
 

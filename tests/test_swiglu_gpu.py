@@ -8,8 +8,8 @@ h = silu(g)*u (|silu'| <= 1.1), plus the fp32 evaluation of the epilogue:
     |dh| <= tau*(1.1*|u|*(1+|g|) + |silu(g)|*(1+|u|) + 1.1*tau*(1+|g|)*(1+|u|))
             + 2^-20*|h|,
 with g, u, h the oracle's float64 values. Shapes cover the fused kernel
-(M <= 16, 16-bit activations, K <= 2560: several tiles, ragged tails, odd
-group counts, M below 8) and the two-step fallback (M > 16, fp32
+(16-bit activations, K <= 2560, row sets of 16: several tiles, ragged tails,
+odd group counts, M below 8 and up to 64) and the two-step fallback (fp32
 activations, larger K).
 """
 
@@ -73,8 +73,10 @@ def run(vqv, c, M=None):
 FUSED = [(16, 512, 2 * 1000, "bf16"), (16, 2560, 2 * 3000, "bf16"), (12, 640, 2 * 777, "fp16"),
          (9, 64, 2 * 5, "bf16"), (1, 512, 2 * 300, "bf16"), (8, 192, 2 * 1234, "fp16"),
          (16, 1280, 2 * 6000, "fp16"), (5, 448, 2 * 41, "bf16"), (16, 128, 2, "bf16")]
-FALLBACK = [(32, 512, 2 * 500, "bf16"), (16, 512, 2 * 300, "fp32"), (16, 5120, 2 * 200, "bf16"),
-            (64, 256, 2 * 130, "fp16"), (3, 4096, 2 * 77, "fp32")]
+FUSED += [(32, 512, 2 * 500, "bf16"), (64, 256, 2 * 130, "fp16"), (48, 2560, 2 * 2100, "bf16"),
+          (17, 640, 2 * 999, "fp16")]
+FALLBACK = [(16, 512, 2 * 300, "fp32"), (16, 5120, 2 * 200, "bf16"), (3, 4096, 2 * 77, "fp32"),
+            (40, 3072, 2 * 150, "fp16")]
 
 
 @pytest.mark.parametrize("M,K,N,act", FUSED + FALLBACK)
@@ -89,7 +91,8 @@ def test_swiglu_parity(vqv, M, K, N, act):
 
 def test_fused_workspace_is_zero(vqv):
     assert vqv.vqv_qgemm_swiglu_workspace_bytes(16, 2560, 18432, 64, vqv.VQV_BF16) == 0
-    assert vqv.vqv_qgemm_swiglu_workspace_bytes(32, 2560, 18432, 64, vqv.VQV_BF16) > 0
+    assert vqv.vqv_qgemm_swiglu_workspace_bytes(64, 2560, 18432, 64, vqv.VQV_BF16) == 0
+    assert vqv.vqv_qgemm_swiglu_workspace_bytes(16, 2560, 18432, 64, vqv.VQV_FP32) > 0
 
 
 def test_matches_plain_projection(vqv):

@@ -1,5 +1,6 @@
-// W4 group-64 dequant GEMM for 9..16 activation rows on gfx950, and the same
-// kernel with a SwiGLU epilogue over a stacked gate/up weight.
+// W4 group-64 dequant GEMM for 9..64 activation rows on gfx950 (row sets of
+// 16), and the same kernel with a SwiGLU epilogue over a stacked gate/up
+// weight.
 //
 // y[m,n] = sum_k x[m,k] * (s[n,k/64]*q[n,k] + b[n,k/64]), as the projection of
 // qgemm.hip, for one row set of up to 16 rows: the verify block of 16 and the
@@ -17,6 +18,15 @@
 //     y += s*acc' + (b - c0*s)*xs,  acc' = sum x*(c0+q),  xs = sum x.
 // The per-step work, the exact unpack and the weight ring follow
 // qgemm_w4_m8; the activation image holds 16 rows per group pair.
+//
+// Persistent work-groups. One work-group per CU stages its row set's
+// activations once and then takes column groups in turn (worker w: groups w,
+// w + workers, ...), with the table, the weight ring and the reduction per
+// group. With more than 16 rows, row set r (rows 16r .. 16r+15) has workers
+// of its own, and the grid is laid out so that the row sets of one worker are
+// consecutive on one XCD (work-groups are dealt to the 8 XCDs in turn): they
+// walk the same column groups together, so the XCD reads those weights from
+// HBM once and serves the other row sets from its L2.
 //
 // SwiGLU columns. The work-group's logical columns interleave the two halves:
 // logical column 2u reads gate row u and 2u+1 reads up row Nh+u, so the
@@ -67,7 +77,7 @@ template <int ACT, int NW, int TW, int DB, int RB, int D0, int XB, bool SWIGLU>
 __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
-    float* __restrict__ y, int M, int K, int N, int cols) {
+    float* __restrict__ y, int M, int K, int N, int cols, int rsets, int workers) {
   using TR = ActTraits<ACT>;
   static_assert(TR::parts == 1, "16-bit activations only");
   static_assert(TW <= NW, "a run must span at most two tiles");
@@ -78,6 +88,20 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
   constexpr int WGC = 16 * TW;
   constexpr int SBU = 2;
   constexpr unsigned kSkip = 0x7FF00000u;             // scalar offset that reads as zero
+
+  // Work-group -> (row set, worker). Worker w takes the column groups w,
+  // w + workers, ...; the row sets of one worker are consecutive on one XCD.
+  const int ngroups = (N + cols - 1) / cols;
+  int wk = blockIdx.x, rs = 0;
+  if (rsets > 1) {
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    rs = local % rsets;
+    wk = (local / rsets) * 8 + xcd;
+  }
+  if (wk >= workers || wk >= ngroups) return;        // the whole group leaves
+  x = static_cast<const uint16_t*>(x) + (size_t)rs * 16 * K;
+  y += (size_t)rs * 16 * (SWIGLU ? N / 2 : N);
+  M = min(16, M - 16 * rs);
 
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
@@ -98,38 +122,13 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
   float* red = reinterpret_cast<float*>(lds + L.red);
   int* run_tiles = reinterpret_cast<int*>(lds + L.runs);
 
-  const int wg0 = blockIdx.x * cols;                  // first logical column
-  const int wgcols = min(cols, N - wg0);
-  const int tiles = (wgcols + 15) >> 4;
-  const int nblk = tiles * bpt;
-  const int b0 = (wave * nblk) / NW;
-  const int nb = ((wave + 1) * nblk) / NW - b0;
-  const int tfirst = b0 / bpt;
-
-  // Weight row of logical column c of this work-group, relative to `row0`.
-  const int row0 = SWIGLU ? (wg0 >> 1) : wg0;
-  auto rel_row = [&](int c) { return SWIGLU ? (c & 1) * Nh + (c >> 1) : c; };
-  const int nrows = SWIGLU ? N - row0 : wgcols;       // rows the buffers may touch
-
   unsigned magic;
   asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(TR::magic));
-
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(wq) + (size_t)row0 * rowbytes, (short)0, nrows * rowbytes,
-      kBufferFlags);
-  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(scales) + (size_t)row0 * G, (short)0, nrows * G * 2, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(biases) + (size_t)row0 * G, (short)0, nrows * G * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(x), (short)0, M * K * 2, kBufferFlags);
 
-  // Lane j of tile t reads logical column 16t + j: weight row rel_row(j) plus
-  // the tile's rows (16 per tile, or 8 gate and 8 up rows with SWIGLU).
-  const unsigned woff = (unsigned)rel_row(j) * rowbytes + 8u * h;
-  constexpr unsigned kTileRows = SWIGLU ? 8u : 16u;
-
-  // ---- activation staging: lane (e8, mm) moves x[mm + 8r, 64g + 8e8 ..+8].
+  // ---- activation staging, once per work-group: lane (e8, mm) moves
+  // x[mm + 8r, 64g + 8e8 .. +8].
   const int ngrp = 2 * GP;
   const int rounds = (ngrp + NW - 1) / NW;
   const int e8 = lane & 7;
@@ -161,101 +160,27 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
       xsl[g * 16 + mm + 8 * r] = s8;
     }
   };
-  auto x_store = [&](int bb) {
-#pragma unroll
-    for (int i = 0; i < XB; ++i) x_store_round(bb, i);
-  };
-
-  // ---- scale/bias table: row n of the table is logical column n.
   const bool sb_vec = (G % 8) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
                                         reinterpret_cast<uintptr_t>(biases)) & 15) == 0;
-  const int sb_units = sb_vec ? wgcols * G / 8 : wgcols * G;
-  u32x4 sbs[SBU], sbb[SBU];
   const unsigned g_recip = 0xFFFFFFFFu / (unsigned)G + 1u;
   auto div_g = [&](unsigned e) { return G == 1 ? e : __umulhi(e, g_recip); };
-  auto sb_load = [&](int round) {
-#pragma unroll
-    for (int u = 0; u < SBU; ++u) {
-      const int i = (round * SBU + u) * NT + tid;
-      if (sb_vec) {
-        const unsigned e0 = 8u * (unsigned)i;
-        const unsigned n = div_g(e0), g = e0 - n * (unsigned)G;
-        const unsigned off =
-            i < sb_units ? 2u * ((unsigned)rel_row((int)n) * (unsigned)G + g) : kOutOfRange;
-        sbs[u] = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
-        sbb[u] = __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0);
-      } else {
-        const unsigned n = div_g((unsigned)i), g = (unsigned)i - n * (unsigned)G;
-        const unsigned off =
-            i < sb_units ? 2u * ((unsigned)rel_row((int)n) * (unsigned)G + g) : kOutOfRange;
-        sbs[u].x = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
-        sbb[u].x = __builtin_amdgcn_raw_buffer_load_b16(br, off, 0, 0);
-      }
-    }
-  };
-  auto sb_store = [&](int round) {
-#pragma unroll
-    for (int u = 0; u < SBU; ++u) {
-      const int i = (round * SBU + u) * NT + tid;
-      const bool ok = i < sb_units;
-      if (sb_vec) {
-        const unsigned e0 = 8u * (unsigned)i;
-        const unsigned n = div_g(e0), g = e0 - n * (unsigned)G;
-        u32x4 lo, hi;                                 // (s_g | b_g << 16) for g .. g+7
-        lo.x = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x07060302u);
-        lo.z = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x05040100u);
-        lo.w = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x07060302u);
-        hi.x = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x05040100u);
-        hi.y = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x07060302u);
-        hi.z = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x05040100u);
-        hi.w = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x07060302u);
-        // Units past the table write into the partial-sum slots (16 KB, not
-        // read before the end of the loop).
-        const unsigned o = ok ? (unsigned)L.sb + 4u * (n * (unsigned)L.sbs + g)
-                              : (unsigned)L.red + 32u * ((unsigned)tid & 511u);
-        *reinterpret_cast<u32x4*>(lds + o) = lo;
-        *reinterpret_cast<u32x4*>(lds + o + 16) = hi;
-      } else if (ok) {
-        const unsigned n = div_g((unsigned)i), g = (unsigned)i - n * (unsigned)G;
-        sbl[n * L.sbs + g] = (sbs[u].x & 0xFFFFu) | (sbb[u].x << 16);
-      }
-    }
-  };
+  const unsigned char* abase = xl + (h * 16 + j) * kSlot16;
+  const float* xsbase = xsl + 4 * h;
+  const unsigned* sbbase = sbl + j * L.sbs;
+  // Past a run: the zero image's row sums double as a zero (s, b) pair
+  // (8-byte aligned whatever G is).
+  const unsigned* sbzero = reinterpret_cast<const unsigned*>(xsl + GP * 32);
+  auto rel_row = [&](int c) { return SWIGLU ? (c & 1) * Nh + (c >> 1) : c; };
+  // Lane j of tile t reads logical column 16t + j: weight row rel_row(j) plus
+  // the tile's rows (16 per tile, or 8 gate and 8 up rows with SWIGLU).
+  const unsigned woff = (unsigned)rel_row(j) * rowbytes + 8u * h;
+  constexpr unsigned kTileRows = SWIGLU ? 8u : 16u;
 
-  // ---- blocks of the run (as qgemm_w4_m8).
-  struct Blk {
-    int t, p, left;
-  };
-  const Blk kfirst = {tfirst, (b0 - tfirst * bpt) * DB, nb};
-  auto next = [&](Blk k) {
-    k.p += DB;
-    k.t += k.p == GP;
-    k.p = k.p == GP ? 0 : k.p;
-    k.left -= 1;
-    return k;
-  };
-  u32x4 st[D];
-  auto codes_at = [&](const Blk& k) {
-    return k.left > 0 ? (unsigned)k.t * kTileRows * rowbytes + 64u * (unsigned)k.p : kSkip;
-  };
-  // Step d of the block at scalar offset `so`: 8 bytes of each group.
-  auto load = [&](unsigned so, int d, u32x4& w) {
-    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(wr, woff + 64u * d, so, 0);
-    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(wr, woff + 32u + 64u * d, so, 0);
-    w = u32x4{a.x, a.y, b.x, b.y};
-  };
-
-  // ---- prologue.
-  Blk kl = kfirst;
-  auto ring_load = [&](int d) {
-    load(codes_at(kl), d % DB, st[d]);
-    if (d % DB == DB - 1) kl = next(kl);
-  };
-  x_load(0);
-  sb_load(0);
+  for (int bb = 0; bb < rounds; bb += XB) {
+    x_load(bb);
 #pragma unroll
-  for (int d = 0; d < D0; ++d) ring_load(d);
+    for (int i = 0; i < XB; ++i) x_store_round(bb, i);
+  }
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int i = tid; i < kPair16 / 16; i += NT)      // the zero image
@@ -263,167 +188,258 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
     if (tid < 32) xsl[GP * 32 + tid] = 0.0f;
     for (int i = tid; i < WGC * 2; i += NT) sbl[(i >> 1) * L.sbs + G + (i & 1)] = 0u;
   }
-#pragma unroll
-  for (int i = 0; i < XB; ++i) {
-    if (D0 + i < D) ring_load(D0 + i);
-    x_store_round(0, i);
-  }
-  sb_store(0);
-  for (int bb = XB; bb < rounds; bb += XB) {
-    x_load(bb);
-    x_store(bb);
-  }
-  for (int round = 1; round * SBU * NT < sb_units; ++round) {
-    sb_load(round);
-    sb_store(round);
-  }
-#pragma unroll
-  for (int d = D0 + XB; d < D; ++d) ring_load(d);
-  if (lane == 0) {
-    run_tiles[2 * wave] = nb > 0 ? tfirst : 1 << 30;
-    run_tiles[2 * wave + 1] = nb > 0 ? (b0 + nb - 1) / bpt : -1;
-  }
-  __syncthreads();
 
-  // ---- main loop.
-  const unsigned char* abase = xl + (h * 16 + j) * kSlot16;
-  const float* xsbase = xsl + 4 * h;
-  const unsigned* sbbase = sbl + j * L.sbs;
-  // Past the run: the zero image's row sums double as a zero (s, b) pair
-  // (8-byte aligned whatever G is).
-  const unsigned* sbzero = reinterpret_cast<const unsigned*>(xsl + GP * 32);
-  struct Ops {
-    u32x4 A[4];
-    f32x4 xs0, xs1;
-    u32x2 sb;
-  };
-  struct Base {
-    const unsigned char* a;
-    const float* xs;
-    const unsigned* sb;
-  };
-  auto base_of = [&](const Blk& k) {
-    const bool in = k.left > 0;                      // uniform
-    const int img = in ? k.p : GP;
-    Base b;
-    b.a = abase + img * kPair16;
-    b.xs = xsbase + img * 32;
-    b.sb = in ? sbbase + k.t * 16 * L.sbs + 2 * k.p : sbzero;
-    return b;
-  };
-  auto fetch = [&](const Base& b, int d, Ops& o) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      o.A[t] = *reinterpret_cast<const u32x4*>(b.a + d * kPair16 + t * kTRow16);
-    o.xs0 = *reinterpret_cast<const f32x4*>(b.xs + d * 32);
-    o.xs1 = *reinterpret_cast<const f32x4*>(b.xs + d * 32 + 16);
-    o.sb = *reinterpret_cast<const u32x2*>(b.sb + 2 * d);
-  };
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  int acc_tile = tfirst;
-  auto flush = [&](int seg) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      red[((wave * 2 + seg) * 16 + 4 * h + e) * 16 + j] = acc[e];
-      acc[e] = 0.0f;
-    }
-  };
-  auto epilogue = [&](const f32x4& C0, const f32x4& C1, const Ops& o) {
-    const float s0 = half_lo(o.sb.x), s1 = half_lo(o.sb.y);
-    const float c0 = fmaf(-TR::c0, s0, half_hi(o.sb.x));
-    const float c1 = fmaf(-TR::c0, s1, half_hi(o.sb.y));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] = fmaf(s0, C0[e], fmaf(c0, o.xs0[e], acc[e]));
-      acc[e] = fmaf(s1, C1[e], fmaf(c1, o.xs1[e], acc[e]));
-    }
-  };
+  for (int cg = wk; cg < ngroups; cg += workers) {
+    const int wg0 = cg * cols;                        // first logical column
+    const int wgcols = min(cols, N - wg0);
+    const int tiles = (wgcols + 15) >> 4;
+    const int nblk = tiles * bpt;
+    const int b0 = (wave * nblk) / NW;
+    const int nb = ((wave + 1) * nblk) / NW - b0;
+    const int tfirst = b0 / bpt;
+    // Weight row of logical column c of this group, relative to `row0`.
+    const int row0 = SWIGLU ? (wg0 >> 1) : wg0;
+    const int nrows = SWIGLU ? N - row0 : wgcols;     // rows the buffers may touch
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(wq) + (size_t)row0 * rowbytes, (short)0, nrows * rowbytes,
+        kBufferFlags);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(scales) + (size_t)row0 * G, (short)0, nrows * G * 2,
+        kBufferFlags);
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(biases) + (size_t)row0 * G, (short)0, nrows * G * 2,
+        kBufferFlags);
 
-  Ops cur, prev;
-  const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-  f32x4 P0 = zero4, P1 = zero4;
-  prev.sb = u32x2{0u, 0u};                           // step -1 adds exactly nothing
-  prev.xs0 = zero4;
-  prev.xs1 = zero4;
-  int prev_tile = tfirst;
-  Blk kc = kfirst;
-  Base bc = base_of(kc);
-  fetch(bc, 0, cur);
-  auto run_block = [&](int r, bool reload) {
-    const Blk kn = next(kc);
-    const Base bn = base_of(kn);
-    const unsigned so = codes_at(kl);
+    // ---- scale/bias table: row n of the table is logical column n.
+    const int sb_units = sb_vec ? wgcols * G / 8 : wgcols * G;
+    u32x4 sbs[SBU], sbb[SBU];
+    auto sb_load = [&](int round) {
 #pragma unroll
-    for (int d = 0; d < DB; ++d) {
-      u32x4 bq[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) bq[t] = unpack_codes(st[r * DB + d][t], magic);
-      f32x4 C0 = mfma16x16x32<TR::f16>(cur.A[0], bq[0], zero4);
-      f32x4 C1 = mfma16x16x32<TR::f16>(cur.A[2], bq[2], zero4);
-      C0 = mfma16x16x32<TR::f16>(cur.A[1], bq[1], C0);
-      C1 = mfma16x16x32<TR::f16>(cur.A[3], bq[3], C1);
-      Ops nxt;
-      if (d + 1 < DB) fetch(bc, d + 1, nxt);
-      else fetch(bn, 0, nxt);
-      if (d == 0 && kc.t != prev_tile) {              // uniform: the last step ended a tile
-        epilogue(P0, P1, prev);
-        flush(0);
-        acc_tile = kc.t;
-        prev_tile = kc.t;
-      } else {
-        epilogue(P0, P1, prev);
+      for (int u = 0; u < SBU; ++u) {
+        const int i = (round * SBU + u) * NT + tid;
+        if (sb_vec) {
+          const unsigned e0 = 8u * (unsigned)i;
+          const unsigned n = div_g(e0), g = e0 - n * (unsigned)G;
+          const unsigned off =
+              i < sb_units ? 2u * ((unsigned)rel_row((int)n) * (unsigned)G + g) : kOutOfRange;
+          sbs[u] = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
+          sbb[u] = __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0);
+        } else {
+          const unsigned n = div_g((unsigned)i), g = (unsigned)i - n * (unsigned)G;
+          const unsigned off =
+              i < sb_units ? 2u * ((unsigned)rel_row((int)n) * (unsigned)G + g) : kOutOfRange;
+          sbs[u].x = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
+          sbb[u].x = __builtin_amdgcn_raw_buffer_load_b16(br, off, 0, 0);
+        }
       }
-      if (reload) load(so, d, st[r * DB + d]);
-      P0 = C0;
-      P1 = C1;
-      prev = cur;
-      cur = nxt;
-    }
-    if (reload) kl = next(kl);
-    kc = kn;
-    bc = bn;
-  };
-  int i = 0;
-  for (; i + RB <= nb; i += RB) {
+    };
+    auto sb_store = [&](int round) {
 #pragma unroll
-    for (int r = 0; r < RB; ++r) run_block(r, true);
-  }
-#pragma unroll
-  for (int r = 0; r < RB - 1; ++r)
-    if (i + r < nb) run_block(r, false);
-  epilogue(P0, P1, prev);
-  flush(acc_tile > tfirst ? 1 : 0);
+      for (int u = 0; u < SBU; ++u) {
+        const int i = (round * SBU + u) * NT + tid;
+        const bool ok = i < sb_units;
+        if (sb_vec) {
+          const unsigned e0 = 8u * (unsigned)i;
+          const unsigned n = div_g(e0), g = e0 - n * (unsigned)G;
+          u32x4 lo, hi;                               // (s_g | b_g << 16) for g .. g+7
+          lo.x = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x05040100u);
+          lo.y = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x07060302u);
+          lo.z = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x05040100u);
+          lo.w = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x07060302u);
+          hi.x = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x05040100u);
+          hi.y = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x07060302u);
+          hi.z = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x05040100u);
+          hi.w = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x07060302u);
+          // Units past the table write into the partial-sum slots (16 KB,
+          // not read until this group's loop has ended).
+          const unsigned o = ok ? (unsigned)L.sb + 4u * (n * (unsigned)L.sbs + g)
+                                : (unsigned)L.red + 32u * ((unsigned)tid & 511u);
+          *reinterpret_cast<u32x4*>(lds + o) = lo;
+          *reinterpret_cast<u32x4*>(lds + o + 16) = hi;
+        } else if (ok) {
+          const unsigned n = div_g((unsigned)i), g = (unsigned)i - n * (unsigned)G;
+          sbl[n * L.sbs + g] = (sbs[u].x & 0xFFFFu) | (sbb[u].x << 16);
+        }
+      }
+    };
 
-  // ---- reduce: each output tile adds the flushed partials of the runs that
-  // cover it, in wave order; SWIGLU takes the (gate, up) column pairs.
-  __syncthreads();
-  auto tile_sum = [&](int t, int within) {
-    float s = 0.0f;
+    // ---- blocks of the run (as qgemm_w4_m8).
+    struct Blk {
+      int t, p, left;
+    };
+    const Blk kfirst = {tfirst, (b0 - tfirst * bpt) * DB, nb};
+    auto next = [&](Blk k) {
+      k.p += DB;
+      k.t += k.p == GP;
+      k.p = k.p == GP ? 0 : k.p;
+      k.left -= 1;
+      return k;
+    };
+    u32x4 st[D];
+    auto codes_at = [&](const Blk& k) {
+      return k.left > 0 ? (unsigned)k.t * kTileRows * rowbytes + 64u * (unsigned)k.p : kSkip;
+    };
+    // Step d of the block at scalar offset `so`: 8 bytes of each group.
+    auto load = [&](unsigned so, int d, u32x4& w) {
+      const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(wr, woff + 64u * d, so, 0);
+      const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(wr, woff + 32u + 64u * d, so, 0);
+      w = u32x4{a.x, a.y, b.x, b.y};
+    };
+
+    // ---- table, then the weight ring; run bounds for the reduction.
+    Blk kl = kfirst;
+    sb_load(0);
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const int tb = run_tiles[2 * w], te = run_tiles[2 * w + 1];
-      if (t >= tb && t <= te) s += red[((w * 2 + (t - tb)) * 256) + within];
+    for (int d = 0; d < D; ++d) {
+      load(codes_at(kl), d % DB, st[d]);
+      if (d % DB == DB - 1) kl = next(kl);
     }
-    return s;
-  };
-  if constexpr (SWIGLU) {
-    for (int idx = tid; idx < tiles * 128; idx += NT) {
-      const int t = idx >> 7;
-      const int m = (idx >> 3) & 15;
-      const int c = t * 16 + 2 * (idx & 7);           // gate column; c + 1 is its up
-      if (m < M && c < wgcols) {
-        const float g = tile_sum(t, m * 16 + (c & 15));
-        const float u = tile_sum(t, m * 16 + (c & 15) + 1);
-        y[(size_t)m * Nh + ((wg0 + c) >> 1)] = swiglu(g, u);
+    sb_store(0);
+    for (int round = 1; round * SBU * NT < sb_units; ++round) {
+      sb_load(round);
+      sb_store(round);
+    }
+    if (lane == 0) {
+      run_tiles[2 * wave] = nb > 0 ? tfirst : 1 << 30;
+      run_tiles[2 * wave + 1] = nb > 0 ? (b0 + nb - 1) / bpt : -1;
+    }
+    __syncthreads();
+
+    // ---- main loop.
+    struct Ops {
+      u32x4 A[4];
+      f32x4 xs0, xs1;
+      u32x2 sb;
+    };
+    struct Base {
+      const unsigned char* a;
+      const float* xs;
+      const unsigned* sb;
+    };
+    auto base_of = [&](const Blk& k) {
+      const bool in = k.left > 0;                     // uniform
+      const int img = in ? k.p : GP;
+      Base bs;
+      bs.a = abase + img * kPair16;
+      bs.xs = xsbase + img * 32;
+      bs.sb = in ? sbbase + k.t * 16 * L.sbs + 2 * k.p : sbzero;
+      return bs;
+    };
+    auto fetch = [&](const Base& bs, int d, Ops& o) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        o.A[t] = *reinterpret_cast<const u32x4*>(bs.a + d * kPair16 + t * kTRow16);
+      o.xs0 = *reinterpret_cast<const f32x4*>(bs.xs + d * 32);
+      o.xs1 = *reinterpret_cast<const f32x4*>(bs.xs + d * 32 + 16);
+      o.sb = *reinterpret_cast<const u32x2*>(bs.sb + 2 * d);
+    };
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int acc_tile = tfirst;
+    auto flush = [&](int seg) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        red[((wave * 2 + seg) * 16 + 4 * h + e) * 16 + j] = acc[e];
+        acc[e] = 0.0f;
+      }
+    };
+    auto epilogue = [&](const f32x4& C0, const f32x4& C1, const Ops& o) {
+      const float s0 = half_lo(o.sb.x), s1 = half_lo(o.sb.y);
+      const float c0 = fmaf(-TR::c0, s0, half_hi(o.sb.x));
+      const float c1 = fmaf(-TR::c0, s1, half_hi(o.sb.y));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = fmaf(s0, C0[e], fmaf(c0, o.xs0[e], acc[e]));
+        acc[e] = fmaf(s1, C1[e], fmaf(c1, o.xs1[e], acc[e]));
+      }
+    };
+
+    Ops cur, prev;
+    const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 P0 = zero4, P1 = zero4;
+    prev.sb = u32x2{0u, 0u};                         // step -1 adds exactly nothing
+    prev.xs0 = zero4;
+    prev.xs1 = zero4;
+    int prev_tile = tfirst;
+    Blk kc = kfirst;
+    Base bc = base_of(kc);
+    fetch(bc, 0, cur);
+    auto run_block = [&](int r, bool reload) {
+      const Blk kn = next(kc);
+      const Base bn = base_of(kn);
+      const unsigned so = codes_at(kl);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        u32x4 bq[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bq[t] = unpack_codes(st[r * DB + d][t], magic);
+        f32x4 C0 = mfma16x16x32<TR::f16>(cur.A[0], bq[0], zero4);
+        f32x4 C1 = mfma16x16x32<TR::f16>(cur.A[2], bq[2], zero4);
+        C0 = mfma16x16x32<TR::f16>(cur.A[1], bq[1], C0);
+        C1 = mfma16x16x32<TR::f16>(cur.A[3], bq[3], C1);
+        Ops nxt;
+        if (d + 1 < DB) fetch(bc, d + 1, nxt);
+        else fetch(bn, 0, nxt);
+        if (d == 0 && kc.t != prev_tile) {            // uniform: the last step ended a tile
+          epilogue(P0, P1, prev);
+          flush(0);
+          acc_tile = kc.t;
+          prev_tile = kc.t;
+        } else {
+          epilogue(P0, P1, prev);
+        }
+        if (reload) load(so, d, st[r * DB + d]);
+        P0 = C0;
+        P1 = C1;
+        prev = cur;
+        cur = nxt;
+      }
+      if (reload) kl = next(kl);
+      kc = kn;
+      bc = bn;
+    };
+    int i = 0;
+    for (; i + RB <= nb; i += RB) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) run_block(r, true);
+    }
+#pragma unroll
+    for (int r = 0; r < RB - 1; ++r)
+      if (i + r < nb) run_block(r, false);
+    epilogue(P0, P1, prev);
+    flush(acc_tile > tfirst ? 1 : 0);
+
+    // ---- reduce: each output tile adds the flushed partials of the runs
+    // that cover it, in wave order; SWIGLU takes the (gate, up) column pairs.
+    __syncthreads();
+    auto tile_sum = [&](int t, int within) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int tb = run_tiles[2 * w], te = run_tiles[2 * w + 1];
+        if (t >= tb && t <= te) sum += red[((w * 2 + (t - tb)) * 256) + within];
+      }
+      return sum;
+    };
+    if constexpr (SWIGLU) {
+      for (int idx = tid; idx < tiles * 128; idx += NT) {
+        const int t = idx >> 7;
+        const int m = (idx >> 3) & 15;
+        const int c = t * 16 + 2 * (idx & 7);         // gate column; c + 1 is its up
+        if (m < M && c < wgcols) {
+          const float g = tile_sum(t, m * 16 + (c & 15));
+          const float u = tile_sum(t, m * 16 + (c & 15) + 1);
+          y[(size_t)m * Nh + ((wg0 + c) >> 1)] = swiglu(g, u);
+        }
+      }
+    } else {
+      for (int idx = tid; idx < tiles * 256; idx += NT) {
+        const int t = idx >> 8;
+        const int m = (idx >> 4) & 15;
+        const int c = t * 16 + (idx & 15);
+        if (m < M && c < wgcols) y[(size_t)m * N + wg0 + c] = tile_sum(t, idx & 255);
       }
     }
-  } else {
-    for (int idx = tid; idx < tiles * 256; idx += NT) {
-      const int t = idx >> 8;
-      const int m = (idx >> 4) & 15;
-      const int c = t * 16 + (idx & 15);
-      if (m < M && c < wgcols) y[(size_t)m * N + wg0 + c] = tile_sum(t, idx & 255);
-    }
+    __syncthreads();                                  // the table, runs and partials are reused
   }
 }
 
@@ -447,6 +463,14 @@ template <int ACT, int DB, int RB, bool SWIGLU>
 hipError_t launch_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
                       const uint16_t* biases, float* y, int M, int K, int N, int cols,
                       hipStream_t stream) {
+  // One work-group per CU: rsets row sets of `workers` workers each (a
+  // multiple of 8 when there are several row sets, for the XCD layout).
+  const int rsets = (M + 15) / 16;
+  const int groups = (N + cols - 1) / cols;
+  const int cus = device_cus();
+  int workers = rsets > 1 ? (cus / rsets) / 8 * 8 : cus;
+  if (workers < 8) workers = 8;
+  if (rsets == 1 && workers > groups) workers = groups;
   const M16Layout L = m16_layout(K >> 6, 16 * kM16Tiles, kM16Waves, kM16XB);
   auto kern = qgemm_w4_m16<ACT, kM16Waves, kM16Tiles, DB, RB, 2, kM16XB, SWIGLU>;
   if (L.total > 65536) {
@@ -455,9 +479,9 @@ hipError_t launch_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
                                              L.total);
     if (e != hipSuccess) return e;
   }
-  const dim3 grid((N + cols - 1) / cols);
+  const dim3 grid(workers * rsets);
   hipLaunchKernelGGL(kern, grid, dim3(64 * kM16Waves), L.total, stream, x, wq, scales, biases,
-                     y, M, K, N, cols);
+                     y, M, K, N, cols, rsets, workers);
   return hipGetLastError();
 }
 
@@ -479,7 +503,7 @@ hipError_t launch_m16_blocks(const void* x, const uint8_t* wq, const uint16_t* s
 
 bool qgemm_m16_fits(int M, int K, int act) {
   // One batch of staging (K <= 64 * waves * XB) keeps the padded image small.
-  return M <= 16 && act != ACT_FP32 && K <= 64 * kM16Waves * kM16XB &&
+  return M <= 64 && act != ACT_FP32 && K <= 64 * kM16Waves * kM16XB &&
          m16_layout(K >> 6, 16 * kM16Tiles, kM16Waves, kM16XB).total <= kLdsLimit;
 }
 
