@@ -71,6 +71,8 @@ def compare(vqv, c, B, T, accept=None, want_y=True, ws=None):
     (8, 512, 1024, "bf16", 1, 8), (8, 512, 1024, "fp16", 2, 4), (4, 1280, 3000, "bf16", 1, 4),
     (1, 64, 17, "bf16", 1, 1), (8, 192, 999, "fp16", 8, 1), (5, 320, 5000, "bf16", 1, 5),
     (8, 2560, 17408, "bf16", 1, 8), (6, 5120, 1000, "bf16", 3, 2), (8, 640, 12000, "fp16", 4, 2),
+    # vocabulary widths: the persistent whole-tile kernel's fused epilogue
+    (8, 512, 70000, "bf16", 1, 8), (4, 1024, 66001, "fp16", 2, 2), (1, 2560, 66000, "bf16", 1, 1),
 ])
 def test_fused_matches_separate(vqv, M, K, N, act, B, T):
     compare(vqv, case(M, K, N, act, seed=M * 7 + K + N), B, T)

@@ -56,6 +56,10 @@ SHAPES = [
     # Row sets of 16 (17..64 rows): several column groups per XCD, ragged
     # last row set, a padded grid.
     (64, 2560, 5000), (48, 1280, 3001), (20, 512, 12000), (64, 64, 99), (40, 2560, 17408),
+    # Wide outputs (at least two column tiles per wave): waves own whole
+    # tiles (one row set, a ragged last tile, three and four row sets).
+    (8, 512, 70000), (16, 1024, 66000), (12, 2560, 66001), (48, 512, 30000), (64, 1536, 25000),
+    (3, 2560, 66001),
 ]
 
 

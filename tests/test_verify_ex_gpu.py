@@ -175,7 +175,7 @@ def compare_fused(vqv, c, B, T, accept=None, draft_len=None, want_y=True, ws=Non
     (8, 512, 1024, "bf16", 1, 8), (8, 512, 1024, "fp16", 2, 4), (4, 1280, 3000, "bf16", 1, 4),
     (1, 64, 17, "bf16", 1, 1), (8, 192, 999, "fp16", 8, 1), (5, 320, 5000, "bf16", 1, 5),
     (8, 2560, 17408, "bf16", 1, 8), (6, 5120, 1000, "bf16", 3, 2), (8, 640, 12000, "fp16", 4, 2),
-    (2, 128, 1, "bf16", 1, 2),
+    (2, 128, 1, "bf16", 1, 2), (8, 512, 70000, "fp16", 2, 4), (3, 1024, 66001, "bf16", 1, 3),
 ])
 def test_fused_ex_matches_separate(vqv, M, K, N, act, B, T):
     compare_fused(vqv, case(M, K, N, act, seed=M * 11 + K + N), B, T)

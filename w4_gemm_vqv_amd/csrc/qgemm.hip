@@ -974,6 +974,12 @@ template <int ACT>
 hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                          const uint16_t* biases, float* y, int M, int K, int N,
                          hipStream_t s) {
+  if (qgemm_wide_fits(M, K, N, ACT)) {
+    // Vocabulary widths: whole-tile waves (the fused verify's projection
+    // takes the same kernel, so the two paths agree bit for bit).
+    const VerifyArgs none{};
+    return launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, ACT, none, s);
+  }
   if constexpr (ACT != ACT_FP32) if (M <= 8 && m8_fits(K)) {
     const VerifyArgs none{};
     return launch_m8_any<ACT>(x, wq, scales, biases, y, M, K, N, none, s);
@@ -1022,8 +1028,12 @@ hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales
 
 int qgemm_verify_groups(int M, int K, int N, int act) {
   // The projection kernel of the fused path writes one partial per
-  // work-group and row; verify_finish (verify.hip) reduces them.
-  if (M > 8 || act == ACT_FP32 || !m8_fits(K)) return 0;
+  // work-group and row; verify_finish (verify.hip) reduces them. Vocabulary widths
+  // take the persistent whole-tile kernel (one partial per CU and row
+  // instead of one per 80 columns).
+  if (M > 8 || act == ACT_FP32) return 0;
+  if (qgemm_wide_fits(M, K, N, act)) return qgemm_wide_groups(M);
+  if (!m8_fits(K)) return 0;
   const int cols = m8_cols(N);
   return (N + cols - 1) / cols;
 }
@@ -1032,8 +1042,12 @@ hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t*
                                const uint16_t* biases, float* y, int M, int K, int N, int act,
                                const VerifyArgs& va, hipStream_t stream) {
   hipError_t e = hipErrorInvalidValue;
-  if (act == ACT_BF16) e = launch_m8_any<ACT_BF16>(x, wq, scales, biases, y, M, K, N, va, stream);
-  if (act == ACT_FP16) e = launch_m8_any<ACT_FP16>(x, wq, scales, biases, y, M, K, N, va, stream);
+  if (qgemm_wide_fits(M, K, N, act))
+    e = launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, act, va, stream);
+  else if (act == ACT_BF16)
+    e = launch_m8_any<ACT_BF16>(x, wq, scales, biases, y, M, K, N, va, stream);
+  else if (act == ACT_FP16)
+    e = launch_m8_any<ACT_FP16>(x, wq, scales, biases, y, M, K, N, va, stream);
   if (e != hipSuccess) return e;
   return launch_verify_finish(va.partials, qgemm_verify_groups(M, K, N, act), va, stream);
 }

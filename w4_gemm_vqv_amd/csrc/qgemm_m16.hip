@@ -33,6 +33,7 @@
 // gate and up values of one hidden unit land in adjacent output columns of
 // the same tile and the final reduction pairs them.
 
+#include "argmax.h"
 #include "qgemm_common.h"
 #include "vqv_internal.h"
 
@@ -443,6 +444,331 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide outputs (vocabulary projections, N/16 tiles far above the wave count).
+// The per-step arithmetic and the 16-row MFMA layout are those of
+// qgemm_w4_m16; the split is by whole column tiles: persistent work-groups
+// stage their row set's activations once (one barrier), then each wave
+// streams its own tiles over all of K (tiles tbeg + w, tbeg + w + 8, ... of
+// its worker's range), with a weight ring that runs on across tiles, a
+// private (s, b) table in LDS rebuilt per tile from loads issued a tile
+// ahead, and each finished tile stored straight to y. No barrier, partial
+// sum or reduction follows the staging. Row sets and the XCD layout are as
+// in qgemm_w4_m16. With va.argmax set (one row set, M <= 8) each lane also
+// keeps the top two of its rows over all its columns, and the work-group
+// writes one top-two partial per row for verify_finish (the greedy verify's
+// first half, as in qgemm_w4_m8's fused epilogue).
+template <int ACT, int DB, int RB>
+__global__ __launch_bounds__(512) void qgemm_w4_wide(
+    const void* __restrict__ x, const uint8_t* __restrict__ wq,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
+    float* __restrict__ y, int M, int K, int N, int rsets, int workers, int tpw,
+    VerifyArgs va) {
+  using TR = ActTraits<ACT>;
+  static_assert(TR::parts == 1, "16-bit activations only");
+  constexpr int NW = 8, NT = 512, XB = 5;
+  const bool fused = va.argmax != nullptr;           // uniform
+  constexpr int D = DB * RB;
+  constexpr unsigned kSkip = 0x7FF00000u;
+
+  const int T = (N + 15) >> 4;                        // column tiles
+  int wk = blockIdx.x, rs = 0;
+  if (rsets > 1) {
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    rs = local % rsets;
+    wk = (local / rsets) * 8 + xcd;
+  }
+  const int tbeg = wk * tpw, tend = min(T, tbeg + tpw);
+  if (wk >= workers || tbeg >= T) {                  // the whole group leaves
+    if (fused && threadIdx.x < 8)                     // with an empty partial
+      va.partials[(size_t)blockIdx.x * 8 + threadIdx.x] = top2_pack(top2_none());
+    return;
+  }
+  x = static_cast<const uint16_t*>(x) + (size_t)rs * 16 * K;
+  y += (size_t)rs * 16 * N;
+  M = min(16, M - 16 * rs);
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15;
+  const int h = lane >> 4;
+  const int G = K >> 6;                               // even, a multiple of 8 (host)
+  const int GP = G >> 1;
+  const int bpt = GP / DB;
+  const unsigned rowbytes = (unsigned)K >> 1;
+  const M16Layout L = m16_layout(G, 16, NW, XB);
+  unsigned char* xl = lds;
+  float* xsl = reinterpret_cast<float*>(lds + L.xs);
+  // Per-wave table: [16 columns][G] of (s | b << 16), after the row sums.
+  unsigned* tab = reinterpret_cast<unsigned*>(lds + L.sb) + wave * 16 * G;
+
+  unsigned magic;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(TR::magic));
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(x), (short)0, M * K * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(wq), (short)0, (unsigned)N * rowbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(scales), (short)0, (unsigned)N * G * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(biases), (short)0, (unsigned)N * G * 2, kBufferFlags);
+
+  // ---- this wave's tiles and blocks: tile ordinal k is column tile
+  // tbeg + wave + 8k; block (k, p) covers pairs p .. p + DB - 1.
+  const int ntile = tend > tbeg + wave ? (tend - tbeg - wave + NW - 1) / NW : 0;
+  const int nb = ntile * bpt;
+  struct Blk {
+    int k, p, left;
+  };
+  auto next = [&](Blk b) {
+    b.p += DB;
+    b.k += b.p == GP;
+    b.p = b.p == GP ? 0 : b.p;
+    b.left -= 1;
+    return b;
+  };
+  auto col0 = [&](int k) { return (tbeg + wave + NW * k) * 16; };
+  const unsigned woff = (unsigned)j * rowbytes + 8u * h;
+  auto codes_at = [&](const Blk& b) {
+    return b.left > 0 ? (unsigned)col0(b.k) * rowbytes + 64u * (unsigned)b.p : kSkip;
+  };
+  u32x4 st[D];
+  auto load = [&](unsigned so, int d, u32x4& w) {
+    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(wr, woff + 64u * d, so, 0);
+    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(wr, woff + 32u + 64u * d, so, 0);
+    w = u32x4{a.x, a.y, b.x, b.y};
+  };
+  // A tile's table: 16 columns x G groups, contiguous in memory; unit u (16
+  // bytes, groups 8(u % (G/8)) ..) of each array per lane and round.
+  const int tunits = 2 * G;                           // 16 * G / 8
+  u32x4 ts[2], tb[2];
+  auto tab_load = [&](int k) {                        // k may be past the run: zeros
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int u = r * 64 + lane;
+      const int c = col0(k) + (8 * u) / G;
+      const bool ok = k < ntile && u < tunits && c < N;
+      const unsigned off = ok ? 2u * ((unsigned)col0(k) * (unsigned)G + 8u * (unsigned)u) : kOutOfRange;
+      ts[r] = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
+      tb[r] = __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0);
+    }
+  };
+  auto tab_store = [&]() {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int u = r * 64 + lane;
+      if (u < tunits) {
+        u32x4 lo, hi;
+        lo.x = __builtin_amdgcn_perm(tb[r].x, ts[r].x, 0x05040100u);
+        lo.y = __builtin_amdgcn_perm(tb[r].x, ts[r].x, 0x07060302u);
+        lo.z = __builtin_amdgcn_perm(tb[r].y, ts[r].y, 0x05040100u);
+        lo.w = __builtin_amdgcn_perm(tb[r].y, ts[r].y, 0x07060302u);
+        hi.x = __builtin_amdgcn_perm(tb[r].z, ts[r].z, 0x05040100u);
+        hi.y = __builtin_amdgcn_perm(tb[r].z, ts[r].z, 0x07060302u);
+        hi.z = __builtin_amdgcn_perm(tb[r].w, ts[r].w, 0x05040100u);
+        hi.w = __builtin_amdgcn_perm(tb[r].w, ts[r].w, 0x07060302u);
+        *reinterpret_cast<u32x4*>(tab + 8 * u) = lo;
+        *reinterpret_cast<u32x4*>(tab + 8 * u + 4) = hi;
+      }
+    }
+  };
+
+  // ---- prologue: the activation loads first, then tile 0's table and the
+  // weight ring; staging; tile 0's table to LDS and tile 1's loads.
+  const int ngrp = 2 * GP;
+  const int rounds = (ngrp + NW - 1) / NW;            // <= XB (host: K <= 64 * NW * XB)
+  const int e8 = lane & 7;
+  const int mm = lane >> 3;
+  u32x4 xv[XB][2];
+#pragma unroll
+  for (int i = 0; i < XB; ++i) {
+    const int g = wave + NW * i;
+    const int kk = 64 * g + 8 * e8;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = mm + 8 * r;
+      const bool ok = row < M && kk < K;
+      xv[i][r] = __builtin_amdgcn_raw_buffer_load_b128(
+          xr, ok ? (unsigned)((row * K + kk) * 2) : kOutOfRange, 0, 0);
+    }
+  }
+  tab_load(0);
+  const Blk kfirst = {0, 0, nb};
+  Blk kl = kfirst;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    load(codes_at(kl), d % DB, st[d]);
+    if (d % DB == DB - 1) kl = next(kl);
+  }
+  (void)rounds;
+  const unsigned xl_lane = (e8 & 1) * kTRow16 + ((e8 >> 1) * 16 + mm) * kSlot16;
+#pragma unroll
+  for (int i = 0; i < XB; ++i) {
+    const int g = wave + NW * i;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const float s8 = sum8_lanes(block_sum<ACT>(xv[i][r]));
+      *reinterpret_cast<u32x4*>(xl + (g >> 1) * kPair16 + (g & 1) * 2 * kTRow16 + xl_lane +
+                                r * 8 * kSlot16) = permute_pairs(xv[i][r]);
+      xsl[g * 16 + mm + 8 * r] = s8;
+    }
+  }
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < kPair16 / 16; i += NT)      // the zero image
+      *reinterpret_cast<u32x4*>(xl + GP * kPair16 + 16 * i) = z;
+    if (tid < 32) xsl[GP * 32 + tid] = 0.0f;
+  }
+  tab_store();
+  tab_load(1);
+  __syncthreads();                                    // the activation image is complete
+
+  // ---- main loop (the step, ring and deferred epilogue of qgemm_w4_m16).
+  const unsigned char* abase = xl + (h * 16 + j) * kSlot16;
+  const float* xsbase = xsl + 4 * h;
+  const unsigned* tbase = tab + j * G;
+  const unsigned* sbzero = reinterpret_cast<const unsigned*>(xsl + GP * 32);
+  struct Ops {
+    u32x4 A[4];
+    f32x4 xs0, xs1;
+    u32x2 sb;
+  };
+  struct Base {
+    const unsigned char* a;
+    const float* xs;
+    const unsigned* sb;
+  };
+  auto base_of = [&](const Blk& b) {
+    const bool in = b.left > 0;                       // uniform
+    const int img = in ? b.p : GP;
+    Base bs;
+    bs.a = abase + img * kPair16;
+    bs.xs = xsbase + img * 32;
+    bs.sb = in ? tbase + 2 * b.p : sbzero;
+    return bs;
+  };
+  auto fetch = [&](const Base& bs, int d, Ops& o) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      o.A[t] = *reinterpret_cast<const u32x4*>(bs.a + d * kPair16 + t * kTRow16);
+    o.xs0 = *reinterpret_cast<const f32x4*>(bs.xs + d * 32);
+    o.xs1 = *reinterpret_cast<const f32x4*>(bs.xs + d * 32 + 16);
+    o.sb = *reinterpret_cast<const u32x2*>(bs.sb + 2 * d);
+  };
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  Top2 best[4] = {top2_none(), top2_none(), top2_none(), top2_none()};
+  // A finished tile goes straight to y: lane (j, h) holds rows 4h .. 4h+3 of
+  // column j.
+  auto store_tile = [&](int k) {
+    const int c = col0(k) + j;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * h + e;
+      if (m < M && c < N) {
+        if (!fused || y) y[(size_t)m * N + c] = acc[e];
+        if (fused) top2_add(best[e], acc[e], c);
+      }
+      acc[e] = 0.0f;
+    }
+  };
+  auto epilogue = [&](const f32x4& C0, const f32x4& C1, const Ops& o) {
+    const float s0 = half_lo(o.sb.x), s1 = half_lo(o.sb.y);
+    const float c0 = fmaf(-TR::c0, s0, half_hi(o.sb.x));
+    const float c1 = fmaf(-TR::c0, s1, half_hi(o.sb.y));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] = fmaf(s0, C0[e], fmaf(c0, o.xs0[e], acc[e]));
+      acc[e] = fmaf(s1, C1[e], fmaf(c1, o.xs1[e], acc[e]));
+    }
+  };
+
+  Ops cur, prev;
+  const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 P0 = zero4, P1 = zero4;
+  prev.sb = u32x2{0u, 0u};                           // step -1 adds exactly nothing
+  prev.xs0 = zero4;
+  prev.xs1 = zero4;
+  Blk kc = kfirst;
+  Base bc = base_of(kc);
+  fetch(bc, 0, cur);
+  auto run_block = [&](int r, bool reload) {
+    const Blk kn = next(kc);
+    const unsigned so = codes_at(kl);
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      u32x4 bq[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bq[t] = unpack_codes(st[r * DB + d][t], magic);
+      f32x4 C0 = mfma16x16x32<TR::f16>(cur.A[0], bq[0], zero4);
+      f32x4 C1 = mfma16x16x32<TR::f16>(cur.A[2], bq[2], zero4);
+      C0 = mfma16x16x32<TR::f16>(cur.A[1], bq[1], C0);
+      C1 = mfma16x16x32<TR::f16>(cur.A[3], bq[3], C1);
+      Ops nxt;
+      if (d + 1 < DB) {
+        fetch(bc, d + 1, nxt);
+      } else {
+        // The next block starts a new tile: its table (loaded during this
+        // tile) replaces this tile's, whose remaining entries are already in
+        // registers, and the loads for the tile after it go out.
+        if (kn.p == 0 && kn.left > 0) {
+          tab_store();
+          tab_load(kn.k + 1);
+        }
+        fetch(base_of(kn), 0, nxt);
+      }
+      epilogue(P0, P1, prev);
+      if (d == 0 && kc.p == 0 && kc.k > 0) store_tile(kc.k - 1);  // uniform
+      if (reload) load(so, d, st[r * DB + d]);
+      P0 = C0;
+      P1 = C1;
+      prev = cur;
+      cur = nxt;
+    }
+    if (reload) kl = next(kl);
+    kc = kn;
+    bc = base_of(kc);
+  };
+  int i = 0;
+  for (; i + RB <= nb; i += RB) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) run_block(r, true);
+  }
+#pragma unroll
+  for (int r = 0; r < RB - 1; ++r)
+    if (i + r < nb) run_block(r, false);
+  epilogue(P0, P1, prev);
+  if (ntile > 0) store_tile(ntile - 1);
+
+  if (fused) {
+    // The 16 lanes of a (row, h) group reduce; the waves' results combine in
+    // wave order in LDS (the activation image is no longer read once every
+    // wave is past its loop); lane m of wave 0 writes row m's partial.
+    __syncthreads();
+    unsigned* cand = reinterpret_cast<unsigned*>(lds);  // [NW][8 rows] x (k1, i1, k2)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      top2_best16(best[e]);
+      if (j == 0 && h < 2) {
+        unsigned* q = cand + (wave * 8 + 4 * h + e) * 3;
+        q[0] = best[e].k1;
+        q[1] = (unsigned)best[e].i1;
+        q[2] = best[e].k2;
+      }
+    }
+    __syncthreads();
+    if (wave == 0 && lane < 8) {
+      Top2 r = top2_none();
+      for (int w = 0; w < NW; ++w) {
+        const unsigned* q = cand + (w * 8 + lane) * 3;
+        top2_merge(r, q[0], (int)q[1], q[2]);
+      }
+      va.partials[(size_t)blockIdx.x * 8 + lane] = top2_pack(r);
+    }
+  }
+}
+
 // Elementwise SwiGLU of a [M, 2*Nh] projection output (the fallback path).
 __global__ __launch_bounds__(256) void swiglu_rows(const float* __restrict__ yg,
                                                    float* __restrict__ hout, int M, int Nh) {
@@ -499,7 +825,74 @@ hipError_t launch_m16_blocks(const void* x, const uint8_t* wq, const uint16_t* s
   return launch_m16<ACT, 1, 8, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, s);
 }
 
+template <int ACT, int DB, int RB>
+hipError_t launch_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
+                       const uint16_t* biases, float* y, int M, int K, int N, int rsets,
+                       int workers, const VerifyArgs& va, hipStream_t stream) {
+  const int G = K >> 6;
+  const M16Layout L = m16_layout(G, 16, 8, 5);
+  const int lds_bytes = L.sb + 8 * 16 * G * 4;
+  auto kern = qgemm_w4_wide<ACT, DB, RB>;
+  if (lds_bytes > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             lds_bytes);
+    if (e != hipSuccess) return e;
+  }
+  const int T = (N + 15) / 16;
+  const int tpw = (T + workers - 1) / workers;
+  hipLaunchKernelGGL(kern, dim3(workers * rsets), dim3(512), lds_bytes, stream, x, wq, scales,
+                     biases, y, M, K, N, rsets, workers, tpw, va);
+  return hipGetLastError();
+}
+
+// Workers per row set: one work-group per CU (a multiple of 8 with several
+// row sets, for the XCD layout).
+int wide_workers(int rsets) {
+  const int cus = device_cus();
+  int w = rsets > 1 ? (cus / rsets) / 8 * 8 : cus;
+  return w < 8 ? 8 : w;
+}
+
+template <int ACT>
+hipError_t launch_wide_any(const void* x, const uint8_t* wq, const uint16_t* scales,
+                           const uint16_t* biases, float* y, int M, int K, int N,
+                           const VerifyArgs& va, hipStream_t s) {
+  const int rsets = (M + 15) / 16;
+  const int workers = wide_workers(rsets);
+  const int GP = (K >> 6) >> 1;
+  if (GP % 5 == 0)
+    return launch_wide<ACT, 5, 1>(x, wq, scales, biases, y, M, K, N, rsets, workers, va, s);
+  if (GP % 4 == 0)
+    return launch_wide<ACT, 4, 1>(x, wq, scales, biases, y, M, K, N, rsets, workers, va, s);
+  if (GP % 2 == 0)
+    return launch_wide<ACT, 2, 4>(x, wq, scales, biases, y, M, K, N, rsets, workers, va, s);
+  return launch_wide<ACT, 1, 8>(x, wq, scales, biases, y, M, K, N, rsets, workers, va, s);
+}
+
 }  // namespace
+
+bool qgemm_wide_fits(int M, int K, int N, int act) {
+  // Whole tiles per wave need many of them: at least two per wave.
+  const int G = K >> 6;
+  const int T = (N + 15) / 16;
+  const int rsets = (M + 15) / 16;
+  return M <= 64 && act != ACT_FP32 && K <= 64 * 8 * 5 && G % 8 == 0 &&
+         (size_t)N * (size_t)(K / 2) < 0x7F000000u && T >= 16 * wide_workers(rsets) &&
+         m16_layout(G, 16, 8, 5).sb + 8 * 16 * G * 4 <= kLdsLimit;
+}
+
+int qgemm_wide_groups(int M) { return wide_workers((M + 15) / 16) * ((M + 15) / 16); }
+
+hipError_t launch_qgemm_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
+                             const uint16_t* biases, float* y, int M, int K, int N, int act,
+                             const VerifyArgs& va, hipStream_t stream) {
+  if (act == ACT_BF16)
+    return launch_wide_any<ACT_BF16>(x, wq, scales, biases, y, M, K, N, va, stream);
+  if (act == ACT_FP16)
+    return launch_wide_any<ACT_FP16>(x, wq, scales, biases, y, M, K, N, va, stream);
+  return hipErrorInvalidValue;
+}
 
 bool qgemm_m16_fits(int M, int K, int act) {
   // One batch of staging (K <= 64 * waves * XB) keeps the padded image small.

@@ -54,6 +54,16 @@ hipError_t launch_qgemm_m16(const void* x, const uint8_t* wq, const uint16_t* sc
                             const uint16_t* biases, float* y, int M, int K, int N, int act,
                             hipStream_t stream);
 
+// Wide outputs (at least two column tiles per wave of one work-group per
+// CU): qgemm_w4_wide (qgemm_m16.hip), waves own whole tiles over all of K.
+// With va.argmax (M <= 8) it is the fused verify's projection, one partial
+// per row and work-group (qgemm_wide_groups(M) work-groups).
+bool qgemm_wide_fits(int M, int K, int N, int act);
+int qgemm_wide_groups(int M);
+hipError_t launch_qgemm_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
+                             const uint16_t* biases, float* y, int M, int K, int N, int act,
+                             const VerifyArgs& va, hipStream_t stream);
+
 // h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:] of y = x . W^T, W the stacked
 // gate/up weight [N, K]. Fused into the 16-row kernel when
 // qgemm_swiglu_fused(); otherwise the projection writes `scratch_y` [M, N]
