@@ -134,8 +134,16 @@ def test_rows_independent_of_M(vqv):
     print(f"row results bit-identical across M=1/4/8: {same}")
 
 
-def test_deterministic_fingerprint(vqv):
-    c = case(8, 2048, 4096, "bf16", seed=12)
+# Shapes that reach each projection kernel: qgemm_w4_m8 (M <= 8), the 16-row
+# kernel (9..64 rows), the whole-tile kernel (vocabulary widths) and the
+# generic kernel (fp32 activations).
+KERNEL_SHAPES = [(8, 2048, 4096, "bf16"), (16, 1024, 3000, "fp16"), (16, 1024, 66000, "bf16"),
+                 (8, 512, 300, "fp32")]
+
+
+@pytest.mark.parametrize("M,K,N,act", KERNEL_SHAPES)
+def test_deterministic_fingerprint(vqv, M, K, N, act):
+    c = case(M, K, N, act, seed=12)
     d = to_device(c)
     hs = set()
     for _ in range(3):
@@ -145,29 +153,44 @@ def test_deterministic_fingerprint(vqv):
     assert len(hs) == 1
 
 
-def test_nonfinite_activation_propagates(vqv):
-    c = case(4, 256, 64, "fp32", seed=13)
-    c["x"][1, 70] = np.nan
-    c["x"][2, 3] = np.inf
+def _set_act(c, m, k, value):
+    """Write one activation (given as a float) in the config's own encoding."""
+    if c["act"] == "fp32":
+        c["x"][m, k] = value
+    elif c["act"] == "fp16":
+        c["x"][m, k] = np.float16(value).view(np.uint16)
+    else:
+        c["x"][m, k] = np.uint16(np.float32(value).view(np.uint32) >> 16)
+
+
+@pytest.mark.parametrize("M,K,N,act", [(4, 256, 64, "fp32"), (4, 256, 64, "bf16"),
+                                       (12, 256, 64, "fp16"), (12, 1024, 66000, "bf16")])
+def test_nonfinite_activation_propagates(vqv, M, K, N, act):
+    c = case(M, K, N, act, seed=13)
+    _set_act(c, 1, 70, np.nan)
+    _set_act(c, 2, 3, np.inf)
     y = run(vqv, c)
     assert np.isnan(y[1]).all()
     assert (~np.isfinite(y[2])).all()
-    ref = qgemm_ref(c["x"], "fp32", c["wq"], c["scales"], c["biases"])
-    assert_close(y[[0, 3]], ref[[0, 3]], "fp32", "finite rows")
+    rows = [r for r in range(M) if r not in (1, 2)]
+    ref = qgemm_ref(c["x"][rows], act, c["wq"], c["scales"], c["biases"])
+    assert_close(y[rows], ref, act, "finite rows")
 
 
-def test_writes_only_its_output(vqv):
+@pytest.mark.parametrize("M,K,N,act", [(5, 256, 70, "bf16"), (13, 256, 70, "fp16"),
+                                       (16, 1024, 66001, "bf16"), (5, 256, 70, "fp32")])
+def test_writes_only_its_output(vqv, M, K, N, act):
     """y is written exactly in [M, N]; guard bytes around it stay untouched."""
-    c = case(5, 256, 70, "bf16", seed=14)
+    c = case(M, K, N, act, seed=14)
     d = to_device(c)
-    buf = torch.full((5 * 70 + 64,), 123.0, dtype=torch.float32, device="cuda")
-    y = buf[32:32 + 5 * 70].view(5, 70)
+    buf = torch.full((M * N + 64,), 123.0, dtype=torch.float32, device="cuda")
+    y = buf[32:32 + M * N].view(M, N)
     vqv.vqv_qgemm(d["x"], d["wq"], d["scales"], d["biases"], y=y)
     torch.cuda.synchronize()
     b = buf.cpu().numpy()
-    assert np.all(b[:32] == 123.0) and np.all(b[32 + 350:] == 123.0)
-    ref = qgemm_ref(c["x"], "bf16", c["wq"], c["scales"], c["biases"])
-    assert_close(y.cpu().numpy(), ref, "bf16", "offset output")
+    assert np.all(b[:32] == 123.0) and np.all(b[32 + M * N:] == 123.0)
+    ref = qgemm_ref(c["x"], act, c["wq"], c["scales"], c["biases"])
+    assert_close(y.cpu().numpy(), ref, act, "offset output")
 
 
 # ---------------------------------------------------------------- full sizes
