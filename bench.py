@@ -44,6 +44,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "verified rows/s + achieved HBM GB/s, W4 M=8 QMM K=5120 N=17408"
 MALL_BYTES = 256 << 20
 COPY_PROBE_BYTES = 1 << 30
+COPY_REF_BYTES = 512 << 20                     # the secondary bandwidth reference
 QMM_LAUNCHES = 240
 
 # workload -> (verify block T, sequences B) for the steps that include verify
@@ -114,10 +115,22 @@ def cpu_baseline(c, M, T, B, budget_s):
         t0 = time.perf_counter()
         verify_ref(lg, d, B, T)
         t_v = time.perf_counter() - t0
+    # One single-threaded pass over a smaller sample, for reference.
+    t_1 = None
+    try:
+        from threadpoolctl import threadpool_limits
+        n1 = max(64, ncols // 8)
+        with threadpool_limits(limits=1, user_api="blas"):
+            t_1 = run(n1) * N / n1
+    except Exception:
+        pass
     return {"value": M / (t_q + t_v), "unit": "rows/s", "cores": threads, "kind": "oracle",
             "sample": f"qgemm over {ncols} of {N} columns (median of 3, scaled to N) + "
                       f"verify over all {B * T} x {N} logits; host cpus {os.cpu_count()}",
-            "seconds_per_step": t_q + t_v}
+            "seconds_per_step": t_q + t_v,
+            "host_cpu_count": os.cpu_count(), "host_affinity": len(os.sched_getaffinity(0)),
+            "blas_threads": threads,
+            "single_thread_qgemm_rows_s": (M / t_1) if t_1 else None}
 
 
 def _counter_rows(run_dir):
@@ -376,6 +389,38 @@ def main():
         g_f.replay()
         f_runs = [timed(g_f) * 1e3 / nq for _ in range(5)]
 
+    # Secondary bandwidth reference: a device copy of 512 MiB each way,
+    # timed the same way (graph of back-to-back copies).
+    csrc = torch.empty(COPY_REF_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    g_c = graph_of(lambda i, st: cdst.copy_(csrc), 4)
+    g_c.replay()
+    copy_gbs = 2 * COPY_REF_BYTES * 4 / (min(timed(g_c) for _ in range(3)) * 1e-3) / 1e9
+    del csrc, cdst, g_c
+
+    # Rows/s against M with the same weights (the first M rows of x): the
+    # plain projection's per-launch time at M = 1 and 4 as well.
+    by_m = {}
+    if args.workload == "target":
+        for m_sub in (1, 4):
+            xs_sub = [cp[0][:m_sub].contiguous() for cp in copies]
+            ys_sub = torch.empty((m_sub, N), dtype=torch.float32, device=dev)
+
+            def qm(i, st, xs_sub=xs_sub, ys_sub=ys_sub):
+                _, wc, sc, bc = copies[i % R]
+                vqv.vqv_qgemm(xs_sub[i % R], wc, sc, bc, y=ys_sub, stream=st)
+            g_m = graph_of(qm, nq)
+            g_m.replay()
+            t_m = statistics.fmean(timed(g_m) * 1e3 / nq for _ in range(3))
+            by_m[m_sub] = {"us_per_launch": t_m, "rows_per_s": m_sub / (t_m * 1e-6)}
+        by_m[M] = {"us_per_launch": q_mean, "rows_per_s": M / (q_mean * 1e-6)}
+
+    props = torch.cuda.get_device_properties(dev)
+    device = {"name": props.name, "cus": props.multi_processor_count,
+              "arch": getattr(props, "gcnArchName", None),
+              "memory_gib": round(props.total_memory / 2 ** 30, 1),
+              "hip": torch.version.hip, "torch": torch.__version__}
+
     qb = qgemm_bytes(M, K, N, esz)
     # The dominant kernel is the projection. Its launches are timed in a graph
     # of their own (the fused step's instance adds only the per-group argmax
@@ -425,8 +470,11 @@ def main():
         "swiglu_us_mean": statistics.fmean(s_runs) if s_runs else None,
         "step_path": "fused" if use_fused else ("swiglu" if use_swiglu else "separate"),
         "step_hbm_gbs": (qb + (4 * M * N if T and not use_fused else 0)) / (ms_step * 1e-3) / 1e9,
+        "device": device,
+        "copy_probe_gbs": copy_gbs,
+        "qgemm_by_M": by_m or None,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
+                     "frac": achieved / HBM_PEAK_GBS, "frac_of_copy_probe": achieved / copy_gbs,
                      "traffic": None if use_swiglu else traffic_record(args.workload, M),
                      "kernel": kname, "bytes_per_launch": qb, "us_per_launch": k_us},
         "cpu_baseline": None,
