@@ -834,16 +834,28 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
   // output idx is row (idx >> 4) & 7, and NT is a multiple of 128, so that row
   // is fixed per thread, (tid >> 4) & 7.
   __syncthreads();
+  // Every wave's slot is read unconditionally (a run's first or last tile
+  // slot, whichever is nearer) and the covering runs are selected afterwards,
+  // so the reads of one output go out together instead of one after another.
+  int tb[NW], te[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    tb[w] = run_tiles[2 * w];
+    te[w] = run_tiles[2 * w + 1];
+  }
   Top2 best = top2_none();
   for (int idx = tid; idx < tiles * 128; idx += NT) {
     const int t = idx >> 7;
     const int within = idx & 127;                     // row * 16 + column
-    float s = 0.0f;
+    float v[NW];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const int tb = run_tiles[2 * w], te = run_tiles[2 * w + 1];
-      if (t >= tb && t <= te) s += red[((w * 2 + (t - tb)) * 128) + within];
+      const int seg = min(max(t - tb[w], 0), 1);
+      v[w] = red[((w * 2 + seg) * 128) + within];
     }
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s = (t >= tb[w] && t <= te[w]) ? s + v[w] : s;
     const int m = within >> 4;
     const int c = t * 16 + (within & 15);
     if (m < M && c < wgcols) {

@@ -113,7 +113,7 @@ __device__ __forceinline__ void pair_step(const u32x4 (&A)[4], const u32x4& w,
   }
 }
 
-template <int ACT, int NW, int TW, int DB, int RB, int D0, int XB, bool SWIGLU>
+template <int ACT, int NW, int TW, int DB, int RB, int D0, int XB, bool SWIGLU, bool SBV>
 __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
@@ -202,8 +202,11 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
       xsl[g * 16 + mm + 8 * r] = s8;
     }
   };
-  const bool sb_vec = (G % 8) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
-                                        reinterpret_cast<uintptr_t>(biases)) & 15) == 0;
+  // SBV (host): K/64 a multiple of 8 and 16-byte aligned scale and bias
+  // arrays, so the table moves in 16-byte units. A template flag rather than
+  // a runtime branch: loads on either side of a branch make the compiler wait
+  // for every load in flight, the staging loads included.
+  constexpr bool sb_vec = SBV;
   const unsigned g_recip = 0xFFFFFFFFu / (unsigned)G + 1u;
   auto div_g = [&](unsigned e) { return G == 1 ? e : __umulhi(e, g_recip); };
   const unsigned char* abase = xl + (h * 16 + j) * kSlot16;
@@ -218,10 +221,15 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
   const unsigned woff = (unsigned)rel_row(j) * rowbytes + 16u * h;
   constexpr unsigned kTileRows = SWIGLU ? 8u : 16u;
 
-  for (int bb = 0; bb < rounds; bb += XB) {
-    x_load(bb);
+  // The activation loads go out now (one batch: K <= 64*NW*XB, host). With a
+  // one-block ring (RB == 1) they are staged inside the first column group,
+  // once that group's table and ring are in flight too, so the weight stream
+  // starts while the staging waits; deeper rings stage here (registers).
+  constexpr bool kLateStaging = RB == 1;
+  x_load(0);
+  if constexpr (!kLateStaging) {
 #pragma unroll
-    for (int i = 0; i < XB; ++i) x_store_round(bb, i);
+    for (int i = 0; i < XB; ++i) x_store_round(0, i);
   }
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -259,7 +267,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
 #pragma unroll
       for (int u = 0; u < SBU; ++u) {
         const int i = (round * SBU + u) * NT + tid;
-        if (sb_vec) {
+        if constexpr (sb_vec) {
           const unsigned e0 = 8u * (unsigned)i;
           const unsigned n = div_g(e0), g = e0 - n * (unsigned)G;
           const unsigned off =
@@ -280,7 +288,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
       for (int u = 0; u < SBU; ++u) {
         const int i = (round * SBU + u) * NT + tid;
         const bool ok = i < sb_units;
-        if (sb_vec) {
+        if constexpr (sb_vec) {
           const unsigned e0 = 8u * (unsigned)i;
           const unsigned n = div_g(e0), g = e0 - n * (unsigned)G;
           u32x4 lo, hi;                               // (s_g | b_g << 16) for g .. g+7
@@ -330,7 +338,22 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
     Blk kl = kfirst;
     sb_load(0);
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
+    for (int d = 0; d < D0; ++d) {
+      load(codes_at(kl), d % DB, st[d]);
+      if (d % DB == DB - 1) kl = next(kl);
+    }
+    asm volatile("" ::: "memory");                   // the loads above go out first
+    if (kLateStaging && cg == wk) {                   // uniform: the first group stages
+      // The empty asm keeps the staging arithmetic here, after the loads
+      // above: hoisted out of the loop it would wait for the activations first.
+#pragma unroll
+      for (int i = 0; i < XB; ++i) {
+        asm volatile("" : "+v"(xv[i][0]), "+v"(xv[i][1]));
+        x_store_round(0, i);
+      }
+    }
+#pragma unroll
+    for (int d = D0; d < D; ++d) {
       load(codes_at(kl), d % DB, st[d]);
       if (d % DB == DB - 1) kl = next(kl);
     }
@@ -446,13 +469,24 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
     // ---- reduce: each output tile adds the flushed partials of the runs
     // that cover it, in wave order; SWIGLU takes the (gate, up) column pairs.
     __syncthreads();
+    // All waves' slots are read unconditionally (nearest valid slot) and the
+    // covering runs selected afterwards: the reads go out together.
+    int tb[NW], te[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      tb[w] = run_tiles[2 * w];
+      te[w] = run_tiles[2 * w + 1];
+    }
     auto tile_sum = [&](int t, int within) {
-      float sum = 0.0f;
+      float v[NW];
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const int tb = run_tiles[2 * w], te = run_tiles[2 * w + 1];
-        if (t >= tb && t <= te) sum += red[((w * 2 + (t - tb)) * 256) + within];
+        const int seg = min(max(t - tb[w], 0), 1);
+        v[w] = red[((w * 2 + seg) * 256) + within];
       }
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum = (t >= tb[w] && t <= te[w]) ? sum + v[w] : sum;
       return sum;
     };
     if constexpr (SWIGLU) {
@@ -826,7 +860,12 @@ hipError_t launch_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
   if (workers < 8) workers = 8;
   if (rsets == 1 && workers > groups) workers = groups;
   const M16Layout L = m16_layout(K >> 6, 16 * kM16Tiles, kM16Waves, kM16XB);
-  auto kern = qgemm_w4_m16<ACT, kM16Waves, kM16Tiles, DB, RB, 2, kM16XB, SWIGLU>;
+  constexpr int D0 = DB;                                // one block ahead of the staging
+  const bool sbv = ((K >> 6) % 8) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(biases)) &
+                    15) == 0;
+  auto kern = sbv ? qgemm_w4_m16<ACT, kM16Waves, kM16Tiles, DB, RB, D0, kM16XB, SWIGLU, true>
+                  : qgemm_w4_m16<ACT, kM16Waves, kM16Tiles, DB, RB, D0, kM16XB, SWIGLU, false>;
   if (L.total > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
