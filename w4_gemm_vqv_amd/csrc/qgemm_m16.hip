@@ -13,12 +13,11 @@
 // activation row i. Lane (column j = lane%16, k slot h = lane/16) of B loads
 // the 16 contiguous bytes [16h, 16h+16) of its column's 64-byte group pair
 // (one 16-byte load per lane: full 64-byte runs of each weight row, which the
-// memory system streams much faster than 32-byte pieces), so lanes h < 2
-// hold group 2p and lanes h >= 2 group 2p+1. Each of the four code dwords t
-// feeds two MFMAs against the same A operand: one sees the codes of the
-// h < 2 lanes and exact zeros elsewhere (group 2p), the other the h >= 2
-// lanes (group 2p+1). Each result therefore sums within one group, and its
-// group epilogue applies that group's scale and bias:
+// memory system streams much faster than 32-byte pieces). Two lane-half swaps
+// (split_groups) then give each lane 8 bytes of group 2p in dwords 0-1 and
+// the same 8 bytes of group 2p+1 in dwords 2-3, so MFMAs 0-1 sum within group
+// 2p, MFMAs 2-3 within 2p+1, and each group epilogue applies that group's
+// scale and bias:
 //     y += s*acc' + (b - c0*s)*xs,  acc' = sum x*(c0+q),  xs = sum x.
 // The per-step work, the exact unpack and the weight ring follow
 // qgemm_w4_m8; the activation image holds 16 rows per group pair.
@@ -78,39 +77,34 @@ __host__ __device__ inline M16Layout m16_layout(int G, int WGC, int NW, int XB) 
 // silu(g) * u in fp32 with the library's exp and an IEEE division.
 __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
-// Per-lane masks of the two-group step: a lane's 16 code bytes belong to
-// group 2p (k slot h < 2) or 2p+1 (h >= 2); each group's MFMAs see the codes
-// of its own lanes and exact zeros elsewhere.
-struct UnpackMasks {
-  unsigned lo0, mg0, lo1, mg1;
-};
-__device__ __forceinline__ UnpackMasks unpack_masks(int h, unsigned magic) {
-  const bool g0 = h < 2;
-  return UnpackMasks{g0 ? 0x000F000Fu : 0u, g0 ? magic : 0u, g0 ? 0u : 0x000F000Fu,
-                     g0 ? 0u : magic};
+// Lane (j, h) loads bytes [16h, 16h+16) of its column's 64-byte group pair:
+// group 2p for h < 2, group 2p+1 for h >= 2. Two swaps between the lane
+// halves (lane L < 32 with lane L + 32) leave every lane 8 bytes of each
+// group: dwords 0-1 hold bytes [8s, 8s+8) of group 2p and dwords 2-3 the same
+// bytes of group 2p+1, with s = sigma(h) = (0, 2, 1, 3)[h] (h's two bits
+// swapped), so that MFMAs 0-1 sum within group 2p and MFMAs 2-3 within 2p+1.
+__device__ __forceinline__ int sigma_slot(int h) { return ((h & 1) << 1) | (h >> 1); }
+
+__device__ __forceinline__ u32x4 split_groups(const u32x4& w) {
+  const auto a = __builtin_amdgcn_permlane32_swap(w.x, w.z, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(w.y, w.w, false, false);
+  return u32x4{a[0], b[0], a[1], b[1]};
 }
 
-// unpack_codes with a lane mask: (c0 + q) pairs, or zeros when lo = mg = 0.
-__device__ __forceinline__ u32x4 unpack_codes_masked(unsigned d, unsigned lo, unsigned mg) {
-  u32x4 q;
-  q.x = (d & lo) | mg;
-  q.y = ((d >> 4) & lo) | mg;
-  q.z = ((d >> 8) & lo) | mg;
-  q.w = ((d >> 12) & lo) | mg;
-  return q;
-}
-
-// One group pair for 16 rows: A[t] holds x[row][32h + 8t ..] of the pair (all
-// 16 rows real) and w the lane's 16 code bytes, [16h, 16h + 16) of its
-// column's pair. C0 collects group 2p, C1 group 2p+1, each over its 64 k.
+// One group pair for 16 rows: A[t] holds the activations whose codes sit in
+// dword t after split_groups (all 16 rows real). C0 collects group 2p, C1
+// group 2p+1.
 template <bool F16>
-__device__ __forceinline__ void pair_step(const u32x4 (&A)[4], const u32x4& w,
-                                          const UnpackMasks& um, f32x4& C0, f32x4& C1) {
+__device__ __forceinline__ void pair_step(const u32x4 (&A)[4], const u32x4& w, unsigned magic,
+                                          f32x4& C0, f32x4& C1) {
+  const u32x4 v = split_groups(w);
+  u32x4 bq[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    C0 = mfma16x16x32<F16>(A[t], unpack_codes_masked(w[t], um.lo0, um.mg0), C0);
-    C1 = mfma16x16x32<F16>(A[t], unpack_codes_masked(w[t], um.lo1, um.mg1), C1);
-  }
+  for (int t = 0; t < 4; ++t) bq[t] = unpack_codes(v[t], magic);
+  C0 = mfma16x16x32<F16>(A[0], bq[0], C0);
+  C1 = mfma16x16x32<F16>(A[2], bq[2], C1);
+  C0 = mfma16x16x32<F16>(A[1], bq[1], C0);
+  C1 = mfma16x16x32<F16>(A[3], bq[3], C1);
 }
 
 template <int ACT, int NW, int TW, int DB, int RB, int D0, int XB, bool SWIGLU, bool SBV>
@@ -164,7 +158,6 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
 
   unsigned magic;
   asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(TR::magic));
-  const UnpackMasks um = unpack_masks(h, magic);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(x), (short)0, M * K * 2, kBufferFlags);
 
@@ -189,15 +182,15 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
       }
     }
   };
-  // Values k = 8e8.. of group g sit at offset 64(g&1) + 8e8 = 32h + 8t of the
-  // pair: k slot h = 2(g&1) + e8/4 of MFMA t = e8%4.
-  const unsigned xl_lane = (e8 & 3) * kTRow16 + ((e8 >> 2) * 16 + mm) * kSlot16;
+  // Values k = 8e8.. of group g feed MFMA t = 2(g&1) + e8%2 in the k slot h
+  // whose lanes hold those codes after split_groups: sigma(h) = e8/2.
+  const unsigned xl_lane = (e8 & 1) * kTRow16 + (sigma_slot(e8 >> 1) * 16 + mm) * kSlot16;
   auto x_store_round = [&](int bb, int i) {
     const int g = wave + NW * (bb + i);               // uniform
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const float s8 = sum8_lanes(block_sum<ACT>(xv[i][r]));
-      *reinterpret_cast<u32x4*>(xl + (g >> 1) * kPair16 + (g & 1) * 32 * kSlot16 + xl_lane +
+      *reinterpret_cast<u32x4*>(xl + (g >> 1) * kPair16 + (g & 1) * 2 * kTRow16 + xl_lane +
                                 r * 8 * kSlot16) = permute_pairs(xv[i][r]);
       xsl[g * 16 + mm + 8 * r] = s8;
     }
@@ -433,7 +426,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
 #pragma unroll
       for (int d = 0; d < DB; ++d) {
         f32x4 C0 = zero4, C1 = zero4;
-        pair_step<TR::f16>(cur.A, st[r * DB + d], um, C0, C1);
+        pair_step<TR::f16>(cur.A, st[r * DB + d], magic, C0, C1);
         Ops nxt;
         if (d + 1 < DB) fetch(bc, d + 1, nxt);
         else fetch(bn, 0, nxt);
@@ -574,7 +567,6 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
 
   unsigned magic;
   asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(TR::magic));
-  const UnpackMasks um = unpack_masks(h, magic);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(x), (short)0, M * K * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
@@ -670,14 +662,14 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
     if (d % DB == DB - 1) kl = next(kl);
   }
   (void)rounds;
-  const unsigned xl_lane = (e8 & 3) * kTRow16 + ((e8 >> 2) * 16 + mm) * kSlot16;
+  const unsigned xl_lane = (e8 & 1) * kTRow16 + (sigma_slot(e8 >> 1) * 16 + mm) * kSlot16;
 #pragma unroll
   for (int i = 0; i < XB; ++i) {
     const int g = wave + NW * i;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const float s8 = sum8_lanes(block_sum<ACT>(xv[i][r]));
-      *reinterpret_cast<u32x4*>(xl + (g >> 1) * kPair16 + (g & 1) * 32 * kSlot16 + xl_lane +
+      *reinterpret_cast<u32x4*>(xl + (g >> 1) * kPair16 + (g & 1) * 2 * kTRow16 + xl_lane +
                                 r * 8 * kSlot16) = permute_pairs(xv[i][r]);
       xsl[g * 16 + mm + 8 * r] = s8;
     }
@@ -766,7 +758,7 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
       f32x4 C0 = zero4, C1 = zero4;
-      pair_step<TR::f16>(cur.A, st[r * DB + d], um, C0, C1);
+      pair_step<TR::f16>(cur.A, st[r * DB + d], magic, C0, C1);
       Ops nxt;
       if (d + 1 < DB) {
         fetch(bc, d + 1, nxt);
