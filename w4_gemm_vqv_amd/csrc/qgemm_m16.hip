@@ -162,9 +162,8 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
       const_cast<void*>(x), (short)0, M * K * 2, kBufferFlags);
 
   // ---- activation staging, once per work-group: lane (e8, mm) moves
-  // x[mm + 8r, 64g + 8e8 .. +8].
-  const int ngrp = 2 * GP;
-  const int rounds = (ngrp + NW - 1) / NW;
+  // x[mm + 8r, 64g + 8e8 .. +8]; one batch of XB rounds covers the 2*GP
+  // groups (host: K <= 64 * NW * XB).
   const int e8 = lane & 7;
   const int mm = lane >> 3;
   u32x4 xv[XB][2];
