@@ -60,6 +60,10 @@ SHAPES = [
     # tiles (one row set, a ragged last tile, three and four row sets).
     (8, 512, 70000), (16, 1024, 66000), (12, 2560, 66001), (48, 512, 30000), (64, 1536, 25000),
     (3, 2560, 66001),
+    # 17..64 rows at vocabulary widths, every row set on one weight stream:
+    # two, three and four row sets, K in whole and partial chunks of 5 pairs,
+    # ragged last tile and row set.
+    (64, 2560, 70000), (40, 1280, 40001), (17, 768, 33000), (33, 384, 36000),
 ]
 
 
@@ -135,10 +139,11 @@ def test_rows_independent_of_M(vqv):
 
 
 # Shapes that reach each projection kernel: qgemm_w4_m8 (M <= 8), the 16-row
-# kernel (9..64 rows), the whole-tile kernel (vocabulary widths) and the
-# generic kernel (fp32 activations).
+# kernel (9..64 rows), the whole-tile kernel (vocabulary widths), the
+# all-row-sets kernel (17..64 rows at vocabulary widths) and the generic
+# kernel (fp32 activations).
 KERNEL_SHAPES = [(8, 2048, 4096, "bf16"), (16, 1024, 3000, "fp16"), (16, 1024, 66000, "bf16"),
-                 (8, 512, 300, "fp32")]
+                 (64, 1280, 40000, "bf16"), (8, 512, 300, "fp32")]
 
 
 @pytest.mark.parametrize("M,K,N,act", KERNEL_SHAPES)

@@ -986,6 +986,10 @@ template <int ACT>
 hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                          const uint16_t* biases, float* y, int M, int K, int N,
                          hipStream_t s) {
+  if constexpr (ACT != ACT_FP32) if (qgemm_rows_fits(M, K, N, ACT)) {
+    // 17..64 rows at vocabulary widths: all row sets on one weight stream.
+    return launch_qgemm_rows(x, wq, scales, biases, y, M, K, N, ACT, s);
+  }
   if (qgemm_wide_fits(M, K, N, ACT)) {
     // Vocabulary widths: whole-tile waves (the fused verify's projection
     // takes the same kernel, so the two paths agree bit for bit).

@@ -904,6 +904,245 @@ hipError_t launch_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Wide outputs with 17..64 rows: every row set on one weight stream.
+// qgemm_w4_wide gives each row set work-groups of their own, so each weight
+// byte is unpacked once per row set and crosses the CU-L2 link once per row
+// set. Here one work-group per CU owns a contiguous range of column tiles for
+// all RS row sets, and K is cut into chunks of KCP group pairs: the chunk's
+// activations of all rows (RS images per pair, the 16-row layout above) and
+// the waves' (s, b) tables are staged, then each wave runs its tiles over
+// the chunk's pairs with one unpack per code and RS x 4 MFMAs per step,
+// accumulating in registers across chunks (KT tiles x RS row sets).
+// * Step order: pair-major within a chunk (pair p of tiles 0..KT-1, then
+//   pair p+1). Each step unpacks one tile's codes once for all row sets; the
+//   first RH row sets' A operands are read once per pair and held, the other
+//   row sets' operands and the row sums are read per step (registers).
+// * Weight ring: slot k holds tile k's next pair (D = KT), and runs on across
+//   chunk boundaries, so the next chunk's first weights are in flight during
+//   its staging. Steps past a wave's tiles or past K read zeros.
+// * The work-group's tiles: [tbeg, tbeg + tpw); wave w takes tbeg + w + 8k.
+// Every sum runs in a fixed order, so results are deterministic.
+template <int ACT, int RS, int KT, int KCP>
+__global__ __launch_bounds__(512) void qgemm_w4_rows(
+    const void* __restrict__ x, const uint8_t* __restrict__ wq,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
+    float* __restrict__ y, int M, int K, int N, int tpw) {
+  using TR = ActTraits<ACT>;
+  static_assert(TR::parts == 1, "16-bit activations only");
+  constexpr int NW = 8;
+  constexpr int RH = RS >= 4 ? 1 : (RS < 2 ? RS : 2);  // row sets whose A stays in registers
+  constexpr int GC = 2 * KCP;                        // groups per chunk
+  constexpr int ITEMS = GC * 2 * RS;                 // (group, row octet) staging items
+  constexpr int XR = (ITEMS + NW - 1) / NW;          // staging loads per lane
+  constexpr int TABD = KT * 16 * KCP;                // table dwords per array and wave
+  constexpr int TABL = (TABD + 63) / 64;             // table loads per array and lane
+  constexpr unsigned kSkip = 0x7FF00000u;
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  unsigned char* ximg = lds;                                        // [KCP][RS] images
+  float* xsl = reinterpret_cast<float*>(lds + KCP * RS * kPair16);  // [KCP][RS][2][16]
+  unsigned* tab_all = reinterpret_cast<unsigned*>(lds + KCP * RS * (kPair16 + 128));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15;
+  const int h = lane >> 4;
+  const int G = K >> 6;                              // even (host)
+  const int GP = G >> 1;
+  const int nch = (GP + KCP - 1) / KCP;
+  const unsigned rowbytes = (unsigned)K >> 1;
+  const int T = (N + 15) >> 4;
+  const int tbeg = blockIdx.x * tpw;
+  const int tend = min(T, tbeg + tpw);
+  unsigned* tab = tab_all + wave * KT * 16 * GC;     // [KT][16 columns][GC] of (s | b << 16)
+
+  unsigned magic;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(TR::magic));
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(x), (short)0, M * K * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(wq), (short)0, (unsigned)N * rowbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(scales), (short)0, (unsigned)N * G * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(biases), (short)0, (unsigned)N * G * 2, kBufferFlags);
+
+  // This wave's tiles (uniform): tile k is tbeg + wave + 8k while below tend.
+  int tile[KT];
+  bool tin[KT];
+#pragma unroll
+  for (int k = 0; k < KT; ++k) {
+    tile[k] = tbeg + wave + NW * k;
+    tin[k] = tile[k] < tend;
+  }
+  const unsigned woff = (unsigned)j * rowbytes + 16u * h;
+  auto codes_at = [&](int c, int p, int k) {        // step (chunk, pair, tile)
+    const int pg = c * KCP + p;
+    return tin[k] && c < nch && pg < GP
+               ? (unsigned)tile[k] * 16u * rowbytes + 64u * (unsigned)pg
+               : kSkip;
+  };
+  u32x4 ring[KT];
+#pragma unroll
+  for (int k = 0; k < KT; ++k)
+    ring[k] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, codes_at(0, 0, k), 0);
+
+  f32x4 acc[KT][RS];
+#pragma unroll
+  for (int k = 0; k < KT; ++k)
+#pragma unroll
+    for (int r = 0; r < RS; ++r) acc[k][r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int e8 = lane & 7;
+  const int mm = lane >> 3;
+  const unsigned xl_lane = (e8 & 1) * kTRow16 + (sigma_slot(e8 >> 1) * 16 + mm) * kSlot16;
+
+  for (int c = 0; c < nch; ++c) {
+    if (c > 0) __syncthreads();                      // chunk c-1's image and tables are read
+    // ---- activations of all rows for groups c*GC .. c*GC + GC-1, and this
+    // wave's table; items (group gl, row octet ro) are dealt to the waves.
+    u32x4 xv[XR];
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      const int it = wave + NW * i;
+      const int gl = it / (2 * RS), ro = it % (2 * RS);
+      const int row = 8 * ro + mm;
+      const int kk = 64 * (c * GC + gl) + 8 * e8;
+      const bool ok = it < ITEMS && row < M && kk < K;
+      xv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          xr, ok ? (unsigned)((row * K + kk) * 2) : kOutOfRange, 0, 0);
+    }
+    unsigned ts[TABL], tb[TABL];
+#pragma unroll
+    for (int n = 0; n < TABL; ++n) {
+      const int e = 64 * n + lane;
+      const int k = e / (16 * KCP), jj = (e / KCP) % 16, d = e % KCP;
+      const int col = (tbeg + wave + NW * k) * 16 + jj;
+      const bool ok = e < TABD && tbeg + wave + NW * k < tend && col < N && c * KCP + d < GP;
+      const unsigned off = ok ? 2u * ((unsigned)col * (unsigned)G + (unsigned)(c * GC + 2 * d))
+                              : kOutOfRange;
+      ts[n] = __builtin_amdgcn_raw_buffer_load_b32(sr, off, 0, 0);
+      tb[n] = __builtin_amdgcn_raw_buffer_load_b32(br, off, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      const int it = wave + NW * i;
+      if (it >= ITEMS) continue;                     // uniform: the last round is partial
+      const int gl = it / (2 * RS), ro = it % (2 * RS);
+      const int r = ro >> 1, r8 = ro & 1;
+      const float s8 = sum8_lanes(block_sum<ACT>(xv[i]));
+      *reinterpret_cast<u32x4*>(ximg + ((gl >> 1) * RS + r) * kPair16 + (gl & 1) * 2 * kTRow16 +
+                                xl_lane + r8 * 8 * kSlot16) = permute_pairs(xv[i]);
+      xsl[((gl >> 1) * RS + r) * 32 + (gl & 1) * 16 + mm + 8 * r8] = s8;
+    }
+#pragma unroll
+    for (int n = 0; n < TABL; ++n) {
+      const int e = 64 * n + lane;
+      if (e < TABD) {
+        const int k = e / (16 * KCP), jj = (e / KCP) % 16, d = e % KCP;
+        unsigned* q = tab + (k * 16 + jj) * GC + 2 * d;
+        q[0] = __builtin_amdgcn_perm(tb[n], ts[n], 0x05040100u);
+        q[1] = __builtin_amdgcn_perm(tb[n], ts[n], 0x07060302u);
+      }
+    }
+    __syncthreads();
+
+    // ---- the chunk's steps, pair-major: (pair p, tile k) for k = 0..KT-1.
+#pragma unroll
+    for (int p = 0; p < KCP; ++p) {
+      // The first RH row sets' A operands stay in registers for the pair's
+      // KT steps; the others' and all row sums are read per step.
+      const unsigned a_lane = (unsigned)(h * 16 + j) * kSlot16;
+      auto a_of = [&](int r, int t, unsigned base) {
+        return *reinterpret_cast<const u32x4*>(ximg + base + (p * RS + r) * kPair16 + t * kTRow16);
+      };
+      u32x4 A[RH][4];
+#pragma unroll
+      for (int r = 0; r < RH; ++r)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) A[r][t] = a_of(r, t, a_lane);
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        // Per-step LDS offsets behind an empty asm: the per-step reads below
+        // must not be hoisted out of the tile loop (registers).
+        unsigned a_step = a_lane, x_step = 4u * (unsigned)h;
+        asm volatile("" : "+v"(a_step), "+v"(x_step));
+        const u32x4 w = ring[k];
+        ring[k] = __builtin_amdgcn_raw_buffer_load_b128(
+            wr, woff, p + 1 < KCP ? codes_at(c, p + 1, k) : codes_at(c + 1, 0, k), 0);
+        const u32x4 v = split_groups(w);
+        u32x4 bq[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bq[t] = unpack_codes(v[t], magic);
+        const u32x2 sb = *reinterpret_cast<const u32x2*>(tab + (k * 16 + j) * GC + 2 * p);
+        const float s0 = half_lo(sb.x), s1 = half_lo(sb.y);
+        const float c0 = fmaf(-TR::c0, s0, half_hi(sb.x));
+        const float c1 = fmaf(-TR::c0, s1, half_hi(sb.y));
+#pragma unroll
+        for (int r = 0; r < RS; ++r) {
+          const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+          u32x4 Ar[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) Ar[t] = r < RH ? A[r < RH ? r : 0][t] : a_of(r, t, a_step);
+          f32x4 C0 = mfma16x16x32<TR::f16>(Ar[0], bq[0], zero4);
+          f32x4 C1 = mfma16x16x32<TR::f16>(Ar[2], bq[2], zero4);
+          C0 = mfma16x16x32<TR::f16>(Ar[1], bq[1], C0);
+          C1 = mfma16x16x32<TR::f16>(Ar[3], bq[3], C1);
+          const float* xs = xsl + (p * RS + r) * 32 + x_step;
+          const f32x4 xs0 = *reinterpret_cast<const f32x4*>(xs);
+          const f32x4 xs1 = *reinterpret_cast<const f32x4*>(xs + 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[k][r][e] = fmaf(s0, C0[e], fmaf(c0, xs0[e], acc[k][r][e]));
+            acc[k][r][e] = fmaf(s1, C1[e], fmaf(c1, xs1[e], acc[k][r][e]));
+          }
+        }
+      }
+    }
+  }
+
+  // ---- results: lane (j, h) holds rows 4h .. 4h+3 of column j of each row set.
+#pragma unroll
+  for (int k = 0; k < KT; ++k) {
+    const int col = tile[k] * 16 + j;
+    if (!tin[k] || col >= N) continue;
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * r + 4 * h + e;
+        if (m < M) y[(size_t)m * N + col] = acc[k][r][e];
+      }
+  }
+}
+
+template <int RS, int KT, int KCP>
+constexpr int rows_lds_bytes() {
+  return KCP * RS * (kPair16 + 128) + 8 * KT * 16 * 2 * KCP * 4;
+}
+
+constexpr int kRowsKT = 5;
+constexpr int kRowsKCP = 5;
+
+template <int ACT, int RS>
+hipError_t launch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
+                       const uint16_t* biases, float* y, int M, int K, int N, hipStream_t stream) {
+  constexpr int lds_bytes = rows_lds_bytes<RS, kRowsKT, kRowsKCP>();
+  auto kern = qgemm_w4_rows<ACT, RS, kRowsKT, kRowsKCP>;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  if (e != hipSuccess) return e;
+  const int cus = device_cus();
+  const int T = (N + 15) / 16;
+  const int tpw = (T + cus - 1) / cus;
+  const int groups = (T + tpw - 1) / tpw;
+  hipLaunchKernelGGL(kern, dim3(groups), dim3(512), lds_bytes, stream, x, wq, scales, biases, y,
+                     M, K, N, tpw);
+  return hipGetLastError();
+}
+
 // Workers per row set: one work-group per CU (a multiple of 8 with several
 // row sets, for the XCD layout).
 int wide_workers(int rsets) {
@@ -929,6 +1168,34 @@ hipError_t launch_wide_any(const void* x, const uint8_t* wq, const uint16_t* sca
 }
 
 }  // namespace
+
+bool qgemm_rows_fits(int M, int K, int N, int act) {
+  // 17..64 rows of 16-bit activations, whole group pairs, 32-bit offsets,
+  // and at most kRowsKT tiles per wave with every wave busy.
+  if (M <= 16 || M > 64 || act == ACT_FP32 || K % 128 != 0) return false;
+  if ((size_t)N * (size_t)(K / 2) >= 0x7F000000u) return false;
+  const int cus = device_cus();
+  const long long T = (N + 15) / 16;
+  const long long tpw = (T + cus - 1) / cus;
+  return tpw >= 8 && tpw <= 8 * kRowsKT;
+}
+
+hipError_t launch_qgemm_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
+                             const uint16_t* biases, float* y, int M, int K, int N, int act,
+                             hipStream_t stream) {
+  const int rs = (M + 15) / 16;
+  if (act == ACT_BF16) {
+    if (rs == 2) return launch_rows<ACT_BF16, 2>(x, wq, scales, biases, y, M, K, N, stream);
+    if (rs == 3) return launch_rows<ACT_BF16, 3>(x, wq, scales, biases, y, M, K, N, stream);
+    return launch_rows<ACT_BF16, 4>(x, wq, scales, biases, y, M, K, N, stream);
+  }
+  if (act == ACT_FP16) {
+    if (rs == 2) return launch_rows<ACT_FP16, 2>(x, wq, scales, biases, y, M, K, N, stream);
+    if (rs == 3) return launch_rows<ACT_FP16, 3>(x, wq, scales, biases, y, M, K, N, stream);
+    return launch_rows<ACT_FP16, 4>(x, wq, scales, biases, y, M, K, N, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 bool qgemm_wide_fits(int M, int K, int N, int act) {
   // Whole tiles per wave need many of them: at least two per wave.

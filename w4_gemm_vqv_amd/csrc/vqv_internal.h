@@ -58,6 +58,12 @@ hipError_t launch_qgemm_m16(const void* x, const uint8_t* wq, const uint16_t* sc
 // CU): qgemm_w4_wide (qgemm_m16.hip), waves own whole tiles over all of K.
 // With va.argmax (M <= 8) it is the fused verify's projection, one partial
 // per row and work-group (qgemm_wide_groups(M) work-groups).
+// 17..64 rows at vocabulary widths: one weight stream for every row set
+// (qgemm_w4_rows, qgemm_m16.hip).
+bool qgemm_rows_fits(int M, int K, int N, int act);
+hipError_t launch_qgemm_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
+                             const uint16_t* biases, float* y, int M, int K, int N, int act,
+                             hipStream_t stream);
 bool qgemm_wide_fits(int M, int K, int N, int act);
 int qgemm_wide_groups(int M);
 hipError_t launch_qgemm_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
