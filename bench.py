@@ -62,6 +62,26 @@ def qgemm_bytes(M, K, N, esz):
 KERNEL_SOURCES = ("qgemm.hip", "qgemm_common.h", "qgemm_m16.hip")
 
 
+def projection_kernel(M, K, N, act, cus):
+    """Name of the projection kernel the library launches for this shape (the
+    order of the library's dispatch; a label for the bench line only)."""
+    G, T = K // 64, (N + 15) // 16
+    rsets = (M + 15) // 16
+    if act == "fp32":
+        return "qgemm_w4"
+    tpw = (T + cus - 1) // cus
+    if 16 < M <= 64 and K % 128 == 0 and N * (K // 2) < 0x7F000000 and 8 <= tpw <= 40:
+        return "qgemm_w4_rows"
+    workers = max(8, (cus // rsets) // 8 * 8) if rsets > 1 else cus
+    if M <= 64 and K <= 2560 and G % 8 == 0 and N * (K // 2) < 0x7F000000 and T >= 16 * workers:
+        return "qgemm_w4_wide"
+    if M <= 8 and K <= 5120:
+        return "qgemm_w4_m8"
+    if M <= 64 and K <= 2560:
+        return "qgemm_w4_m16"
+    return "qgemm_w4"
+
+
 def kernel_sha():
     """sha256 over the projection kernels' sources, in a fixed order."""
     h = hashlib.sha256()
@@ -427,14 +447,7 @@ def main():
     # epilogue, 8 bytes per row and work-group, and is timed with the finish
     # kernel in fused_us_mean).
     k_us = q_mean
-    if act == "fp32":
-        kname = "qgemm_w4"
-    elif M <= 8:
-        kname = "qgemm_w4_m8"
-    elif M <= 16 and K <= 2560:
-        kname = "qgemm_w4_m16"
-    else:
-        kname = "qgemm_w4"
+    kname = projection_kernel(M, K, N, act, props.multi_processor_count)
     if use_swiglu:
         # The step's kernel is the projection with the SwiGLU epilogue: it
         # writes h [M, N/2] instead of y [M, N].
