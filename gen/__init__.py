@@ -23,8 +23,9 @@ Array conventions (all numpy, C-contiguous):
 
 * ``wq``      uint8  [N, K/2]  packed 4-bit codes; byte j of row n holds
                                k=2j in bits 0-3 and k=2j+1 in bits 4-7.
-* ``scales``  uint16 [N, K/64] IEEE fp16 bit patterns.
-* ``biases``  uint16 [N, K/64] IEEE fp16 bit patterns.
+* ``scales``  uint16 [N, K/group] IEEE fp16 bit patterns (group 64 unless
+                               asked for 128).
+* ``biases``  uint16 [N, K/group] IEEE fp16 bit patterns.
 * ``x``       uint16 [M, K] bf16 or fp16 bit patterns, or float32 [M, K].
 * ``draft``   int32  [B, T-1].
 """
@@ -93,17 +94,19 @@ def make_x(rng: np.random.Generator, M: int, K: int, act: str, sigma: float = 1.
 
 
 def make_config(name: str, seed: int | None = None, **overrides) -> dict:
-    """Inputs of one named workload. ``overrides`` may change M, K, N or the
-    seed (for scaled-down parity cases that keep the recipe)."""
+    """Inputs of one named workload. ``overrides`` may change M, K, N, the
+    seed (for scaled-down parity cases that keep the recipe) or the group
+    size (64 or 128 k per scale and bias)."""
     spec = dict(CONFIGS[name])
     spec.update(overrides)
     if seed is not None:
         spec["seed"] = seed
     rng = np.random.default_rng(spec["seed"])
     M, K, N = spec["M"], spec["K"], spec["N"]
-    wq, scales, biases = make_weights(rng, N, K)
+    group = spec.get("group", GROUP)
+    wq, scales, biases = make_weights(rng, N, K, group)
     x = make_x(rng, M, K, spec["act"], spec.get("sigma", 1.0), spec.get("real_rows"))
-    out = dict(spec, name=name, group=GROUP, wq=wq, scales=scales, biases=biases, x=x)
+    out = dict(spec, name=name, group=group, wq=wq, scales=scales, biases=biases, x=x)
     return out
 
 

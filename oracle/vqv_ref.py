@@ -33,7 +33,8 @@ Sources on the pages:
 
 Where the pages are silent the readings are: little-endian nibbles (even k
 in the low nibble), W stored as [N, K] with K contiguous ("K-major"), an
-affine w = s*q + b with fp16 scale and bias per group of 64 contiguous k,
+affine w = s*q + b with fp16 scale and bias per group of 64 contiguous k
+(128 taken as the other group size, with the same layout),
 NaN-first argmax with a lowest-index tie break, and accept_len counting the
 accepted drafts only (0..T-1). Every function here is pinned by tests that do
 not reuse its code (brute force, closed forms, library argmax, hand walks).
@@ -80,6 +81,8 @@ def dequantize(wq: np.ndarray, scales: np.ndarray, biases: np.ndarray,
     K = q.shape[1]
     if K % group:
         raise ValueError("K must be a multiple of the group size")
+    if scales.shape[-1] != K // group or biases.shape[-1] != K // group:
+        raise ValueError("scales and biases must hold K/group entries per row")
     g = np.arange(K) // group
     s = decode_f16(scales)
     b = decode_f16(biases)

@@ -37,7 +37,7 @@ def _act(x, act, m, k) -> Fraction:
     return Fraction(float(x[m][k]))
 
 
-def _brute_qgemm(x, act, wq, scales, biases, M, K, N):
+def _brute_qgemm(x, act, wq, scales, biases, M, K, N, group=64):
     """Exact rational y[m][n] = sum_k x*(s*q + b), with nothing shared with the
     oracle: nibbles read one at a time, fp16/bf16 decoded by struct."""
     xs, wb, sb, bb = x.tolist(), wq.tolist(), scales.tolist(), biases.tolist()
@@ -46,7 +46,7 @@ def _brute_qgemm(x, act, wq, scales, biases, M, K, N):
         for k in range(K):
             byte = wb[n][k // 2]
             q = (byte & 15) if k % 2 == 0 else (byte >> 4)
-            w = _f16(sb[n][k // 64]) * q + _f16(bb[n][k // 64])
+            w = _f16(sb[n][k // group]) * q + _f16(bb[n][k // group])
             for m in range(M):
                 y[m][n] += _act(xs, act, m, k) * w
     return y
@@ -65,6 +65,41 @@ def test_brute_force_tiny(act, M, K, N, seed):
         for n in range(N):
             e = float(exact[m][n])
             assert abs(y[m, n] - e) <= 1e-12 * (1.0 + abs(e)), (m, n, y[m, n], e)
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("M,K,N,seed", [(1, 128, 2, 20), (2, 384, 3, 21)])
+def test_brute_force_tiny_group128(act, M, K, N, seed):
+    """Group 128: one scale and bias per 128 contiguous k."""
+    rng = np.random.default_rng(seed)
+    wq, s, b = gen.make_weights(rng, N, K, group=128)
+    assert s.shape == (N, K // 128)
+    x = gen.make_x(rng, M, K, act)
+    y = qgemm_ref(x, act, wq, s, b, group=128)
+    exact = _brute_qgemm(x, act, wq, s, b, M, K, N, group=128)
+    for m in range(M):
+        for n in range(N):
+            e = float(exact[m][n])
+            assert abs(y[m, n] - e) <= 1e-12 * (1.0 + abs(e)), (m, n, y[m, n], e)
+
+
+def test_group128_is_group64_with_each_entry_twice():
+    """A 128-group's scale and bias cover both of its 64-halves."""
+    rng = np.random.default_rng(22)
+    wq, s, b = gen.make_weights(rng, 9, 512, group=128)
+    x = gen.make_x(rng, 4, 512, "bf16")
+    y128 = qgemm_ref(x, "bf16", wq, s, b, group=128)
+    y64 = qgemm_ref(x, "bf16", wq, np.repeat(s, 2, axis=1), np.repeat(b, 2, axis=1), group=64)
+    np.testing.assert_allclose(y128, y64, rtol=1e-13, atol=1e-13)
+
+
+def test_group_size_must_match_table():
+    rng = np.random.default_rng(23)
+    wq, s, b = gen.make_weights(rng, 3, 256, group=64)
+    with pytest.raises(ValueError):
+        dequantize(wq, s, b, group=128)
+    with pytest.raises(ValueError):
+        dequantize(wq[:, :96], s[:, :3], b[:, :3], group=128)   # K = 192
 
 
 # ---------------------------------------------------------------- closed forms
@@ -223,6 +258,18 @@ def test_dequantize_group_boundary():
                  dtype=np.uint16)
     w = dequantize(wq, s, b)
     assert w[0, 63] == 1.0 and w[0, 64] == 3.5 and w[0, 0] == 1.0 and w[0, 127] == 3.5
+
+
+def test_dequantize_group128_boundary():
+    """k=127 and k=128 sit in different 128-groups; k=63 and k=64 share one."""
+    wq = np.full((1, 128), 0x11, dtype=np.uint8)  # every code 1
+    s = np.array([[np.float16(2.0).view(np.uint16), np.float16(3.0).view(np.uint16)]],
+                 dtype=np.uint16)
+    b = np.array([[np.float16(-1.0).view(np.uint16), np.float16(0.5).view(np.uint16)]],
+                 dtype=np.uint16)
+    w = dequantize(wq, s, b, group=128)
+    assert w[0, 63] == 1.0 and w[0, 64] == 1.0 and w[0, 127] == 1.0
+    assert w[0, 128] == 3.5 and w[0, 255] == 3.5
 
 
 def test_chunking_and_column_subset_agree():

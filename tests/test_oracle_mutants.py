@@ -20,6 +20,7 @@ MUTANTS = {
     "drop_bias": ("return s[:, g] * q + b[:, g]", "return s[:, g] * q"),
     "bias_sign": ("return s[:, g] * q + b[:, g]", "return s[:, g] * q - b[:, g]"),
     "group_index": ("g = np.arange(K) // group", "g = np.arange(K) % (K // group)"),
+    "group_fixed_64": ("g = np.arange(K) // group", "g = (np.arange(K) // 64) % (K // group)"),
     "reversed_columns": ("y[:, c0:c0 + sel.size] = xd @ w.T",
                          "y[:, c0:c0 + sel.size] = (w @ xd.T).T[:, ::-1]"),
     "argmax_last_tie": ("return int(np.flatnonzero(v == top)[0])",
