@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the W4 verify projection + greedy verify on one MI355X.
 
-One step is the whole hot path over one verify block: the W4 group-64 QMM
-y[M,N] = x[M,K] . W^T, then the per-row argmax and accept walk over y. By
+One step is the whole hot path over one verify block: the W4 QMM (group 64,
+or 128 with --group 128) y[M,N] = x[M,K] . W^T, then the per-row argmax and accept walk over y. By
 default a step is one vqv_qgemm_verify call (the argmax fused into the QMM
 epilogue, a one-work-group kernel finishing the rows and the walk); with
 --path separate it is vqv_qgemm followed by vqv_verify; with --path swiglu
@@ -55,8 +55,8 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def qgemm_bytes(M, K, N, esz):
-    return K * N // 2 + 4 * N * (K // 64) + M * K * esz + 4 * M * N
+def qgemm_bytes(M, K, N, esz, group=64):
+    return K * N // 2 + 4 * N * (K // group) + M * K * esz + 4 * M * N
 
 
 KERNEL_SOURCES = ("qgemm.hip", "qgemm_common.h", "qgemm_m16.hip")
@@ -90,14 +90,18 @@ def kernel_sha():
     return h.hexdigest()
 
 
-def traffic_record(workload, M):
+def traffic_key(workload, M, group):
+    return f"{workload}:M={M}" + ("" if group == 64 else f":group={group}")
+
+
+def traffic_record(workload, M, group=64):
     """Measured HBM bytes per launch from committed rocprofv3 counter runs,
     valid only while the kernel source is unchanged."""
     path = os.path.join(ROOT, "profiles", "qgemm_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    entry = rec.get("workloads", {}).get(f"{workload}:M={M}")
+    entry = rec.get("workloads", {}).get(traffic_key(workload, M, group))
     if not entry or rec.get("kernel_sources_sha256") != kernel_sha():
         return None
     return entry["fetch_bytes"] + entry["write_bytes"]
@@ -119,7 +123,8 @@ def cpu_baseline(c, M, T, B, budget_s):
 
     def run(ncols):
         t0 = time.perf_counter()
-        qgemm_ref(x, c["act"], c["wq"][:ncols], c["scales"][:ncols], c["biases"][:ncols])
+        qgemm_ref(x, c["act"], c["wq"][:ncols], c["scales"][:ncols], c["biases"][:ncols],
+                  c["group"])
         return time.perf_counter() - t0
 
     probe = min(N, 1024)
@@ -174,7 +179,15 @@ def _counter_rows(run_dir):
     return rows
 
 
-def write_traffic(fetch_dir, write_dir, workload, M):
+def _fused_kernel(kname):
+    """qgemm_w4_m8 with the verify epilogue (its eighth template argument)."""
+    if "qgemm_w4_m8<" not in kname:
+        return False
+    args = kname.split("qgemm_w4_m8<", 1)[1].split(">", 1)[0].split(",")
+    return len(args) > 7 and args[7].strip() == "true"
+
+
+def write_traffic(fetch_dir, write_dir, workload, M, group=64):
     """Per-launch HBM bytes of the QMM from a FETCH_SIZE pass and a WRITE_SIZE
     pass of `bench.py --counter-pass`, each scaled by what the same counter
     reads for the copy kernel (COPY_PROBE_BYTES read and written per launch)."""
@@ -184,7 +197,7 @@ def write_traffic(fetch_dir, write_dir, workload, M):
         for kname, cname, v in _counter_rows(run_dir):
             if cname != counter:
                 continue
-            if "qgemm_w4" in kname and ", true>" not in kname:
+            if "qgemm_w4" in kname and not _fused_kernel(kname):
                 q.append(v)
             elif "neg" in kname.lower():
                 cp.append(v)
@@ -203,7 +216,7 @@ def write_traffic(fetch_dir, write_dir, workload, M):
     sha = kernel_sha()
     if rec.get("kernel_sources_sha256") != sha:
         rec = {"kernel_sources_sha256": sha, "workloads": {}}
-    key = f"{workload}:M={M}"
+    key = traffic_key(workload, M, group)
     rec["workloads"][key] = out
     json.dump(rec, open(path, "w"), indent=1, sort_keys=True)
     print(json.dumps({key: out}))
@@ -218,6 +231,8 @@ def main():
                     choices=["tiny", "target", "draft_w4a32", "vocab_verify", "batched_vocab",
                              "gate_up"])
     ap.add_argument("--m", type=int, default=None, help="rows (default: the workload's M)")
+    ap.add_argument("--group", type=int, choices=[64, 128], default=64,
+                    help="k per scale and bias (the workloads are quoted at 64)")
     ap.add_argument("--rotate", type=int, default=None, help="weight copies cycled per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -233,7 +248,7 @@ def main():
     if args.write_traffic:
         import gen
         write_traffic(*args.write_traffic, args.workload,
-                      args.m or gen.CONFIGS[args.workload]["M"])
+                      args.m or gen.CONFIGS[args.workload]["M"], args.group)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -252,7 +267,7 @@ def main():
     vqv.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    c = gen.make_config(args.workload)
+    c = gen.make_config(args.workload, group=args.group)
     M = args.m or c["M"]
     K, N, act = c["K"], c["N"], c["act"]
     esz = 4 if act == "fp32" else 2
@@ -264,7 +279,8 @@ def main():
         elif B * T != M:
             raise SystemExit(f"{args.workload}: M must be {B * T}")
 
-    wbytes = K * N // 2 + 4 * N * (K // 64)
+    group = args.group
+    wbytes = K * N // 2 + 4 * N * (K // group)
     R = args.rotate or (math.ceil(2 * MALL_BYTES / (wbytes + M * K * esz)) + 1)
     log(f"device {torch.cuda.get_device_name(dev)}; workload {args.workload} M={M} K={K} N={N} "
         f"{act}; verify T={T} B={B}; rotating {R} copies ({R * wbytes / 1e6:.0f} MB)")
@@ -288,9 +304,9 @@ def main():
         vws = torch.empty(max(vqv.vqv_verify_workspace_bytes(B, T, N), 8), dtype=torch.uint8,
                           device=dev)
     stream = torch.cuda.current_stream()
-    fused_ok = T > 0 and vqv.vqv_qgemm_verify_workspace_bytes(M, K, N, 64, vqv_act) > 0
+    fused_ok = T > 0 and vqv.vqv_qgemm_verify_workspace_bytes(M, K, N, group, vqv_act) > 0
     if fused_ok:
-        fws = torch.zeros(vqv.vqv_qgemm_verify_workspace_bytes(M, K, N, 64, vqv_act),
+        fws = torch.zeros(vqv.vqv_qgemm_verify_workspace_bytes(M, K, N, group, vqv_act),
                           dtype=torch.uint8, device=dev)
     use_fused = fused_ok and args.path == "fused"
     use_swiglu = args.path == "swiglu"
@@ -298,12 +314,12 @@ def main():
         if T or N % 2:
             raise SystemExit("--path swiglu takes a gate/up workload (even N, no verify)")
         hbuf = torch.empty((M, N // 2), dtype=torch.float32, device=dev)
-        sws_n = vqv.vqv_qgemm_swiglu_workspace_bytes(M, K, N, 64, vqv_act)
+        sws_n = vqv.vqv_qgemm_swiglu_workspace_bytes(M, K, N, group, vqv_act)
         sws = torch.empty(sws_n, dtype=torch.uint8, device=dev) if sws_n else None
 
     def qmm(i, st):
         xc, wc, sc, bc = copies[i % R]
-        vqv.vqv_qgemm(xc, wc, sc, bc, y=y, stream=st)
+        vqv.vqv_qgemm(xc, wc, sc, bc, y=y, group=group, stream=st)
 
     def ver(st):
         vqv.vqv_verify(y, draft if T > 1 else None, B, T, argmax=am, accept_len=al,
@@ -312,11 +328,11 @@ def main():
     def fused(i, st):
         xc, wc, sc, bc = copies[i % R]
         vqv.vqv_qgemm_verify(xc, wc, sc, bc, draft if T > 1 else None, B, T, y=y, argmax=am,
-                             accept_len=al, workspace=fws, stream=st)
+                             accept_len=al, workspace=fws, group=group, stream=st)
 
     def swiglu(i, st):
         xc, wc, sc, bc = copies[i % R]
-        vqv.vqv_qgemm_swiglu(xc, wc, sc, bc, h=hbuf, workspace=sws, stream=st)
+        vqv.vqv_qgemm_swiglu(xc, wc, sc, bc, h=hbuf, workspace=sws, group=group, stream=st)
 
     def step(i, st):
         if use_fused:
@@ -428,7 +444,7 @@ def main():
 
             def qm(i, st, xs_sub=xs_sub, ys_sub=ys_sub):
                 _, wc, sc, bc = copies[i % R]
-                vqv.vqv_qgemm(xs_sub[i % R], wc, sc, bc, y=ys_sub, stream=st)
+                vqv.vqv_qgemm(xs_sub[i % R], wc, sc, bc, y=ys_sub, group=group, stream=st)
             g_m = graph_of(qm, nq)
             g_m.replay()
             t_m = statistics.fmean(timed(g_m) * 1e3 / nq for _ in range(3))
@@ -441,7 +457,7 @@ def main():
               "memory_gib": round(props.total_memory / 2 ** 30, 1),
               "hip": torch.version.hip, "torch": torch.__version__}
 
-    qb = qgemm_bytes(M, K, N, esz)
+    qb = qgemm_bytes(M, K, N, esz, group)
     # The dominant kernel is the projection. Its launches are timed in a graph
     # of their own (the fused step's instance adds only the per-group argmax
     # epilogue, 8 bytes per row and work-group, and is timed with the finish
@@ -469,11 +485,11 @@ def main():
         "vs_baseline": None,
         "dtype": act,
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: W4 group-64 QMM M={M} K={K} N={N} {act} "
+        "config": {"workload": f"{args.workload}: W4 group-{group} QMM M={M} K={K} N={N} {act} "
                                + (f"+ greedy verify B={B} T={T}" if T else "(no verify)")
                                + (" (verify fused into the QMM epilogue)" if use_fused else "")
                                + (" with the SwiGLU epilogue, h[M, N/2]" if use_swiglu else ""),
-                   "M": M, "K": K, "N": N, "group": 64, "act": act, "verify_B": B,
+                   "M": M, "K": K, "N": N, "group": group, "act": act, "verify_B": B,
                    "verify_T": T, "weight_copies": R},
         "eager_ms_per_step": ms_eager,
         "qgemm_us_mean": q_mean,
@@ -488,7 +504,7 @@ def main():
         "qgemm_by_M": by_m or None,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "frac_of_copy_probe": achieved / copy_gbs,
-                     "traffic": None if use_swiglu else traffic_record(args.workload, M),
+                     "traffic": None if use_swiglu else traffic_record(args.workload, M, group),
                      "kernel": kname, "bytes_per_launch": qb, "us_per_launch": k_us},
         "cpu_baseline": None,
     }

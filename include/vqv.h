@@ -5,7 +5,7 @@
  * Two core operations, each an asynchronous launch on the caller's HIP stream:
  *
  *   vqv_qgemm   y[M,N] = x[M,K] . W^T, W[N,K] 4-bit group-quantized (affine,
- *               group 64 along K), fp32 output. This is the quantized linear
+ *               group 64 or 128 along K), fp32 output. This is the quantized linear
  *               that a target model runs over the M rows of a verify block
  *               ("perf: tune DFlash2 M=8 verification for M1 and M2", PR
  *               description: tuned M=8 verification QMM with BF16/FP16
@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define VQV_ABI_VERSION 3
+#define VQV_ABI_VERSION 4
 
 typedef enum {
   VQV_BF16 = 0, /* bfloat16 activations                                  */
@@ -91,17 +91,20 @@ const char* vqv_status_string(vqv_status s);
  *   y          [M, N] fp32, written. 4-byte aligned. Must not overlap any
  *              input (VQV_ERR_ARG).
  *   M          1..64 verify rows (a block of 8 or 16, up to 64 batched).
- *   K          multiple of 64, 64 <= K <= 16384 (larger K returns
- *              VQV_ERR_UNSUPPORTED); M*K*sizeof(act) < 2^31.
+ *   K          multiple of the group, 64 <= K <= 16384 (larger K returns
+ *              VQV_ERR_UNSUPPORTED; K not a multiple of the group returns
+ *              VQV_ERR_ARG); M*K*sizeof(act) < 2^31.
  *   N          >= 1 output columns; any N (tails are masked).
- *   group      must be 64 (else VQV_ERR_UNSUPPORTED).
+ *   group      64 or 128 contiguous k per scale and bias (else
+ *              VQV_ERR_UNSUPPORTED). The pages name no group size; 64 is the
+ *              layout of the tuned kernels, 128 the other common W4 layout.
  *   act_dtype  a vqv_dtype (else VQV_ERR_ARG).
  *   workspace  device scratch of at least vqv_qgemm_workspace_bytes(...)
  *              bytes; may be NULL when that is 0.
  *
  * Numerics: products of x and the 4-bit codes are exact; sums are fp32; the
- * per-group scale and bias are applied in fp32 after each group's partial
- * sum. NaN/Inf in x, scales or biases propagate by IEEE rules.
+ * scale and bias are applied in fp32 after each 64-value partial sum (a
+ * 128-group's scale and bias apply to each of its two halves). NaN/Inf in x, scales or biases propagate by IEEE rules.
  */
 size_t vqv_qgemm_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype);
 

@@ -53,7 +53,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.vqv_abi_version() == 3
+    assert L.vqv_abi_version() == 4
     for s in range(6):
         assert L.vqv_status_string(s)
     assert L.vqv_status_string(99) == b"unknown status"
@@ -77,6 +77,10 @@ def test_fused_workspace_queries(L):
     assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 64, FP32) >= head + 8 * 1000 * 4
     assert L.vqv_qgemm_verify_workspace_bytes(0, 512, 1000, 64, BF16) == 0
     assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 32, BF16) == 0
+    # group 128 takes the same paths as group 64
+    assert (L.vqv_qgemm_verify_workspace_bytes(8, 5120, 17408, 128, BF16) ==
+            L.vqv_qgemm_verify_workspace_bytes(8, 5120, 17408, 64, BF16))
+    assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 256, BF16) == 0
 
 
 # Fabricated, well-aligned and non-overlapping device addresses.
@@ -90,7 +94,8 @@ def q(L, x=X, wq=W, s=S, b=B_, y=Y, M=8, K=512, N=1024, group=64, act=BF16, ws=N
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), ARG), (dict(wq=None), ARG), (dict(s=None), ARG), (dict(b=None), ARG),
     (dict(y=None), ARG), (dict(M=0), ARG), (dict(M=65), ARG), (dict(N=0), ARG), (dict(K=0), ARG),
-    (dict(K=32), ARG), (dict(K=100), ARG), (dict(group=32), UNSUP), (dict(group=128), UNSUP),
+    (dict(K=32), ARG), (dict(K=100), ARG), (dict(group=32), UNSUP), (dict(group=256), UNSUP),
+    (dict(group=128, K=192), ARG), (dict(group=128, s=S + 1), ALIGN),
     (dict(act=3), ARG), (dict(act=-1), ARG), (dict(x=X + 8), ALIGN), (dict(wq=W + 4), ALIGN),
     (dict(s=S + 1), ALIGN), (dict(y=Y + 2), ALIGN), (dict(y=X), ARG), (dict(y=W + 64), ARG),
     (dict(y=S), ARG), (dict(M=64, K=64 * 2 ** 20, act=FP32), UNSUP), (dict(K=16384 + 64), UNSUP),
@@ -119,7 +124,8 @@ DR, AM, AC = 0x70000000, 0x80000000, 0x90000000
 
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), ARG), (dict(am=None), ARG), (dict(ac=None), ARG), (dict(dr=None), ARG),
-    (dict(B=2), ARG), (dict(T=4), ARG), (dict(M=65, B=65, T=1), ARG), (dict(group=128), UNSUP),
+    (dict(B=2), ARG), (dict(T=4), ARG), (dict(M=65, B=65, T=1), ARG), (dict(group=32), UNSUP),
+    (dict(group=128, K=320), ARG),
     (dict(K=100), ARG), (dict(y=Y + 4), ALIGN), (dict(am=AM + 2), ALIGN), (dict(ws=None), WS),
     (dict(wsb=8), WS), (dict(ws=WSP + 16), WS), (dict(am=X), ARG), (dict(ws=W), ARG),
     (dict(y=DR), ARG), (dict(ac=AM + 16), ARG), (dict(K=16384 + 64), UNSUP),
@@ -175,12 +181,15 @@ def test_swiglu_workspace_queries(L):
     # invalid: odd N, group, M
     assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1001, 64, BF16) == 0
     assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1000, 32, BF16) == 0
+    assert L.vqv_qgemm_swiglu_workspace_bytes(64, 512, 1000, 128, BF16) == 0
+    assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1000, 256, BF16) == 0
     assert L.vqv_qgemm_swiglu_workspace_bytes(0, 512, 1000, 64, BF16) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), ARG), (dict(h=None), ARG), (dict(N=1001), ARG), (dict(N=0), ARG),
     (dict(M=65), ARG), (dict(K=100), ARG), (dict(group=32), UNSUP), (dict(act=3), ARG),
+    (dict(group=128, K=448), ARG),
     (dict(x=X + 8), ALIGN), (dict(h=Y + 2), ALIGN), (dict(h=X), ARG), (dict(h=W + 64), ARG),
     (dict(h=S), ARG), (dict(K=16384 + 64), UNSUP),
     (dict(act=FP32, ws=None), WS), (dict(act=FP32, wsb=64), WS),

@@ -27,17 +27,17 @@ def vqv():
     return v
 
 
-def case(M, K, N, act, seed):
+def case(M, K, N, act, seed, group=64):
     rng = np.random.default_rng(seed)
-    wq, s, b = gen.make_weights(rng, N, K)
+    wq, s, b = gen.make_weights(rng, N, K, group)
     x = gen.make_x(rng, M, K, act, 1.0, None)
-    return dict(M=M, K=K, N=N, act=act, wq=wq, scales=s, biases=b, x=x, seed=seed)
+    return dict(M=M, K=K, N=N, act=act, wq=wq, scales=s, biases=b, x=x, seed=seed, group=group)
 
 
-def drafts_for(vqv, d, B, T, N, seed, accept):
+def drafts_for(vqv, d, B, T, N, seed, accept, group=64):
     """Drafts that realise the given accept lengths against the GPU's own
     argmax (from the separate path)."""
-    y = vqv.vqv_qgemm(d["x"], d["wq"], d["scales"], d["biases"])
+    y = vqv.vqv_qgemm(d["x"], d["wq"], d["scales"], d["biases"], group=group)
     torch.cuda.synchronize()
     a = np.array([argmax_ref(r) for r in y.cpu().numpy()])
     return gen.make_drafts(a, B, T, N, seed=seed, accept=accept)
@@ -48,12 +48,13 @@ def compare(vqv, c, B, T, accept=None, want_y=True, ws=None):
     M, N = c["M"], c["N"]
     if accept is None:
         accept = np.random.default_rng(c["seed"] + 1).integers(0, T, size=B)
-    draft = drafts_for(vqv, d, B, T, N, c["seed"], accept)
+    group = c.get("group", 64)
+    draft = drafts_for(vqv, d, B, T, N, c["seed"], accept, group)
     dt = torch.from_numpy(draft).cuda() if T > 1 else None
-    y1 = vqv.vqv_qgemm(d["x"], d["wq"], d["scales"], d["biases"])
+    y1 = vqv.vqv_qgemm(d["x"], d["wq"], d["scales"], d["biases"], group=group)
     a1, l1 = vqv.vqv_verify(y1, dt, B, T)
     y2, a2, l2 = vqv.vqv_qgemm_verify(d["x"], d["wq"], d["scales"], d["biases"], dt, B, T,
-                                      want_y=want_y, workspace=ws)
+                                      want_y=want_y, workspace=ws, group=group)
     torch.cuda.synchronize()
     if want_y:
         assert torch.equal(y1, y2), "fused y differs from vqv_qgemm"
@@ -84,6 +85,21 @@ def test_fused_matches_separate(vqv, M, K, N, act, B, T):
 ])
 def test_fallback_matches_separate(vqv, M, K, N, act, B, T):
     compare(vqv, case(M, K, N, act, seed=M + K + N), B, T)
+
+
+@pytest.mark.parametrize("M,K,N,act,B,T", [
+    (8, 512, 1024, "bf16", 1, 8), (8, 2560, 17408, "fp16", 2, 4), (5, 384, 5000, "bf16", 1, 5),
+    (8, 512, 70000, "bf16", 1, 8), (1, 2560, 66000, "fp16", 1, 1), (16, 512, 1000, "bf16", 1, 16),
+    (8, 512, 700, "fp32", 1, 8),
+])
+def test_group128_matches_separate(vqv, M, K, N, act, B, T):
+    """Group 128 through the fused kernels (8-row and whole-tile epilogues) and
+    the two-stage fallback; the logits themselves are pinned by the projection
+    tests."""
+    c = case(M, K, N, act, seed=M * 11 + K + N, group=128)
+    y, _, _ = compare(vqv, c, B, T)
+    ref = qgemm_ref(c["x"], act, c["wq"], c["scales"], c["biases"], group=128)
+    assert_close(y.cpu().numpy(), ref, act, f"group 128 fused M={M} K={K} N={N}")
 
 
 def test_without_logits(vqv):

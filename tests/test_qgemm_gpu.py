@@ -27,16 +27,16 @@ def vqv():
 def run(vqv, c, M=None):
     d = to_device(c)
     x = d["x"] if M is None else d["x"][:M].contiguous()
-    y = vqv.vqv_qgemm(x, d["wq"], d["scales"], d["biases"])
+    y = vqv.vqv_qgemm(x, d["wq"], d["scales"], d["biases"], group=c.get("group", 64))
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
 
-def case(M, K, N, act, seed, sigma=1.0, real_rows=None):
+def case(M, K, N, act, seed, sigma=1.0, real_rows=None, group=64):
     rng = np.random.default_rng(seed)
-    wq, s, b = gen.make_weights(rng, N, K)
+    wq, s, b = gen.make_weights(rng, N, K, group)
     x = gen.make_x(rng, M, K, act, sigma, real_rows)
-    return dict(M=M, K=K, N=N, act=act, wq=wq, scales=s, biases=b, x=x)
+    return dict(M=M, K=K, N=N, act=act, wq=wq, scales=s, biases=b, x=x, group=group)
 
 
 # Shapes span several column tiles and work-group splits, ragged N tails,
@@ -74,6 +74,57 @@ def test_parity_small(vqv, act, M, K, N):
     y = run(vqv, c)
     ref = qgemm_ref(c["x"], act, c["wq"], c["scales"], c["biases"])
     assert_close(y, ref, act, f"M={M} K={K} N={N} {act}")
+
+
+# Group 128 through every kernel: the target projection and the 8-row kernel,
+# the generic kernel (K/64 not a multiple of 8, odd K/128), the 16-row kernel
+# with and without 16-byte table units, row sets on one weight stream
+# (partial chunks), whole-tile waves, and the narrow draft projection.
+SHAPES_G128 = [
+    (8, 5120, 17408), (8, 512, 1024), (4, 1280, 12000), (1, 128, 17), (5, 384, 1000),
+    (16, 640, 300), (16, 1024, 5000), (12, 2560, 17408), (48, 1280, 3001),
+    (64, 2560, 70000), (40, 1280, 40001), (33, 384, 36000),
+    (8, 512, 70000), (16, 1024, 66000), (48, 512, 30000), (1, 5120, 1024), (8, 5120, 1000),
+]
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("M,K,N", SHAPES_G128)
+def test_parity_group128(vqv, act, M, K, N):
+    c = case(M, K, N, act, seed=M * 1000 + K + N + 128, group=128)
+    y = run(vqv, c)
+    ref = qgemm_ref(c["x"], act, c["wq"], c["scales"], c["biases"], group=128)
+    assert_close(y, ref, act, f"group 128 M={M} K={K} N={N} {act}")
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp32"])
+@pytest.mark.parametrize("M,K,N", SHAPES_G128[::2])
+def test_group128_equals_group64_twice(vqv, act, M, K, N):
+    """A 128-group's entry serves both 64-halves in the kernels: the result
+    equals, bit for bit, group 64 with every entry repeated."""
+    c = case(M, K, N, act, seed=M + K + N, group=128)
+    y128 = run(vqv, c)
+    c64 = dict(c, group=64, scales=np.repeat(c["scales"], 2, axis=1),
+               biases=np.repeat(c["biases"], 2, axis=1))
+    np.testing.assert_array_equal(y128, run(vqv, c64))
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("M,K,N", [(8, 512, 1024), (3, 384, 37), (16, 1280, 96), (64, 256, 40)])
+def test_integer_case_bit_exact_group128(vqv, act, M, K, N):
+    """Integer-exact inputs with one scale and bias per 128 k: fp32 is exact in
+    any order, so the GPU equals the oracle bit for bit."""
+    rng = np.random.default_rng(17 + M + K + N)
+    wq = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    G = K // 128
+    s = np.full((N, G), np.float16(1.0).view(np.uint16), dtype=np.uint16)
+    b = rng.integers(-8, 1, size=(N, G)).astype(np.float16).view(np.uint16)
+    xi = rng.integers(-8, 9, size=(M, K)).astype(np.float32)
+    x = {"bf16": lambda: gen.f32_to_bf16_bits(xi), "fp16": lambda: xi.astype(np.float16).view(np.uint16),
+         "fp32": lambda: xi}[act]()
+    c = dict(M=M, K=K, N=N, act=act, wq=wq, scales=s, biases=b, x=x, group=128)
+    np.testing.assert_array_equal(run(vqv, c), qgemm_ref(x, act, wq, s, b, group=128)
+                                  .astype(np.float32))
 
 
 @pytest.mark.parametrize("act", ["bf16", "fp16", "fp32"])

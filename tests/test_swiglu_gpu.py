@@ -32,19 +32,20 @@ def vqv():
     return v
 
 
-def case(M, K, N, act, seed, sigma=1.0):
+def case(M, K, N, act, seed, sigma=1.0, group=64):
     rng = np.random.default_rng(seed)
-    wq, s, b = gen.make_weights(rng, N, K)
+    wq, s, b = gen.make_weights(rng, N, K, group)
     x = gen.make_x(rng, M, K, act, sigma, None)
-    return dict(M=M, K=K, N=N, act=act, wq=wq, scales=s, biases=b, x=x)
+    return dict(M=M, K=K, N=N, act=act, wq=wq, scales=s, biases=b, x=x, group=group)
 
 
 def gate_up_ref(c, cols=None):
     """float64 gate g, up u and h = silu(g)*u for hidden columns `cols`."""
     nh = c["N"] // 2
     idx = np.arange(nh) if cols is None else np.asarray(cols)
-    g = qgemm_ref(c["x"], c["act"], c["wq"], c["scales"], c["biases"], cols=idx)
-    u = qgemm_ref(c["x"], c["act"], c["wq"], c["scales"], c["biases"], cols=nh + idx)
+    group = c.get("group", 64)
+    g = qgemm_ref(c["x"], c["act"], c["wq"], c["scales"], c["biases"], group, cols=idx)
+    u = qgemm_ref(c["x"], c["act"], c["wq"], c["scales"], c["biases"], group, cols=nh + idx)
     return g, u, silu_ref(g) * u
 
 
@@ -65,7 +66,7 @@ def assert_swiglu_close(h_gpu, g, u, h_ref, act, what):
 def run(vqv, c, M=None):
     d = to_device(c)
     x = d["x"] if M is None else d["x"][:M].contiguous()
-    h = vqv.vqv_qgemm_swiglu(x, d["wq"], d["scales"], d["biases"])
+    h = vqv.vqv_qgemm_swiglu(x, d["wq"], d["scales"], d["biases"], group=c.get("group", 64))
     torch.cuda.synchronize()
     return h.cpu().numpy()
 
@@ -87,6 +88,16 @@ def test_swiglu_parity(vqv, M, K, N, act):
     g, u, ref = gate_up_ref(c)
     worst = assert_swiglu_close(h, g, u, ref, act, f"M={M} K={K} N={N} {act}")
     print(f"M={M} K={K} N={N} {act}: worst error/allowance {worst:.3g}")
+
+
+@pytest.mark.parametrize("M,K,N,act", [(16, 512, 2 * 1000, "bf16"), (12, 640, 2 * 777, "fp16"),
+                                        (16, 2560, 2 * 3000, "bf16"), (64, 256, 2 * 130, "fp16"),
+                                        (16, 512, 2 * 300, "fp32"), (40, 3072, 2 * 150, "fp16")])
+def test_swiglu_group128(vqv, M, K, N, act):
+    c = case(M, K, N, act, seed=M * 100 + K + N + 128, group=128)
+    h = run(vqv, c)
+    g, u, ref = gate_up_ref(c)
+    assert_swiglu_close(h, g, u, ref, act, f"group 128 M={M} K={K} N={N} {act}")
 
 
 def test_fused_workspace_is_zero(vqv):

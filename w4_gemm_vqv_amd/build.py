@@ -2,7 +2,8 @@
 
     python -m w4_gemm_vqv_amd.build
 
-The library is compiled as one shared object from the HIP sources in csrc/.
+The HIP sources in csrc/ are compiled to objects in parallel and linked into
+one shared object.
 Packed fp32 instructions are disabled for the device pass; hipcc's host pass
 warns that it does not know that feature, which is harmless.
 """
@@ -13,6 +14,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -29,26 +32,47 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libvqv)")
 
 
-def command(out: str) -> list[str]:
-    return [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+def flags() -> list[str]:
+    return ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-mllvm", "-amdgpu-mfma-vgpr-form",
-            "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-command-line-argument",
-            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
+            "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-command-line-argument"]
+
+
+def _run(cmd: list[str]) -> tuple[int, list[str]]:
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    return r.returncode, [ln for ln in r.stderr.splitlines()
+                          if "is not a recognized feature" not in ln]
 
 
 def build(verbose: bool = True) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    errs = [ln for ln in r.stderr.splitlines() if "is not a recognized feature" not in ln]
-    if r.returncode != 0:
-        raise RuntimeError("libvqv build failed:\n" + "\n".join(errs))
-    if verbose and errs:
-        print("\n".join(errs), file=sys.stderr)
-    os.replace(tmp, LIB)
+    """Compile every source to an object (in parallel), then link the shared
+    library; the previous library is replaced only when both steps succeed."""
+    objdir = tempfile.mkdtemp(prefix="vqv_build_")
+    try:
+        objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
+        cmds = [[hipcc(), *flags(), "-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), flush=True)
+        with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
+            results = list(ex.map(_run, cmds))
+        errs = [ln for _, e in results for ln in e]
+        if any(rc != 0 for rc, _ in results):
+            raise RuntimeError("libvqv build failed:\n" + "\n".join(errs))
+        tmp = LIB + ".tmp"
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        rc, lerrs = _run(link)
+        if rc != 0:
+            raise RuntimeError("libvqv link failed:\n" + "\n".join(lerrs))
+        if verbose and (errs or lerrs):
+            print("\n".join(errs + lerrs), file=sys.stderr)
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     return LIB
 
 

@@ -113,12 +113,13 @@ __host__ __device__ inline LdsLayout lds_layout(int G) {
   return L;
 }
 
-template <int ACT, int R, int TILES, int WN, int WK, int D, int KC, bool XALL>
+template <int ACT, int R, int TILES, int WN, int WK, int D, int KC, bool XALL, int GS>
 __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     float* __restrict__ y, int M, int K, int N, int cols) {
   using TR = ActTraits<ACT>;
+  constexpr int gs = GS;                            // group 64 << GS
   constexpr int P = TR::parts;
   constexpr int NT = 64 * WN * WK;                  // threads
   constexpr int WCOLS = 16 * TILES;                 // columns per wave
@@ -164,9 +165,11 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
       const_cast<uint8_t*>(wq) + (size_t)wg0 * rowbytes, (short)0, wgcols * rowbytes,
       kBufferFlags);
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(scales) + (size_t)wg0 * G, (short)0, wgcols * G * 2, kBufferFlags);
+      const_cast<uint16_t*>(scales) + (size_t)wg0 * (G >> gs), (short)0, wgcols * (G >> gs) * 2,
+      kBufferFlags);
   const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(biases) + (size_t)wg0 * G, (short)0, wgcols * G * 2, kBufferFlags);
+      const_cast<uint16_t*>(biases) + (size_t)wg0 * (G >> gs), (short)0, wgcols * (G >> gs) * 2,
+      kBufferFlags);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(x), (short)0, M * K * TR::esz, kBufferFlags);
 
@@ -191,11 +194,11 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
     for (int u = 0; u < SBU; ++u) {
       const int i = (round * SBU + u) * NT + tid;
       if (sb_vec) {
-        const unsigned off = i < sb_units ? 16u * i : kOutOfRange;
-        sbs[u] = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
-        sbb[u] = __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0);
+        const unsigned off = i < sb_units ? (16u * i) >> gs : kOutOfRange;
+        sbs[u] = sb_unit_load<GS>(sr, off);
+        sbb[u] = sb_unit_load<GS>(br, off);
       } else {
-        const unsigned off = i < sb_units ? 2u * i : kOutOfRange;
+        const unsigned off = i < sb_units ? 2u * ((unsigned)i >> gs) : kOutOfRange;
         sbs[u].x = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
         sbb[u].x = __builtin_amdgcn_raw_buffer_load_b16(br, off, 0, 0);
       }
@@ -210,14 +213,7 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
           const int e0 = 8 * i;                       // first element of the unit
           const int n = e0 / G, g = e0 - n * G;
           u32x4 lo, hi;                               // (s_g | b_g << 16) for g .. g+7
-          lo.x = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x05040100u);
-          lo.y = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x07060302u);
-          lo.z = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x05040100u);
-          lo.w = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x07060302u);
-          hi.x = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x05040100u);
-          hi.y = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x07060302u);
-          hi.z = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x05040100u);
-          hi.w = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x07060302u);
+          sb_pairs<GS>(sbs[u], sbb[u], lo, hi);
           *reinterpret_cast<u32x4*>(&sbl[n * L.sbs + g]) = lo;
           *reinterpret_cast<u32x4*>(&sbl[n * L.sbs + g + 4]) = hi;
         } else {
@@ -515,12 +511,13 @@ __host__ __device__ inline M8Layout m8_layout(int G, int WGC, int NW, int XB) {
 //    the buffer): its activations, row sum, scale and bias are all zero, so
 //    it adds exactly nothing. Columns past the work-group's read zeros and
 //    are never stored.
-template <int ACT, int NW, int TW, int DB, int RB, int D0, int XB, bool FUSED>
+template <int ACT, int NW, int TW, int DB, int RB, int D0, int XB, bool FUSED, int GS>
 __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     float* __restrict__ y, int M, int K, int N, int cols, VerifyArgs va) {
   using TR = ActTraits<ACT>;
+  constexpr int gs = GS;                            // group 64 << GS
   static_assert(TR::parts == 1, "16-bit activations only");
   static_assert(TW <= NW, "a run must span at most two tiles");
   static_assert(NW >= 8, "the partial-sum slots double as an 8 KB write sink");
@@ -565,9 +562,11 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
       const_cast<uint8_t*>(wq) + (size_t)wg0 * rowbytes, (short)0, wgcols * rowbytes,
       kBufferFlags);
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(scales) + (size_t)wg0 * G, (short)0, wgcols * G * 2, kBufferFlags);
+      const_cast<uint16_t*>(scales) + (size_t)wg0 * (G >> gs), (short)0, wgcols * (G >> gs) * 2,
+      kBufferFlags);
   const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(biases) + (size_t)wg0 * G, (short)0, wgcols * G * 2, kBufferFlags);
+      const_cast<uint16_t*>(biases) + (size_t)wg0 * (G >> gs), (short)0, wgcols * (G >> gs) * 2,
+      kBufferFlags);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(x), (short)0, M * K * 2, kBufferFlags);
 
@@ -618,11 +617,11 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
     for (int u = 0; u < SBU; ++u) {
       const int i = (round * SBU + u) * NT + tid;
       if (sb_vec) {
-        const unsigned off = i < sb_units ? 16u * i : kOutOfRange;
-        sbs[u] = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
-        sbb[u] = __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0);
+        const unsigned off = i < sb_units ? (16u * i) >> gs : kOutOfRange;
+        sbs[u] = sb_unit_load<GS>(sr, off);
+        sbb[u] = sb_unit_load<GS>(br, off);
       } else {
-        const unsigned off = i < sb_units ? 2u * i : kOutOfRange;
+        const unsigned off = i < sb_units ? 2u * ((unsigned)i >> gs) : kOutOfRange;
         sbs[u].x = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
         sbb[u].x = __builtin_amdgcn_raw_buffer_load_b16(br, off, 0, 0);
       }
@@ -641,14 +640,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
         const unsigned e0 = 8u * (unsigned)i;         // first element of the unit
         const unsigned n = div_g(e0), g = e0 - n * (unsigned)G;
         u32x4 lo, hi;                                 // (s_g | b_g << 16) for g .. g+7
-        lo.x = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x07060302u);
-        lo.z = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x05040100u);
-        lo.w = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x07060302u);
-        hi.x = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x05040100u);
-        hi.y = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x07060302u);
-        hi.z = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x05040100u);
-        hi.w = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x07060302u);
+        sb_pairs<GS>(sbs[u], sbb[u], lo, hi);
         // Units past the table write into the partial-sum slots (8 KB, not
         // read before the end of the loop).
         const unsigned o = ok ? (unsigned)L.sb + 4u * (n * (unsigned)L.sbs + g)
@@ -902,10 +894,11 @@ int lds_bytes_for(int K) {
 
 template <int ACT, int R, int TILES, int WN, int WK, int D, int KC, bool XALL>
 hipError_t launch_w4(const void* x, const uint8_t* wq, const uint16_t* scales,
-                     const uint16_t* biases, float* y, int M, int K, int N, int cols,
+                     const uint16_t* biases, float* y, int M, int K, int N, int cols, int gs,
                      hipStream_t stream) {
   const int lds_bytes = lds_bytes_for<ACT, R, TILES, WN, WK, D, KC, XALL>(K);
-  auto kern = qgemm_w4<ACT, R, TILES, WN, WK, D, KC, XALL>;
+  auto kern = gs ? qgemm_w4<ACT, R, TILES, WN, WK, D, KC, XALL, 1>
+                 : qgemm_w4<ACT, R, TILES, WN, WK, D, KC, XALL, 0>;
   if (lds_bytes > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -920,12 +913,14 @@ hipError_t launch_w4(const void* x, const uint8_t* wq, const uint16_t* scales,
 
 template <int ACT, int NW, int DB, int RB, int XB, int D0 = 2>
 hipError_t launch_m8(const void* x, const uint8_t* wq, const uint16_t* scales,
-                     const uint16_t* biases, float* y, int M, int K, int N, int cols,
+                     const uint16_t* biases, float* y, int M, int K, int N, int cols, int gs,
                      const VerifyArgs& va, hipStream_t stream) {
   constexpr int TW = 5;
   const M8Layout L = m8_layout(K >> 6, 16 * TW, NW, XB);
-  auto kern = va.argmax ? qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, true>
-                        : qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, false>;
+  auto kern = va.argmax ? (gs ? qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, true, 1>
+                           : qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, true, 0>)
+                        : (gs ? qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, false, 1>
+                              : qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, false, 0>);
   if (L.total > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -948,15 +943,15 @@ constexpr int m8_xb(int K) { return K <= 2560 ? 5 : 10; }
 template <int ACT, int XB>
 hipError_t launch_m8_blocks(const void* x, const uint8_t* wq, const uint16_t* scales,
                             const uint16_t* biases, float* y, int M, int K, int N, int cols,
-                            const VerifyArgs& va, hipStream_t s) {
+                            int gs, const VerifyArgs& va, hipStream_t s) {
   const int GP = ((K >> 6) + 1) >> 1;
   if (GP % 5 == 0)
-    return launch_m8<ACT, 8, 5, 1, XB>(x, wq, scales, biases, y, M, K, N, cols, va, s);
+    return launch_m8<ACT, 8, 5, 1, XB>(x, wq, scales, biases, y, M, K, N, cols, gs, va, s);
   if (GP % 4 == 0)
-    return launch_m8<ACT, 8, 4, 2, XB>(x, wq, scales, biases, y, M, K, N, cols, va, s);
+    return launch_m8<ACT, 8, 4, 2, XB>(x, wq, scales, biases, y, M, K, N, cols, gs, va, s);
   if (GP % 2 == 0)
-    return launch_m8<ACT, 8, 2, 4, XB>(x, wq, scales, biases, y, M, K, N, cols, va, s);
-  return launch_m8<ACT, 8, 1, 8, XB>(x, wq, scales, biases, y, M, K, N, cols, va, s);
+    return launch_m8<ACT, 8, 2, 4, XB>(x, wq, scales, biases, y, M, K, N, cols, gs, va, s);
+  return launch_m8<ACT, 8, 1, 8, XB>(x, wq, scales, biases, y, M, K, N, cols, gs, va, s);
 }
 
 // Columns per work-group of qgemm_w4_m8 (an equal share of the CUs, at most
@@ -970,12 +965,12 @@ bool m8_fits(int K) { return m8_layout(K >> 6, 80, 8, m8_xb(K)).total <= kLdsLim
 
 template <int ACT>
 hipError_t launch_m8_any(const void* x, const uint8_t* wq, const uint16_t* scales,
-                         const uint16_t* biases, float* y, int M, int K, int N,
+                         const uint16_t* biases, float* y, int M, int K, int N, int gs,
                          const VerifyArgs& va, hipStream_t s) {
   const int cols = m8_cols(N);
   if (m8_xb(K) == 5)
-    return launch_m8_blocks<ACT, 5>(x, wq, scales, biases, y, M, K, N, cols, va, s);
-  return launch_m8_blocks<ACT, 10>(x, wq, scales, biases, y, M, K, N, cols, va, s);
+    return launch_m8_blocks<ACT, 5>(x, wq, scales, biases, y, M, K, N, cols, gs, va, s);
+  return launch_m8_blocks<ACT, 10>(x, wq, scales, biases, y, M, K, N, cols, gs, va, s);
 }
 
 // Configuration per problem. M <= 8 (one row set): when the work-group's
@@ -984,66 +979,66 @@ hipError_t launch_m8_any(const void* x, const uint8_t* wq, const uint16_t* scale
 // to five waves of 16), wide N into 64-column groups.
 template <int ACT>
 hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
-                         const uint16_t* biases, float* y, int M, int K, int N,
+                         const uint16_t* biases, float* y, int M, int K, int N, int gs,
                          hipStream_t s) {
   if constexpr (ACT != ACT_FP32) if (qgemm_rows_fits(M, K, N, ACT)) {
     // 17..64 rows at vocabulary widths: all row sets on one weight stream.
-    return launch_qgemm_rows(x, wq, scales, biases, y, M, K, N, ACT, s);
+    return launch_qgemm_rows(x, wq, scales, biases, y, M, K, N, ACT, gs, s);
   }
   if (qgemm_wide_fits(M, K, N, ACT)) {
     // Vocabulary widths: whole-tile waves (the fused verify's projection
     // takes the same kernel, so the two paths agree bit for bit).
     const VerifyArgs none{};
-    return launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, ACT, none, s);
+    return launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, ACT, gs, none, s);
   }
   if constexpr (ACT != ACT_FP32) if (M <= 8 && m8_fits(K)) {
     const VerifyArgs none{};
-    return launch_m8_any<ACT>(x, wq, scales, biases, y, M, K, N, none, s);
+    return launch_m8_any<ACT>(x, wq, scales, biases, y, M, K, N, gs, none, s);
   }
   if (M > 8 && qgemm_m16_fits(M, K, ACT))
-    return launch_qgemm_m16(x, wq, scales, biases, y, M, K, N, ACT, s);
+    return launch_qgemm_m16(x, wq, scales, biases, y, M, K, N, ACT, gs, s);
   if (M <= 8) {
     const int cus = device_cus();
     const int share = ((N + cus - 1) / cus + 3) / 4 * 4;
     if (share > 48 && share <= 80 &&
         lds_bytes_for<ACT, 1, 1, 5, 2, 8, 1, true>(K) <= kLdsLimit)
-      return launch_w4<ACT, 1, 1, 5, 2, 8, 1, true>(x, wq, scales, biases, y, M, K, N, share, s);
+      return launch_w4<ACT, 1, 1, 5, 2, 8, 1, true>(x, wq, scales, biases, y, M, K, N, share, gs, s);
     // Narrow outputs (fewer 64-column groups than CUs, e.g. the W4A32 draft
     // projection): one 16-column tile per work-group, K split over 8 waves,
     // no weight prefetch beyond the current step (measured fastest at
     // K = 5120, N = 1024: 11.1 us against 15.5 us for 64-column groups).
     if ((N + 63) / 64 < cus && lds_bytes_for<ACT, 1, 1, 1, 8, 1, 1, false>(K) <= kLdsLimit)
-      return launch_w4<ACT, 1, 1, 1, 8, 1, 1, false>(x, wq, scales, biases, y, M, K, N, 16, s);
+      return launch_w4<ACT, 1, 1, 1, 8, 1, 1, false>(x, wq, scales, biases, y, M, K, N, 16, gs, s);
     if (lds_bytes_for<ACT, 1, 1, 4, 2, 8, 1, true>(K) <= kLdsLimit)
-      return launch_w4<ACT, 1, 1, 4, 2, 8, 1, true>(x, wq, scales, biases, y, M, K, N, 64, s);
-    return launch_w4<ACT, 1, 1, 4, 2, 4, 2, false>(x, wq, scales, biases, y, M, K, N, 64, s);
+      return launch_w4<ACT, 1, 1, 4, 2, 8, 1, true>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
+    return launch_w4<ACT, 1, 1, 4, 2, 4, 2, false>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
   }
   // Several row sets: chunked staging; the smaller fallback (32 columns,
   // one K range, one-step chunks) keeps fp32 at large K within LDS.
   if (M <= 16) {
     if (lds_bytes_for<ACT, 2, 1, 4, 2, 4, 2, false>(K) <= kLdsLimit)
-      return launch_w4<ACT, 2, 1, 4, 2, 4, 2, false>(x, wq, scales, biases, y, M, K, N, 64, s);
-    return launch_w4<ACT, 2, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, s);
+      return launch_w4<ACT, 2, 1, 4, 2, 4, 2, false>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
+    return launch_w4<ACT, 2, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, gs, s);
   }
   if (M <= 32) {
     if (lds_bytes_for<ACT, 4, 1, 4, 1, 4, 1, false>(K) <= kLdsLimit)
-      return launch_w4<ACT, 4, 1, 4, 1, 4, 1, false>(x, wq, scales, biases, y, M, K, N, 64, s);
-    return launch_w4<ACT, 4, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, s);
+      return launch_w4<ACT, 4, 1, 4, 1, 4, 1, false>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
+    return launch_w4<ACT, 4, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, gs, s);
   }
   if (lds_bytes_for<ACT, 8, 1, 4, 1, 2, 1, false>(K) <= kLdsLimit)
-    return launch_w4<ACT, 8, 1, 4, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 64, s);
-  return launch_w4<ACT, 8, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, s);
+    return launch_w4<ACT, 8, 1, 4, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
+  return launch_w4<ACT, 8, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, gs, s);
 }
 
 }  // namespace
 
 hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
-                        const uint16_t* biases, float* y, int M, int K, int N, int act,
+                        const uint16_t* biases, float* y, int M, int K, int N, int act, int gs,
                         hipStream_t stream) {
   switch (act) {
-    case ACT_BF16: return dispatch_rows<ACT_BF16>(x, wq, scales, biases, y, M, K, N, stream);
-    case ACT_FP16: return dispatch_rows<ACT_FP16>(x, wq, scales, biases, y, M, K, N, stream);
-    case ACT_FP32: return dispatch_rows<ACT_FP32>(x, wq, scales, biases, y, M, K, N, stream);
+    case ACT_BF16: return dispatch_rows<ACT_BF16>(x, wq, scales, biases, y, M, K, N, gs, stream);
+    case ACT_FP16: return dispatch_rows<ACT_FP16>(x, wq, scales, biases, y, M, K, N, gs, stream);
+    case ACT_FP32: return dispatch_rows<ACT_FP32>(x, wq, scales, biases, y, M, K, N, gs, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1062,14 +1057,14 @@ int qgemm_verify_groups(int M, int K, int N, int act) {
 
 hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* scales,
                                const uint16_t* biases, float* y, int M, int K, int N, int act,
-                               const VerifyArgs& va, hipStream_t stream) {
+                               int gs, const VerifyArgs& va, hipStream_t stream) {
   hipError_t e = hipErrorInvalidValue;
   if (qgemm_wide_fits(M, K, N, act))
-    e = launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, act, va, stream);
+    e = launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, act, gs, va, stream);
   else if (act == ACT_BF16)
-    e = launch_m8_any<ACT_BF16>(x, wq, scales, biases, y, M, K, N, va, stream);
+    e = launch_m8_any<ACT_BF16>(x, wq, scales, biases, y, M, K, N, gs, va, stream);
   else if (act == ACT_FP16)
-    e = launch_m8_any<ACT_FP16>(x, wq, scales, biases, y, M, K, N, va, stream);
+    e = launch_m8_any<ACT_FP16>(x, wq, scales, biases, y, M, K, N, gs, va, stream);
   if (e != hipSuccess) return e;
   return launch_verify_finish(va.partials, qgemm_verify_groups(M, K, N, act), va, stream);
 }

@@ -106,6 +106,48 @@ __device__ __forceinline__ float sum8_lanes(float s) {
   return s;
 }
 
+// Scales and biases hold one 16-bit entry per group of 64 << GS values
+// (GS = 0: group 64, GS = 1: group 128; a template parameter of the kernels).
+// The kernels' tables are per 64-group: a 128-group's entry serves both of
+// its 64-groups, and the per-64-group row sums make the bias term
+// b * (xs0 + xs1) come out as b * xs of the 128-group.
+// A table unit covers 8 consecutive 64-groups of one column (K/64 a multiple
+// of 8). sb_unit_load reads one unit's entries from byte offset `off` of an
+// array: 16 bytes for group 64, or the 4 entries of group 128 (8 bytes,
+// 8-byte aligned) in .x and .y. sb_pairs then forms the unit's 8 LDS words
+// (s_g | b_g << 16) for g = 0..3 (lo) and 4..7 (hi), each 128-group entry
+// serving two consecutive words. The shuffles sit where the words are
+// stored, so the loads need not complete before later loads are issued.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+template <int GS>
+__device__ __forceinline__ u32x4 sb_unit_load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  if constexpr (GS == 0) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  } else {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return u32x4{v.x, v.y, 0u, 0u};
+  }
+}
+
+template <int GS>
+__device__ __forceinline__ void sb_pairs(const u32x4& s, const u32x4& b, u32x4& lo, u32x4& hi) {
+  if constexpr (GS == 0) {
+    lo.x = __builtin_amdgcn_perm(b.x, s.x, 0x05040100u);
+    lo.y = __builtin_amdgcn_perm(b.x, s.x, 0x07060302u);
+    lo.z = __builtin_amdgcn_perm(b.y, s.y, 0x05040100u);
+    lo.w = __builtin_amdgcn_perm(b.y, s.y, 0x07060302u);
+    hi.x = __builtin_amdgcn_perm(b.z, s.z, 0x05040100u);
+    hi.y = __builtin_amdgcn_perm(b.z, s.z, 0x07060302u);
+    hi.z = __builtin_amdgcn_perm(b.w, s.w, 0x05040100u);
+    hi.w = __builtin_amdgcn_perm(b.w, s.w, 0x07060302u);
+  } else {
+    lo.x = lo.y = __builtin_amdgcn_perm(b.x, s.x, 0x05040100u);
+    lo.z = lo.w = __builtin_amdgcn_perm(b.x, s.x, 0x07060302u);
+    hi.x = hi.y = __builtin_amdgcn_perm(b.y, s.y, 0x05040100u);
+    hi.z = hi.w = __builtin_amdgcn_perm(b.y, s.y, 0x07060302u);
+  }
+}
+
 constexpr int kLdsLimit = 160 * 1024;
 
 inline int device_cus() {

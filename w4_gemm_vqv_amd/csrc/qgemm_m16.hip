@@ -107,12 +107,14 @@ __device__ __forceinline__ void pair_step(const u32x4 (&A)[4], const u32x4& w, u
   C1 = mfma16x16x32<F16>(A[3], bq[3], C1);
 }
 
-template <int ACT, int NW, int TW, int DB, int RB, int D0, int XB, bool SWIGLU, bool SBV>
+template <int ACT, int NW, int TW, int DB, int RB, int D0, int XB, bool SWIGLU, bool SBV,
+          int GS>
 __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     float* __restrict__ y, int M, int K, int N, int cols, int rsets, int workers) {
   using TR = ActTraits<ACT>;
+  constexpr int gs = GS;                            // group 64 << GS
   static_assert(TR::parts == 1, "16-bit activations only");
   static_assert(TW <= NW, "a run must span at most two tiles");
   static_assert(NW >= 8, "the partial-sum slots double as a write sink");
@@ -246,11 +248,11 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
         const_cast<uint8_t*>(wq) + (size_t)row0 * rowbytes, (short)0, nrows * rowbytes,
         kBufferFlags);
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(scales) + (size_t)row0 * G, (short)0, nrows * G * 2,
-        kBufferFlags);
+        const_cast<uint16_t*>(scales) + (size_t)row0 * (G >> gs), (short)0,
+        nrows * (G >> gs) * 2, kBufferFlags);
     const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(biases) + (size_t)row0 * G, (short)0, nrows * G * 2,
-        kBufferFlags);
+        const_cast<uint16_t*>(biases) + (size_t)row0 * (G >> gs), (short)0,
+        nrows * (G >> gs) * 2, kBufferFlags);
 
     // ---- scale/bias table: row n of the table is logical column n.
     const int sb_units = sb_vec ? wgcols * G / 8 : wgcols * G;
@@ -263,13 +265,15 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
           const unsigned e0 = 8u * (unsigned)i;
           const unsigned n = div_g(e0), g = e0 - n * (unsigned)G;
           const unsigned off =
-              i < sb_units ? 2u * ((unsigned)rel_row((int)n) * (unsigned)G + g) : kOutOfRange;
-          sbs[u] = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
-          sbb[u] = __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0);
+              i < sb_units ? 2u * (((unsigned)rel_row((int)n) * (unsigned)G + g) >> gs)
+                           : kOutOfRange;
+          sbs[u] = sb_unit_load<GS>(sr, off);
+          sbb[u] = sb_unit_load<GS>(br, off);
         } else {
           const unsigned n = div_g((unsigned)i), g = (unsigned)i - n * (unsigned)G;
           const unsigned off =
-              i < sb_units ? 2u * ((unsigned)rel_row((int)n) * (unsigned)G + g) : kOutOfRange;
+              i < sb_units ? 2u * (((unsigned)rel_row((int)n) * (unsigned)G + g) >> gs)
+                           : kOutOfRange;
           sbs[u].x = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
           sbb[u].x = __builtin_amdgcn_raw_buffer_load_b16(br, off, 0, 0);
         }
@@ -284,14 +288,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
           const unsigned e0 = 8u * (unsigned)i;
           const unsigned n = div_g(e0), g = e0 - n * (unsigned)G;
           u32x4 lo, hi;                               // (s_g | b_g << 16) for g .. g+7
-          lo.x = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x05040100u);
-          lo.y = __builtin_amdgcn_perm(sbb[u].x, sbs[u].x, 0x07060302u);
-          lo.z = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x05040100u);
-          lo.w = __builtin_amdgcn_perm(sbb[u].y, sbs[u].y, 0x07060302u);
-          hi.x = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x05040100u);
-          hi.y = __builtin_amdgcn_perm(sbb[u].z, sbs[u].z, 0x07060302u);
-          hi.z = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x05040100u);
-          hi.w = __builtin_amdgcn_perm(sbb[u].w, sbs[u].w, 0x07060302u);
+          sb_pairs<GS>(sbs[u], sbb[u], lo, hi);
           // Units past the table write into the partial-sum slots (16 KB,
           // not read until this group's loop has ended).
           const unsigned o = ok ? (unsigned)L.sb + 4u * (n * (unsigned)L.sbs + g)
@@ -518,13 +515,14 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
 // keeps the top two of its rows over all its columns, and the work-group
 // writes one top-two partial per row for verify_finish (the greedy verify's
 // first half, as in qgemm_w4_m8's fused epilogue).
-template <int ACT, int DB, int RB>
+template <int ACT, int DB, int RB, int GS>
 __global__ __launch_bounds__(512) void qgemm_w4_wide(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     float* __restrict__ y, int M, int K, int N, int rsets, int workers, int tpw,
     VerifyArgs va) {
   using TR = ActTraits<ACT>;
+  constexpr int gs = GS;                            // group 64 << GS
   static_assert(TR::parts == 1, "16-bit activations only");
   constexpr int NW = 8, NT = 512, XB = 5;
   const bool fused = va.argmax != nullptr;           // uniform
@@ -571,9 +569,9 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(wq), (short)0, (unsigned)N * rowbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(scales), (short)0, (unsigned)N * G * 2, kBufferFlags);
+      const_cast<uint16_t*>(scales), (short)0, (unsigned)N * (G >> gs) * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(biases), (short)0, (unsigned)N * G * 2, kBufferFlags);
+      const_cast<uint16_t*>(biases), (short)0, (unsigned)N * (G >> gs) * 2, kBufferFlags);
 
   // ---- this wave's tiles and blocks: tile ordinal k is column tile
   // tbeg + wave + 8k; block (k, p) covers pairs p .. p + DB - 1.
@@ -608,9 +606,10 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
       const int u = r * 64 + lane;
       const int c = col0(k) + (8 * u) / G;
       const bool ok = k < ntile && u < tunits && c < N;
-      const unsigned off = ok ? 2u * ((unsigned)col0(k) * (unsigned)G + 8u * (unsigned)u) : kOutOfRange;
-      ts[r] = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
-      tb[r] = __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0);
+      const unsigned off =
+          ok ? 2u * (((unsigned)col0(k) * (unsigned)G + 8u * (unsigned)u) >> gs) : kOutOfRange;
+      ts[r] = sb_unit_load<GS>(sr, off);
+      tb[r] = sb_unit_load<GS>(br, off);
     }
   };
   auto tab_store = [&]() {
@@ -619,14 +618,7 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
       const int u = r * 64 + lane;
       if (u < tunits) {
         u32x4 lo, hi;
-        lo.x = __builtin_amdgcn_perm(tb[r].x, ts[r].x, 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(tb[r].x, ts[r].x, 0x07060302u);
-        lo.z = __builtin_amdgcn_perm(tb[r].y, ts[r].y, 0x05040100u);
-        lo.w = __builtin_amdgcn_perm(tb[r].y, ts[r].y, 0x07060302u);
-        hi.x = __builtin_amdgcn_perm(tb[r].z, ts[r].z, 0x05040100u);
-        hi.y = __builtin_amdgcn_perm(tb[r].z, ts[r].z, 0x07060302u);
-        hi.z = __builtin_amdgcn_perm(tb[r].w, ts[r].w, 0x05040100u);
-        hi.w = __builtin_amdgcn_perm(tb[r].w, ts[r].w, 0x07060302u);
+        sb_pairs<GS>(ts[r], tb[r], lo, hi);
         *reinterpret_cast<u32x4*>(tab + 8 * u) = lo;
         *reinterpret_cast<u32x4*>(tab + 8 * u + 4) = hi;
       }
@@ -841,7 +833,7 @@ constexpr int kM16XB = 5;
 template <int ACT, int DB, int RB, bool SWIGLU>
 hipError_t launch_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
                       const uint16_t* biases, float* y, int M, int K, int N, int cols,
-                      hipStream_t stream) {
+                      int gs, hipStream_t stream) {
   // One work-group per CU: rsets row sets of `workers` workers each (a
   // multiple of 8 when there are several row sets, for the XCD layout).
   const int rsets = (M + 15) / 16;
@@ -855,8 +847,11 @@ hipError_t launch_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
   const bool sbv = ((K >> 6) % 8) == 0 &&
                    ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(biases)) &
                     15) == 0;
-  auto kern = sbv ? qgemm_w4_m16<ACT, kM16Waves, kM16Tiles, DB, RB, D0, kM16XB, SWIGLU, true>
-                  : qgemm_w4_m16<ACT, kM16Waves, kM16Tiles, DB, RB, D0, kM16XB, SWIGLU, false>;
+  auto kern =
+      sbv ? (gs ? qgemm_w4_m16<ACT, kM16Waves, kM16Tiles, DB, RB, D0, kM16XB, SWIGLU, true, 1>
+                : qgemm_w4_m16<ACT, kM16Waves, kM16Tiles, DB, RB, D0, kM16XB, SWIGLU, true, 0>)
+          : (gs ? qgemm_w4_m16<ACT, kM16Waves, kM16Tiles, DB, RB, D0, kM16XB, SWIGLU, false, 1>
+                : qgemm_w4_m16<ACT, kM16Waves, kM16Tiles, DB, RB, D0, kM16XB, SWIGLU, false, 0>);
   if (L.total > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -872,25 +867,25 @@ hipError_t launch_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
 template <int ACT, bool SWIGLU>
 hipError_t launch_m16_blocks(const void* x, const uint8_t* wq, const uint16_t* scales,
                              const uint16_t* biases, float* y, int M, int K, int N,
-                             hipStream_t s) {
+                             int gs, hipStream_t s) {
   const int cus = device_cus();
   const int share = ((N + cus - 1) / cus + 3) / 4 * 4;
   const int cols = share < 16 * kM16Tiles ? share : 16 * kM16Tiles;
   const int GP = ((K >> 6) + 1) >> 1;
-  if (GP % 5 == 0) return launch_m16<ACT, 5, 1, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, s);
-  if (GP % 4 == 0) return launch_m16<ACT, 4, 2, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, s);
-  if (GP % 2 == 0) return launch_m16<ACT, 2, 4, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, s);
-  return launch_m16<ACT, 1, 8, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, s);
+  if (GP % 5 == 0) return launch_m16<ACT, 5, 1, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, gs, s);
+  if (GP % 4 == 0) return launch_m16<ACT, 4, 2, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, gs, s);
+  if (GP % 2 == 0) return launch_m16<ACT, 2, 4, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, gs, s);
+  return launch_m16<ACT, 1, 8, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, gs, s);
 }
 
 template <int ACT, int DB, int RB>
 hipError_t launch_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
                        const uint16_t* biases, float* y, int M, int K, int N, int rsets,
-                       int workers, const VerifyArgs& va, hipStream_t stream) {
+                       int workers, int gs, const VerifyArgs& va, hipStream_t stream) {
   const int G = K >> 6;
   const M16Layout L = m16_layout(G, 16, 8, 5);
   const int lds_bytes = L.sb + 8 * 16 * G * 4;
-  auto kern = qgemm_w4_wide<ACT, DB, RB>;
+  auto kern = gs ? qgemm_w4_wide<ACT, DB, RB, 1> : qgemm_w4_wide<ACT, DB, RB, 0>;
   if (lds_bytes > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -923,12 +918,13 @@ hipError_t launch_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
 //   its staging. Steps past a wave's tiles or past K read zeros.
 // * The work-group's tiles: [tbeg, tbeg + tpw); wave w takes tbeg + w + 8k.
 // Every sum runs in a fixed order, so results are deterministic.
-template <int ACT, int RS, int KT, int KCP>
+template <int ACT, int RS, int KT, int KCP, int GS>
 __global__ __launch_bounds__(512) void qgemm_w4_rows(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     float* __restrict__ y, int M, int K, int N, int tpw) {
   using TR = ActTraits<ACT>;
+  constexpr int gs = GS;                            // group 64 << GS
   static_assert(TR::parts == 1, "16-bit activations only");
   constexpr int NW = 8;
   constexpr int RH = RS >= 4 ? 1 : (RS < 2 ? RS : 2);  // row sets whose A stays in registers
@@ -965,9 +961,9 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(wq), (short)0, (unsigned)N * rowbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(scales), (short)0, (unsigned)N * G * 2, kBufferFlags);
+      const_cast<uint16_t*>(scales), (short)0, (unsigned)N * (G >> gs) * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(biases), (short)0, (unsigned)N * G * 2, kBufferFlags);
+      const_cast<uint16_t*>(biases), (short)0, (unsigned)N * (G >> gs) * 2, kBufferFlags);
 
   // This wave's tiles (uniform): tile k is tbeg + wave + 8k while below tend.
   int tile[KT];
@@ -1021,10 +1017,17 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
       const int k = e / (16 * KCP), jj = (e / KCP) % 16, d = e % KCP;
       const int col = (tbeg + wave + NW * k) * 16 + jj;
       const bool ok = e < TABD && tbeg + wave + NW * k < tend && col < N && c * KCP + d < GP;
-      const unsigned off = ok ? 2u * ((unsigned)col * (unsigned)G + (unsigned)(c * GC + 2 * d))
-                              : kOutOfRange;
-      ts[n] = __builtin_amdgcn_raw_buffer_load_b32(sr, off, 0, 0);
-      tb[n] = __builtin_amdgcn_raw_buffer_load_b32(br, off, 0, 0);
+      // Entries of groups 2d and 2d+1 of the chunk: one 32-bit load, or the
+      // one entry of their 128-group twice.
+      const unsigned e0 = ((unsigned)col * (unsigned)G + (unsigned)(c * GC + 2 * d)) >> gs;
+      const unsigned off = ok ? 2u * e0 : kOutOfRange;
+      if constexpr (GS == 0) {
+        ts[n] = __builtin_amdgcn_raw_buffer_load_b32(sr, off, 0, 0);
+        tb[n] = __builtin_amdgcn_raw_buffer_load_b32(br, off, 0, 0);
+      } else {
+        ts[n] = 0x10001u * (unsigned)__builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
+        tb[n] = 0x10001u * (unsigned)__builtin_amdgcn_raw_buffer_load_b16(br, off, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
@@ -1128,9 +1131,11 @@ constexpr int kRowsKCP = 5;
 
 template <int ACT, int RS>
 hipError_t launch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
-                       const uint16_t* biases, float* y, int M, int K, int N, hipStream_t stream) {
+                       const uint16_t* biases, float* y, int M, int K, int N, int gs,
+                       hipStream_t stream) {
   constexpr int lds_bytes = rows_lds_bytes<RS, kRowsKT, kRowsKCP>();
-  auto kern = qgemm_w4_rows<ACT, RS, kRowsKT, kRowsKCP>;
+  auto kern = gs ? qgemm_w4_rows<ACT, RS, kRowsKT, kRowsKCP, 1>
+                 : qgemm_w4_rows<ACT, RS, kRowsKT, kRowsKCP, 0>;
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
@@ -1153,18 +1158,18 @@ int wide_workers(int rsets) {
 
 template <int ACT>
 hipError_t launch_wide_any(const void* x, const uint8_t* wq, const uint16_t* scales,
-                           const uint16_t* biases, float* y, int M, int K, int N,
+                           const uint16_t* biases, float* y, int M, int K, int N, int gs,
                            const VerifyArgs& va, hipStream_t s) {
   const int rsets = (M + 15) / 16;
   const int workers = wide_workers(rsets);
   const int GP = (K >> 6) >> 1;
   if (GP % 5 == 0)
-    return launch_wide<ACT, 5, 1>(x, wq, scales, biases, y, M, K, N, rsets, workers, va, s);
+    return launch_wide<ACT, 5, 1>(x, wq, scales, biases, y, M, K, N, rsets, workers, gs, va, s);
   if (GP % 4 == 0)
-    return launch_wide<ACT, 4, 1>(x, wq, scales, biases, y, M, K, N, rsets, workers, va, s);
+    return launch_wide<ACT, 4, 1>(x, wq, scales, biases, y, M, K, N, rsets, workers, gs, va, s);
   if (GP % 2 == 0)
-    return launch_wide<ACT, 2, 4>(x, wq, scales, biases, y, M, K, N, rsets, workers, va, s);
-  return launch_wide<ACT, 1, 8>(x, wq, scales, biases, y, M, K, N, rsets, workers, va, s);
+    return launch_wide<ACT, 2, 4>(x, wq, scales, biases, y, M, K, N, rsets, workers, gs, va, s);
+  return launch_wide<ACT, 1, 8>(x, wq, scales, biases, y, M, K, N, rsets, workers, gs, va, s);
 }
 
 }  // namespace
@@ -1182,17 +1187,17 @@ bool qgemm_rows_fits(int M, int K, int N, int act) {
 
 hipError_t launch_qgemm_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                              const uint16_t* biases, float* y, int M, int K, int N, int act,
-                             hipStream_t stream) {
+                             int gs, hipStream_t stream) {
   const int rs = (M + 15) / 16;
   if (act == ACT_BF16) {
-    if (rs == 2) return launch_rows<ACT_BF16, 2>(x, wq, scales, biases, y, M, K, N, stream);
-    if (rs == 3) return launch_rows<ACT_BF16, 3>(x, wq, scales, biases, y, M, K, N, stream);
-    return launch_rows<ACT_BF16, 4>(x, wq, scales, biases, y, M, K, N, stream);
+    if (rs == 2) return launch_rows<ACT_BF16, 2>(x, wq, scales, biases, y, M, K, N, gs, stream);
+    if (rs == 3) return launch_rows<ACT_BF16, 3>(x, wq, scales, biases, y, M, K, N, gs, stream);
+    return launch_rows<ACT_BF16, 4>(x, wq, scales, biases, y, M, K, N, gs, stream);
   }
   if (act == ACT_FP16) {
-    if (rs == 2) return launch_rows<ACT_FP16, 2>(x, wq, scales, biases, y, M, K, N, stream);
-    if (rs == 3) return launch_rows<ACT_FP16, 3>(x, wq, scales, biases, y, M, K, N, stream);
-    return launch_rows<ACT_FP16, 4>(x, wq, scales, biases, y, M, K, N, stream);
+    if (rs == 2) return launch_rows<ACT_FP16, 2>(x, wq, scales, biases, y, M, K, N, gs, stream);
+    if (rs == 3) return launch_rows<ACT_FP16, 3>(x, wq, scales, biases, y, M, K, N, gs, stream);
+    return launch_rows<ACT_FP16, 4>(x, wq, scales, biases, y, M, K, N, gs, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -1211,11 +1216,11 @@ int qgemm_wide_groups(int M) { return wide_workers((M + 15) / 16) * ((M + 15) / 
 
 hipError_t launch_qgemm_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
                              const uint16_t* biases, float* y, int M, int K, int N, int act,
-                             const VerifyArgs& va, hipStream_t stream) {
+                             int gs, const VerifyArgs& va, hipStream_t stream) {
   if (act == ACT_BF16)
-    return launch_wide_any<ACT_BF16>(x, wq, scales, biases, y, M, K, N, va, stream);
+    return launch_wide_any<ACT_BF16>(x, wq, scales, biases, y, M, K, N, gs, va, stream);
   if (act == ACT_FP16)
-    return launch_wide_any<ACT_FP16>(x, wq, scales, biases, y, M, K, N, va, stream);
+    return launch_wide_any<ACT_FP16>(x, wq, scales, biases, y, M, K, N, gs, va, stream);
   return hipErrorInvalidValue;
 }
 
@@ -1234,23 +1239,23 @@ bool qgemm_swiglu_fused(int M, int K, int N, int act) {
 
 hipError_t launch_qgemm_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
                             const uint16_t* biases, float* y, int M, int K, int N, int act,
-                            hipStream_t stream) {
+                            int gs, hipStream_t stream) {
   if (act == ACT_BF16)
-    return launch_m16_blocks<ACT_BF16, false>(x, wq, scales, biases, y, M, K, N, stream);
+    return launch_m16_blocks<ACT_BF16, false>(x, wq, scales, biases, y, M, K, N, gs, stream);
   if (act == ACT_FP16)
-    return launch_m16_blocks<ACT_FP16, false>(x, wq, scales, biases, y, M, K, N, stream);
+    return launch_m16_blocks<ACT_FP16, false>(x, wq, scales, biases, y, M, K, N, gs, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_qgemm_swiglu(const void* x, const uint8_t* wq, const uint16_t* scales,
                                const uint16_t* biases, float* h, int M, int K, int N, int act,
-                               float* scratch_y, hipStream_t stream) {
+                               int gs, float* scratch_y, hipStream_t stream) {
   if (qgemm_swiglu_fused(M, K, N, act)) {
     if (act == ACT_BF16)
-      return launch_m16_blocks<ACT_BF16, true>(x, wq, scales, biases, h, M, K, N, stream);
-    return launch_m16_blocks<ACT_FP16, true>(x, wq, scales, biases, h, M, K, N, stream);
+      return launch_m16_blocks<ACT_BF16, true>(x, wq, scales, biases, h, M, K, N, gs, stream);
+    return launch_m16_blocks<ACT_FP16, true>(x, wq, scales, biases, h, M, K, N, gs, stream);
   }
-  hipError_t e = launch_qgemm(x, wq, scales, biases, scratch_y, M, K, N, act, stream);
+  hipError_t e = launch_qgemm(x, wq, scales, biases, scratch_y, M, K, N, act, gs, stream);
   if (e != hipSuccess) return e;
   const long long total = (long long)M * (N / 2);
   const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);

@@ -21,6 +21,9 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 int act_size(vqv_dtype a) { return a == VQV_FP32 ? 4 : 2; }
 
+// Group shift of a supported group size (64 << gs values per scale), or -1.
+int group_shift(int group) { return group == 64 ? 0 : group == 128 ? 1 : -1; }
+
 }  // namespace
 
 extern "C" {
@@ -31,7 +34,7 @@ const char* vqv_status_string(vqv_status s) {
   switch (s) {
     case VQV_OK: return "ok";
     case VQV_ERR_ARG: return "invalid argument (null pointer, size out of range or aliasing)";
-    case VQV_ERR_UNSUPPORTED: return "unsupported request (e.g. group size other than 64)";
+    case VQV_ERR_UNSUPPORTED: return "unsupported request (e.g. group size other than 64 or 128)";
     case VQV_ERR_ALIGN: return "pointer alignment requirement not met";
     case VQV_ERR_WORKSPACE: return "workspace missing or too small";
     case VQV_ERR_HIP: return "HIP runtime error at launch";
@@ -53,13 +56,14 @@ vqv_status vqv_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
   if (act_dtype != VQV_BF16 && act_dtype != VQV_FP16 && act_dtype != VQV_FP32)
     return VQV_ERR_ARG;
   if (M < 1 || M > kMaxRows || N < 1 || K < kGroup) return VQV_ERR_ARG;
-  if (group != kGroup) return VQV_ERR_UNSUPPORTED;
-  if (K % kGroup) return VQV_ERR_ARG;
+  const int gs = group_shift(group);
+  if (gs < 0) return VQV_ERR_UNSUPPORTED;
+  if (K % group) return VQV_ERR_ARG;
   if (K > vqv::kMaxK) return VQV_ERR_UNSUPPORTED;
   const size_t esz = (size_t)act_size(act_dtype);
   const size_t xbytes = (size_t)M * K * esz;
   const size_t wbytes = (size_t)N * (K / 2);
-  const size_t sbytes = (size_t)N * (K / kGroup) * 2;
+  const size_t sbytes = (size_t)N * (K / group) * 2;
   const size_t ybytes = (size_t)M * N * 4;
   if (xbytes >= (1ull << 31) || wbytes >= (1ull << 32) || (size_t)N * (K / kGroup) >= (1ull << 31))
     return VQV_ERR_UNSUPPORTED;
@@ -72,7 +76,7 @@ vqv_status vqv_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
   if (workspace_bytes < vqv_qgemm_workspace_bytes(M, K, N, group, act_dtype))
     return VQV_ERR_WORKSPACE;
   (void)hipGetLastError();  // start from a clean error state
-  const hipError_t e = vqv::launch_qgemm(x, wq, scales, biases, y, M, K, N, (int)act_dtype,
+  const hipError_t e = vqv::launch_qgemm(x, wq, scales, biases, y, M, K, N, (int)act_dtype, gs,
                                          static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? VQV_OK : VQV_ERR_HIP;
 }
@@ -85,7 +89,7 @@ constexpr size_t kHead = 256;
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 size_t vqv_qgemm_verify_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype) {
-  if (M < 1 || M > kMaxRows || N < 1 || K < kGroup || group != kGroup) return 0;
+  if (M < 1 || M > kMaxRows || N < 1 || K < kGroup || group_shift(group) < 0) return 0;
   const int groups = vqv::qgemm_verify_groups(M, K, N, (int)act_dtype);
   if (groups > 0) return kHead + (size_t)groups * 8 * 16;
   return kHead + align256((size_t)M * N * 4) + (size_t)M * vqv::verify_chunks(N) * 16;
@@ -113,13 +117,14 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
   if (M < 1 || M > kMaxRows || N < 1 || K < kGroup) return VQV_ERR_ARG;
   if (B < 1 || T < 1 || T > kMaxBlock || (long long)B * T != M) return VQV_ERR_ARG;
   if (T > 1 && !draft) return VQV_ERR_ARG;
-  if (group != kGroup) return VQV_ERR_UNSUPPORTED;
-  if (K % kGroup) return VQV_ERR_ARG;
+  const int gs = group_shift(group);
+  if (gs < 0) return VQV_ERR_UNSUPPORTED;
+  if (K % group) return VQV_ERR_ARG;
   if (K > vqv::kMaxK) return VQV_ERR_UNSUPPORTED;
   const size_t esz = (size_t)act_size(act_dtype);
   const size_t xbytes = (size_t)M * K * esz;
   const size_t wbytes = (size_t)N * (K / 2);
-  const size_t sbytes = (size_t)N * (K / kGroup) * 2;
+  const size_t sbytes = (size_t)N * (K / group) * 2;
   const size_t ybytes = (size_t)M * N * 4;
   if (xbytes >= (1ull << 31) || wbytes >= (1ull << 32) || (size_t)N * (K / kGroup) >= (1ull << 31) ||
       ybytes >= (1ull << 31))
@@ -150,18 +155,19 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
                      reinterpret_cast<uint4*>(ws + kHead)};
   hipError_t e;
   if (vqv::qgemm_verify_groups(M, K, N, (int)act_dtype) > 0) {
-    e = vqv::launch_qgemm_verify(x, wq, scales, biases, y, M, K, N, (int)act_dtype, va, st);
+    e = vqv::launch_qgemm_verify(x, wq, scales, biases, y, M, K, N, (int)act_dtype, gs, va, st);
   } else {
     float* logits = y ? y : reinterpret_cast<float*>(ws + kHead);
     va.partials = reinterpret_cast<uint4*>(ws + kHead + align256(ybytes));
-    e = vqv::launch_qgemm(x, wq, scales, biases, logits, M, K, N, (int)act_dtype, st);
+    e = vqv::launch_qgemm(x, wq, scales, biases, logits, M, K, N, (int)act_dtype, gs, st);
     if (e == hipSuccess) e = vqv::launch_verify(logits, N, va, st);
   }
   return e == hipSuccess ? VQV_OK : VQV_ERR_HIP;
 }
 
 size_t vqv_qgemm_swiglu_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype) {
-  if (M < 1 || M > kMaxRows || N < 2 || (N & 1) || K < kGroup || group != kGroup) return 0;
+  if (M < 1 || M > kMaxRows || N < 2 || (N & 1) || K < kGroup || group_shift(group) < 0)
+    return 0;
   if (vqv::qgemm_swiglu_fused(M, K, N, (int)act_dtype)) return 0;
   return align256((size_t)M * N * 4);  // the stacked gate/up output
 }
@@ -174,13 +180,14 @@ vqv_status vqv_qgemm_swiglu(const void* x, const uint8_t* wq, const uint16_t* sc
   if (act_dtype != VQV_BF16 && act_dtype != VQV_FP16 && act_dtype != VQV_FP32)
     return VQV_ERR_ARG;
   if (M < 1 || M > kMaxRows || N < 2 || (N & 1) || K < kGroup) return VQV_ERR_ARG;
-  if (group != kGroup) return VQV_ERR_UNSUPPORTED;
-  if (K % kGroup) return VQV_ERR_ARG;
+  const int gs = group_shift(group);
+  if (gs < 0) return VQV_ERR_UNSUPPORTED;
+  if (K % group) return VQV_ERR_ARG;
   if (K > vqv::kMaxK) return VQV_ERR_UNSUPPORTED;
   const size_t esz = (size_t)act_size(act_dtype);
   const size_t xbytes = (size_t)M * K * esz;
   const size_t wbytes = (size_t)N * (K / 2);
-  const size_t sbytes = (size_t)N * (K / kGroup) * 2;
+  const size_t sbytes = (size_t)N * (K / group) * 2;
   const size_t hbytes = (size_t)M * (N / 2) * 4;
   if (xbytes >= (1ull << 31) || wbytes >= (1ull << 32) || (size_t)N * (K / kGroup) >= (1ull << 31) ||
       (size_t)M * N * 4 >= (1ull << 31))
@@ -200,7 +207,7 @@ vqv_status vqv_qgemm_swiglu(const void* x, const uint8_t* wq, const uint16_t* sc
   if (need && overlaps(h, hbytes, workspace, need)) return VQV_ERR_ARG;
   (void)hipGetLastError();
   const hipError_t e = vqv::launch_qgemm_swiglu(x, wq, scales, biases, h, M, K, N,
-                                                (int)act_dtype, static_cast<float*>(workspace),
+                                                (int)act_dtype, gs, static_cast<float*>(workspace),
                                                 static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? VQV_OK : VQV_ERR_HIP;
 }

@@ -13,9 +13,12 @@ enum ActKind { ACT_BF16 = 0, ACT_FP16 = 1, ACT_FP32 = 2 };
 // Largest K: a work-group keeps its columns' scale/bias rows in LDS.
 constexpr int kMaxK = 16384;
 
-// y[M,N] = x[M,K] . W^T for 1 <= M <= 64, 64 <= K <= kMaxK, K % 64 == 0, group 64.
+// y[M,N] = x[M,K] . W^T for 1 <= M <= 64, 64 <= K <= kMaxK, K % 64 == 0.
+// Every launcher takes the group shift gs: scales and biases hold one entry
+// per 64 << gs values of a row (gs = 0: group 64; gs = 1: group 128, which
+// needs K % 128 == 0).
 hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
-                        const uint16_t* biases, float* y, int M, int K, int N, int act,
+                        const uint16_t* biases, float* y, int M, int K, int N, int act, int gs,
                         hipStream_t stream);
 
 // Greedy verify fused into the projection's epilogue (M = B*T <= 8, 16-bit
@@ -44,7 +47,7 @@ int qgemm_verify_groups(int M, int K, int N, int act);
 
 hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* scales,
                                const uint16_t* biases, float* y, int M, int K, int N, int act,
-                               const VerifyArgs& va, hipStream_t stream);
+                               int gs, const VerifyArgs& va, hipStream_t stream);
 
 // 9..64 rows in row sets of 16 (bf16/fp16, K within the kernel's LDS
 // budget): qgemm_w4_m16 (qgemm_m16.hip). Whether it takes the problem, and
@@ -52,7 +55,7 @@ hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t*
 bool qgemm_m16_fits(int M, int K, int act);
 hipError_t launch_qgemm_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
                             const uint16_t* biases, float* y, int M, int K, int N, int act,
-                            hipStream_t stream);
+                            int gs, hipStream_t stream);
 
 // Wide outputs (at least two column tiles per wave of one work-group per
 // CU): qgemm_w4_wide (qgemm_m16.hip), waves own whole tiles over all of K.
@@ -63,12 +66,12 @@ hipError_t launch_qgemm_m16(const void* x, const uint8_t* wq, const uint16_t* sc
 bool qgemm_rows_fits(int M, int K, int N, int act);
 hipError_t launch_qgemm_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                              const uint16_t* biases, float* y, int M, int K, int N, int act,
-                             hipStream_t stream);
+                             int gs, hipStream_t stream);
 bool qgemm_wide_fits(int M, int K, int N, int act);
 int qgemm_wide_groups(int M);
 hipError_t launch_qgemm_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
                              const uint16_t* biases, float* y, int M, int K, int N, int act,
-                             const VerifyArgs& va, hipStream_t stream);
+                             int gs, const VerifyArgs& va, hipStream_t stream);
 
 // h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:] of y = x . W^T, W the stacked
 // gate/up weight [N, K]. Fused into the 16-row kernel when
@@ -77,7 +80,7 @@ hipError_t launch_qgemm_wide(const void* x, const uint8_t* wq, const uint16_t* s
 bool qgemm_swiglu_fused(int M, int K, int N, int act);
 hipError_t launch_qgemm_swiglu(const void* x, const uint8_t* wq, const uint16_t* scales,
                                const uint16_t* biases, float* h, int M, int K, int N, int act,
-                               float* scratch_y, hipStream_t stream);
+                               int gs, float* scratch_y, hipStream_t stream);
 
 // Logits per verify work-group (one row, one chunk of columns).
 constexpr int kVerifyChunk = 4096;

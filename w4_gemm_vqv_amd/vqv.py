@@ -91,6 +91,20 @@ def _dev(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
+def _check_weight(wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, K: int,
+                  group: int) -> None:
+    """The library reads N*K/2 code bytes and N*K/group table entries: the
+    tensors must hold that much."""
+    rows = wq.shape[0]
+    if wq.numel() * wq.element_size() != rows * (K // 2):
+        raise ValueError(f"wq must hold [N, K/2] = [{rows}, {K // 2}] bytes")
+    if group > 0 and K % group == 0:
+        for t, name in ((scales, "scales"), (biases, "biases")):
+            if t.numel() != rows * (K // group) or t.element_size() != 2:
+                raise ValueError(f"{name} must hold [N, K/group] = [{rows}, {K // group}] "
+                                 "16-bit entries")
+
+
 def vqv_abi_version() -> int:
     return lib().vqv_abi_version()
 
@@ -113,6 +127,7 @@ def vqv_qgemm(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: t
         raise ValueError(f"unsupported activation dtype {x.dtype}")
     M, K = x.shape
     N = wq.shape[0]
+    _check_weight(wq, scales, biases, K, group)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
     act = _DTYPES[x.dtype]
@@ -199,6 +214,7 @@ def vqv_qgemm_verify(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor,
         raise ValueError(f"unsupported activation dtype {x.dtype}")
     M, K = x.shape
     N = wq.shape[0]
+    _check_weight(wq, scales, biases, K, group)
     dev = x.device
     act = _DTYPES[x.dtype]
     if y is None and want_y:
@@ -234,6 +250,7 @@ def vqv_qgemm_verify_ex(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor,
         raise ValueError(f"unsupported activation dtype {x.dtype}")
     M, K = x.shape
     N = wq.shape[0]
+    _check_weight(wq, scales, biases, K, group)
     dev = x.device
     act = _DTYPES[x.dtype]
     if y is None and want_y:
@@ -273,6 +290,7 @@ def vqv_qgemm_swiglu(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor,
         raise ValueError(f"unsupported activation dtype {x.dtype}")
     M, K = x.shape
     N = wq.shape[0]
+    _check_weight(wq, scales, biases, K, group)
     act = _DTYPES[x.dtype]
     if h is None:
         h = torch.empty((M, N // 2), dtype=torch.float32, device=x.device)
