@@ -34,7 +34,7 @@ Sources on the pages:
 Where the pages are silent the readings are: little-endian nibbles (even k
 in the low nibble), W stored as [N, K] with K contiguous ("K-major"), an
 affine w = s*q + b with fp16 scale and bias per group of 64 contiguous k
-(128 taken as the other group size, with the same layout),
+(32 and 128 taken as the other group sizes, with the same layout),
 NaN-first argmax with a lowest-index tie break, and accept_len counting the
 accepted drafts only (0..T-1). Every function here is pinned by tests that do
 not reuse its code (brute force, closed forms, library argmax, hand walks).

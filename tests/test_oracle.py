@@ -83,6 +83,43 @@ def test_brute_force_tiny_group128(act, M, K, N, seed):
             assert abs(y[m, n] - e) <= 1e-12 * (1.0 + abs(e)), (m, n, y[m, n], e)
 
 
+@pytest.mark.parametrize("act", ["bf16", "fp32"])
+@pytest.mark.parametrize("M,K,N,seed", [(1, 64, 2, 24), (2, 192, 3, 25)])
+def test_brute_force_tiny_group32(act, M, K, N, seed):
+    """Group 32: one scale and bias per 32 contiguous k."""
+    rng = np.random.default_rng(seed)
+    wq, s, b = gen.make_weights(rng, N, K, group=32)
+    assert s.shape == (N, K // 32)
+    x = gen.make_x(rng, M, K, act)
+    y = qgemm_ref(x, act, wq, s, b, group=32)
+    exact = _brute_qgemm(x, act, wq, s, b, M, K, N, group=32)
+    for m in range(M):
+        for n in range(N):
+            e = float(exact[m][n])
+            assert abs(y[m, n] - e) <= 1e-12 * (1.0 + abs(e)), (m, n, y[m, n], e)
+
+
+def test_group64_is_group32_with_equal_halves():
+    """Group 32 with both halves of every 64-group sharing one entry is group 64."""
+    rng = np.random.default_rng(26)
+    wq, s, b = gen.make_weights(rng, 7, 384, group=64)
+    x = gen.make_x(rng, 3, 384, "fp16")
+    y64 = qgemm_ref(x, "fp16", wq, s, b, group=64)
+    y32 = qgemm_ref(x, "fp16", wq, np.repeat(s, 2, axis=1), np.repeat(b, 2, axis=1), group=32)
+    np.testing.assert_allclose(y32, y64, rtol=1e-13, atol=1e-13)
+
+
+def test_dequantize_group32_boundary():
+    """k=31 and k=32 sit in different 32-groups."""
+    wq = np.full((1, 32), 0x22, dtype=np.uint8)  # every code 2
+    s = np.array([[np.float16(0.5).view(np.uint16), np.float16(4.0).view(np.uint16)]],
+                 dtype=np.uint16)
+    b = np.array([[np.float16(1.0).view(np.uint16), np.float16(-2.0).view(np.uint16)]],
+                 dtype=np.uint16)
+    w = dequantize(wq, s, b, group=32)
+    assert w[0, 0] == 2.0 and w[0, 31] == 2.0 and w[0, 32] == 6.0 and w[0, 63] == 6.0
+
+
 def test_group128_is_group64_with_each_entry_twice():
     """A 128-group's scale and bias cover both of its 64-halves."""
     rng = np.random.default_rng(22)
