@@ -2,7 +2,7 @@
 """Throughput of the W4 verify projection + greedy verify on one MI355X.
 
 One step is the whole hot path over one verify block: the W4 QMM (group 64,
-or 128 with --group 128) y[M,N] = x[M,K] . W^T, then the per-row argmax and accept walk over y. By
+or 32 / 128 with --group) y[M,N] = x[M,K] . W^T, then the per-row argmax and accept walk over y. By
 default a step is one vqv_qgemm_verify call (the argmax fused into the QMM
 epilogue, a one-work-group kernel finishing the rows and the walk); with
 --path separate it is vqv_qgemm followed by vqv_verify; with --path swiglu
@@ -62,12 +62,12 @@ def qgemm_bytes(M, K, N, esz, group=64):
 KERNEL_SOURCES = ("qgemm.hip", "qgemm_common.h", "qgemm_m16.hip")
 
 
-def projection_kernel(M, K, N, act, cus):
+def projection_kernel(M, K, N, act, cus, group=64):
     """Name of the projection kernel the library launches for this shape (the
     order of the library's dispatch; a label for the bench line only)."""
     G, T = K // 64, (N + 15) // 16
     rsets = (M + 15) // 16
-    if act == "fp32":
+    if act == "fp32" or group == 32:
         return "qgemm_w4"
     tpw = (T + cus - 1) // cus
     if 16 < M <= 64 and K % 128 == 0 and N * (K // 2) < 0x7F000000 and 8 <= tpw <= 40:
@@ -231,7 +231,7 @@ def main():
                     choices=["tiny", "target", "draft_w4a32", "vocab_verify", "batched_vocab",
                              "gate_up"])
     ap.add_argument("--m", type=int, default=None, help="rows (default: the workload's M)")
-    ap.add_argument("--group", type=int, choices=[64, 128], default=64,
+    ap.add_argument("--group", type=int, choices=[32, 64, 128], default=64,
                     help="k per scale and bias (the workloads are quoted at 64)")
     ap.add_argument("--rotate", type=int, default=None, help="weight copies cycled per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -309,6 +309,10 @@ def main():
         fws = torch.zeros(vqv.vqv_qgemm_verify_workspace_bytes(M, K, N, group, vqv_act),
                           dtype=torch.uint8, device=dev)
     use_fused = fused_ok and args.path == "fused"
+    # The call fuses the argmax into the projection's epilogue when its
+    # workspace holds only per-group partials; otherwise (M > 8, fp32
+    # activations, group 32) it runs the projection and the two-stage verify.
+    epilogue_fused = use_fused and fws.numel() < M * N * 4
     use_swiglu = args.path == "swiglu"
     if use_swiglu:
         if T or N % 2:
@@ -463,7 +467,7 @@ def main():
     # epilogue, 8 bytes per row and work-group, and is timed with the finish
     # kernel in fused_us_mean).
     k_us = q_mean
-    kname = projection_kernel(M, K, N, act, props.multi_processor_count)
+    kname = projection_kernel(M, K, N, act, props.multi_processor_count, group)
     if use_swiglu:
         # The step's kernel is the projection with the SwiGLU epilogue: it
         # writes h [M, N/2] instead of y [M, N].
@@ -487,7 +491,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: W4 group-{group} QMM M={M} K={K} N={N} {act} "
                                + (f"+ greedy verify B={B} T={T}" if T else "(no verify)")
-                               + (" (verify fused into the QMM epilogue)" if use_fused else "")
+                               + (" (verify fused into the QMM epilogue)" if epilogue_fused
+                                  else " (one vqv_qgemm_verify call: projection, then the "
+                                       "two-stage verify)" if use_fused else "")
                                + (" with the SwiGLU epilogue, h[M, N/2]" if use_swiglu else ""),
                    "M": M, "K": K, "N": N, "group": group, "act": act, "verify_B": B,
                    "verify_T": T, "weight_copies": R},

@@ -76,7 +76,9 @@ def test_fused_workspace_queries(L):
     assert fallback >= head + 16 * 1000 * 4  # room for the logits
     assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 64, FP32) >= head + 8 * 1000 * 4
     assert L.vqv_qgemm_verify_workspace_bytes(0, 512, 1000, 64, BF16) == 0
-    assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 32, BF16) == 0
+    assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 16, BF16) == 0
+    # group 32 has no fused kernel: room for the logits
+    assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 32, BF16) >= head + 8 * 1000 * 4
     # group 128 takes the same paths as group 64
     assert (L.vqv_qgemm_verify_workspace_bytes(8, 5120, 17408, 128, BF16) ==
             L.vqv_qgemm_verify_workspace_bytes(8, 5120, 17408, 64, BF16))
@@ -94,7 +96,8 @@ def q(L, x=X, wq=W, s=S, b=B_, y=Y, M=8, K=512, N=1024, group=64, act=BF16, ws=N
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), ARG), (dict(wq=None), ARG), (dict(s=None), ARG), (dict(b=None), ARG),
     (dict(y=None), ARG), (dict(M=0), ARG), (dict(M=65), ARG), (dict(N=0), ARG), (dict(K=0), ARG),
-    (dict(K=32), ARG), (dict(K=100), ARG), (dict(group=32), UNSUP), (dict(group=256), UNSUP),
+    (dict(K=32), ARG), (dict(K=100), ARG), (dict(group=16), UNSUP), (dict(group=256), UNSUP),
+    (dict(group=32, K=96), UNSUP), (dict(group=32, K=8192 + 64), UNSUP),
     (dict(group=128, K=192), ARG), (dict(group=128, s=S + 1), ALIGN),
     (dict(act=3), ARG), (dict(act=-1), ARG), (dict(x=X + 8), ALIGN), (dict(wq=W + 4), ALIGN),
     (dict(s=S + 1), ALIGN), (dict(y=Y + 2), ALIGN), (dict(y=X), ARG), (dict(y=W + 64), ARG),
@@ -124,7 +127,7 @@ DR, AM, AC = 0x70000000, 0x80000000, 0x90000000
 
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), ARG), (dict(am=None), ARG), (dict(ac=None), ARG), (dict(dr=None), ARG),
-    (dict(B=2), ARG), (dict(T=4), ARG), (dict(M=65, B=65, T=1), ARG), (dict(group=32), UNSUP),
+    (dict(B=2), ARG), (dict(T=4), ARG), (dict(M=65, B=65, T=1), ARG), (dict(group=16), UNSUP),
     (dict(group=128, K=320), ARG),
     (dict(K=100), ARG), (dict(y=Y + 4), ALIGN), (dict(am=AM + 2), ALIGN), (dict(ws=None), WS),
     (dict(wsb=8), WS), (dict(ws=WSP + 16), WS), (dict(am=X), ARG), (dict(ws=W), ARG),
@@ -180,7 +183,8 @@ def test_swiglu_workspace_queries(L):
     assert L.vqv_qgemm_swiglu_workspace_bytes(16, 5120, 1000, 64, BF16) >= 16 * 1000 * 4
     # invalid: odd N, group, M
     assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1001, 64, BF16) == 0
-    assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1000, 32, BF16) == 0
+    assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1000, 16, BF16) == 0
+    assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1000, 32, BF16) >= 16 * 1000 * 4
     assert L.vqv_qgemm_swiglu_workspace_bytes(64, 512, 1000, 128, BF16) == 0
     assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1000, 256, BF16) == 0
     assert L.vqv_qgemm_swiglu_workspace_bytes(0, 512, 1000, 64, BF16) == 0
@@ -188,7 +192,7 @@ def test_swiglu_workspace_queries(L):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), ARG), (dict(h=None), ARG), (dict(N=1001), ARG), (dict(N=0), ARG),
-    (dict(M=65), ARG), (dict(K=100), ARG), (dict(group=32), UNSUP), (dict(act=3), ARG),
+    (dict(M=65), ARG), (dict(K=100), ARG), (dict(group=16), UNSUP), (dict(act=3), ARG),
     (dict(group=128, K=448), ARG),
     (dict(x=X + 8), ALIGN), (dict(h=Y + 2), ALIGN), (dict(h=X), ARG), (dict(h=W + 64), ARG),
     (dict(h=S), ARG), (dict(K=16384 + 64), UNSUP),
@@ -234,7 +238,7 @@ def test_rejected_calls_write_nothing():
     wq = torch.zeros(1024, 256, dtype=torch.uint8, device="cuda")
     s = torch.zeros(1024, 8, dtype=torch.float16, device="cuda")
     y = torch.full((8, 1024), 7.0, device="cuda")
-    for M, K, group in [(0, 512, 64), (8, 512, 32), (8, 500, 64)]:
+    for M, K, group in [(0, 512, 64), (8, 512, 16), (8, 500, 64), (8, 96, 32)]:
         st = Lg.vqv_qgemm(x.data_ptr(), wq.data_ptr(), s.data_ptr(), s.data_ptr(), y.data_ptr(),
                           M, K, 1024, group, BF16, None, 0, None)
         assert st != OK

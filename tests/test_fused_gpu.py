@@ -102,6 +102,18 @@ def test_group128_matches_separate(vqv, M, K, N, act, B, T):
     assert_close(y.cpu().numpy(), ref, act, f"group 128 fused M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("M,K,N,act,B,T", [
+    (8, 512, 1024, "bf16", 1, 8), (8, 5120, 17408, "bf16", 1, 8), (4, 1280, 3000, "fp16", 2, 2),
+    (16, 512, 1000, "fp32", 1, 16),
+])
+def test_group32_matches_separate(vqv, M, K, N, act, B, T):
+    """Group 32 has no fused kernel: the call takes the two-kernel path."""
+    c = case(M, K, N, act, seed=M * 13 + K + N, group=32)
+    y, _, _ = compare(vqv, c, B, T)
+    ref = qgemm_ref(c["x"], act, c["wq"], c["scales"], c["biases"], group=32)
+    assert_close(y.cpu().numpy(), ref, act, f"group 32 fused M={M} K={K} N={N}")
+
+
 def test_without_logits(vqv):
     c = case(8, 1024, 4000, "bf16", seed=21)
     y, a, l = compare(vqv, c, 1, 8, want_y=False)

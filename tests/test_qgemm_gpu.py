@@ -109,6 +109,65 @@ def test_group128_equals_group64_twice(vqv, act, M, K, N):
     np.testing.assert_array_equal(y128, run(vqv, c64))
 
 
+# Group 32 runs on the generic kernel in every configuration its dispatch
+# takes: one row set with the whole K range staged (64-80 column shares and
+# wide N), narrow outputs, chunked staging at large K, two, four and eight row
+# sets, the small fallbacks, and an odd count of 64-groups.
+SHAPES_G32 = [
+    (8, 5120, 17408), (8, 5120, 1024), (1, 640, 300), (4, 1280, 30000), (5, 192, 65),
+    (8, 8192, 300), (16, 640, 300), (12, 8192, 100), (9, 448, 777), (32, 256, 96),
+    (20, 1280, 500), (64, 512, 130), (40, 8192, 70), (64, 64, 99),
+]
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("M,K,N", SHAPES_G32)
+def test_parity_group32(vqv, act, M, K, N):
+    c = case(M, K, N, act, seed=M * 1000 + K + N + 32, group=32)
+    y = run(vqv, c)
+    ref = qgemm_ref(c["x"], act, c["wq"], c["scales"], c["biases"], group=32)
+    assert_close(y, ref, act, f"group 32 M={M} K={K} N={N} {act}")
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("M,K,N", [(8, 512, 1024), (3, 192, 37), (16, 1280, 96), (64, 256, 40)])
+def test_integer_case_bit_exact_group32(vqv, act, M, K, N):
+    """Integer-exact inputs with one scale and bias per 32 k, the two halves
+    of a 64-group given different biases: bit for bit against the oracle."""
+    rng = np.random.default_rng(27 + M + K + N)
+    wq = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    G = K // 32
+    s = np.full((N, G), np.float16(1.0).view(np.uint16), dtype=np.uint16)
+    b = rng.integers(-8, 1, size=(N, G)).astype(np.float16).view(np.uint16)
+    xi = rng.integers(-8, 9, size=(M, K)).astype(np.float32)
+    x = {"bf16": lambda: gen.f32_to_bf16_bits(xi), "fp16": lambda: xi.astype(np.float16).view(np.uint16),
+         "fp32": lambda: xi}[act]()
+    c = dict(M=M, K=K, N=N, act=act, wq=wq, scales=s, biases=b, x=x, group=32)
+    np.testing.assert_array_equal(run(vqv, c), qgemm_ref(x, act, wq, s, b, group=32)
+                                  .astype(np.float32))
+
+
+def test_group32_halves_use_their_own_scale(vqv):
+    """Scale 1 on the first 32-k half of every group and 0 on the second, zero
+    biases: y is the product over the first halves only."""
+    M, K, N = 8, 512, 200
+    rng = np.random.default_rng(28)
+    wq = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    s = np.zeros((N, K // 32), dtype=np.float16)
+    s[:, 0::2] = 1.0
+    s = s.view(np.uint16)
+    b = np.zeros((N, K // 32), dtype=np.uint16)
+    xi = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+    x = gen.f32_to_bf16_bits(xi)
+    c = dict(M=M, K=K, N=N, act="bf16", wq=wq, scales=s, biases=b, x=x, group=32)
+    y = run(vqv, c)
+    q = np.empty((N, K), np.float64)
+    q[:, 0::2] = wq & 15
+    q[:, 1::2] = wq >> 4
+    first = (np.arange(K) // 32) % 2 == 0
+    np.testing.assert_array_equal(y, (xi[:, first] @ q[:, first].T).astype(np.float32))
+
+
 @pytest.mark.parametrize("act", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("M,K,N", [(8, 512, 1024), (3, 384, 37), (16, 1280, 96), (64, 256, 40)])
 def test_integer_case_bit_exact_group128(vqv, act, M, K, N):

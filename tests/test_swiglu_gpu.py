@@ -100,6 +100,15 @@ def test_swiglu_group128(vqv, M, K, N, act):
     assert_swiglu_close(h, g, u, ref, act, f"group 128 M={M} K={K} N={N} {act}")
 
 
+@pytest.mark.parametrize("M,K,N,act", [(16, 512, 2 * 1000, "bf16"), (9, 192, 2 * 77, "fp16"),
+                                        (40, 1280, 2 * 150, "fp32")])
+def test_swiglu_group32(vqv, M, K, N, act):
+    c = case(M, K, N, act, seed=M * 100 + K + N + 32, group=32)
+    h = run(vqv, c)
+    g, u, ref = gate_up_ref(c)
+    assert_swiglu_close(h, g, u, ref, act, f"group 32 M={M} K={K} N={N} {act}")
+
+
 def test_fused_workspace_is_zero(vqv):
     assert vqv.vqv_qgemm_swiglu_workspace_bytes(16, 2560, 18432, 64, vqv.VQV_BF16) == 0
     assert vqv.vqv_qgemm_swiglu_workspace_bytes(64, 2560, 18432, 64, vqv.VQV_BF16) == 0

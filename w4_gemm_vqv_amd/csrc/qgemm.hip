@@ -96,7 +96,8 @@ struct LdsLayout {
   int xl, xs, sb, total, sbs, zimg, zxs;
 };
 
-template <int R, int P, int WK, int KC, int WGC, bool XALL>
+// HV (group 32): row sums and table entries per 32-k half, twice as many.
+template <int R, int P, int WK, int KC, int WGC, bool XALL, bool HV>
 __host__ __device__ inline LdsLayout lds_layout(int G) {
   LdsLayout L{};
   const int GP = (G + 1) >> 1;
@@ -107,8 +108,8 @@ __host__ __device__ inline LdsLayout lds_layout(int G) {
   L.zimg = XALL ? WK * S * R * P : 0;      // index of the zero image (XALL)
   L.xs = nimg * kPairBytes;
   L.zxs = XALL ? WK * S * R : 0;           // index of the zero row-sum group (XALL)
-  L.sb = L.xs + nxs * 16 * 4;
-  L.sbs = G + 4;
+  L.sb = L.xs + nxs * (HV ? 32 : 16) * 4;
+  L.sbs = (HV ? 2 * G : G) + 4;
   L.total = L.sb + WGC * L.sbs * 4;
   return L;
 }
@@ -119,7 +120,12 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     float* __restrict__ y, int M, int K, int N, int cols) {
   using TR = ActTraits<ACT>;
-  constexpr int gs = GS;                            // group 64 << GS
+  // GS: group 64 << GS for GS >= 0; GS = -1 is group 32, a scale and bias
+  // per 32-k half: each step's MFMAs run once per half (the other half's
+  // A slots masked to zero) and each half gets its own epilogue.
+  constexpr int gs = GS > 0 ? GS : 0;               // table shift of group 128
+  constexpr bool HV = GS < 0;
+  constexpr int XSF = HV ? 32 : 16;                 // row sums per image group
   constexpr int P = TR::parts;
   constexpr int NT = 64 * WN * WK;                  // threads
   constexpr int WCOLS = 16 * TILES;                 // columns per wave
@@ -146,7 +152,9 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
   const int S = (GP + WK - 1) / WK;                  // steps per K range
   const bool oddg = (G & 1) != 0;
   const unsigned rowbytes = (unsigned)K >> 1;
-  const LdsLayout L = lds_layout<R, P, WK, KC, WGC, XALL>(G);
+  const LdsLayout L = lds_layout<R, P, WK, KC, WGC, XALL, HV>(G);
+  const int TG = HV ? 2 * G : G;                     // LDS table entries per column
+  const int ME = HV ? 2 * G : (G >> gs);             // table entries per column in memory
   unsigned char* xl = lds + L.xl;
   float* xsl = reinterpret_cast<float*>(lds + L.xs);
   unsigned* sbl = reinterpret_cast<unsigned*>(lds + L.sb);
@@ -165,11 +173,9 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
       const_cast<uint8_t*>(wq) + (size_t)wg0 * rowbytes, (short)0, wgcols * rowbytes,
       kBufferFlags);
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(scales) + (size_t)wg0 * (G >> gs), (short)0, wgcols * (G >> gs) * 2,
-      kBufferFlags);
+      const_cast<uint16_t*>(scales) + (size_t)wg0 * ME, (short)0, wgcols * ME * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(biases) + (size_t)wg0 * (G >> gs), (short)0, wgcols * (G >> gs) * 2,
-      kBufferFlags);
+      const_cast<uint16_t*>(biases) + (size_t)wg0 * ME, (short)0, wgcols * ME * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(x), (short)0, M * K * TR::esz, kBufferFlags);
 
@@ -183,11 +189,12 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
   const int aslot = a_lane ? (h * 8 + (j & 7)) : 32; // the zero slot for idle lanes
 
   // ---- scale/bias table: issued first, written to LDS after the prologue.
-  // Vector path (K/64 a multiple of 8, 16-byte aligned bases): 16-byte units
-  // of the work-group's contiguous block; otherwise 16-bit loads.
-  const bool sb_vec = (G % 8) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
-                                        reinterpret_cast<uintptr_t>(biases)) & 15) == 0;
-  const int sb_units = sb_vec ? wgcols * G / 8 : wgcols * G;
+  // Vector path (LDS entries per column a multiple of 8, 16-byte aligned
+  // bases): 16-byte units of the work-group's contiguous block; otherwise
+  // 16-bit loads.
+  const bool sb_vec = (TG % 8) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
+                                         reinterpret_cast<uintptr_t>(biases)) & 15) == 0;
+  const int sb_units = sb_vec ? wgcols * TG / 8 : wgcols * TG;
   u32x4 sbs[SBU], sbb[SBU];
   auto sb_load = [&](int round) {
 #pragma unroll
@@ -211,13 +218,13 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
       if (i < sb_units) {
         if (sb_vec) {
           const int e0 = 8 * i;                       // first element of the unit
-          const int n = e0 / G, g = e0 - n * G;
+          const int n = e0 / TG, g = e0 - n * TG;
           u32x4 lo, hi;                               // (s_g | b_g << 16) for g .. g+7
           sb_pairs<GS>(sbs[u], sbb[u], lo, hi);
           *reinterpret_cast<u32x4*>(&sbl[n * L.sbs + g]) = lo;
           *reinterpret_cast<u32x4*>(&sbl[n * L.sbs + g + 4]) = hi;
         } else {
-          const int n = i / G, g = i - n * G;
+          const int n = i / TG, g = i - n * TG;
           sbl[n * L.sbs + g] = (sbs[u].x & 0xFFFFu) | (sbb[u].x << 16);
         }
       }
@@ -278,8 +285,8 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
           for (int e = 0; e < 4; ++e) s8 += __uint_as_float(sreg[set][i][v][e]);
       }
       s8 += __shfl_xor(s8, 1);
-      s8 += __shfl_xor(s8, 2);
-      s8 += __shfl_xor(s8, 4);
+      s8 += __shfl_xor(s8, 2);                        // a 32-k half: 4 lanes
+      if constexpr (!HV) s8 += __shfl_xor(s8, 4);     // a 64-group: 8 lanes
       if (bi < cblocks) {
         const int grp = ((buf * WK + ks) * csteps + pp) * R + r;   // (image group)
         unsigned char* dst = xl + grp * P * kPairBytes + t * kTRowBytes + slot * kSlotBytes;
@@ -299,7 +306,11 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
           *reinterpret_cast<u32x4*>(dst + kPairBytes) = high_halves(mi0, mi1);
           *reinterpret_cast<u32x4*>(dst + 2 * kPairBytes) = high_halves(lo0, lo1);
         }
-        if ((bi & 7) == 0) xsl[(grp * 2 + hf) * 8 + (mm & 7)] = s8;
+        if constexpr (HV) {
+          if ((bi & 3) == 0) xsl[((grp * 2 + hf) * 2 + hh) * 8 + (mm & 7)] = s8;
+        } else {
+          if ((bi & 7) == 0) xsl[(grp * 2 + hf) * 8 + (mm & 7)] = s8;
+        }
       }
     }
   };
@@ -339,20 +350,29 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int tt = 0; tt < TILES; ++tt) bq[t][tt] = unpack_codes(w[tt][t], magic);
-    float sv[TILES], bb[TILES];
+    // (s, b) of the lane's group, or of its two halves (HV; sbi = G is the
+    // zero pad either way).
+    constexpr int NH = HV ? 2 : 1;
+    float sv[NH][TILES], bb[NH][TILES];
 #pragma unroll
-    for (int tt = 0; tt < TILES; ++tt) {
-      const unsigned v = sbl[(wcol + 16 * tt + j) * L.sbs + sbi];
-      sv[tt] = half_lo(v);
-      bb[tt] = fmaf(-TR::c0, sv[tt], half_hi(v));
-    }
+    for (int hv = 0; hv < NH; ++hv)
+#pragma unroll
+      for (int tt = 0; tt < TILES; ++tt) {
+        const unsigned v = sbl[(wcol + 16 * tt + j) * L.sbs + NH * sbi + hv];
+        sv[hv][tt] = half_lo(v);
+        bb[hv][tt] = fmaf(-TR::c0, sv[hv][tt], half_hi(v));
+      }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int grp = XALL && !in ? L.zxs : grp0 + r;
       const int img = XALL && !in ? L.zimg : (grp0 + r) * P;
       const unsigned char* ab = xl + img * kPairBytes + aslot * kSlotBytes;
-      const f32x4 xs = *reinterpret_cast<const f32x4*>(&xsl[(grp * 2 + half) * 8 + 4 * (h & 1)]);
-      f32x4 C[TILES];
+      f32x4 xs[NH];
+#pragma unroll
+      for (int hv = 0; hv < NH; ++hv)
+        xs[hv] = *reinterpret_cast<const f32x4*>(
+            &xsl[((grp * 2 + half) * NH + hv) * 8 + 4 * (h & 1)]);
+      f32x4 C[NH][TILES];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -362,14 +382,23 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
           const bool first = (t == 0) && (u == 0);
           const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int tt = 0; tt < TILES; ++tt)
-            C[tt] = mfma16x16x32<TR::f16>(A, bq[t][tt], first ? zero : C[tt]);
+          for (int hv = 0; hv < NH; ++hv) {
+            // HV: lanes of k slot h hold the 32-k half h & 1 of their group.
+            const u32x4 zA = {0u, 0u, 0u, 0u};
+            const u32x4 Ah = !HV || (h & 1) == hv ? A : zA;
+#pragma unroll
+            for (int tt = 0; tt < TILES; ++tt)
+              C[hv][tt] = mfma16x16x32<TR::f16>(Ah, bq[t][tt], first ? zero : C[hv][tt]);
+          }
         }
 #pragma unroll
-      for (int tt = 0; tt < TILES; ++tt)
+      for (int hv = 0; hv < NH; ++hv)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[r][tt][e] = fmaf(sv[tt], C[tt][e], fmaf(bb[tt], xs[e], acc[r][tt][e]));
+        for (int tt = 0; tt < TILES; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[r][tt][e] = fmaf(sv[hv][tt], C[hv][tt][e],
+                                 fmaf(bb[hv][tt], xs[hv][e], acc[r][tt][e]));
     }
   };
 
@@ -384,9 +413,9 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
     if constexpr (XALL) {
       for (int i = tid; i < kPairBytes / 16; i += NT)
         *reinterpret_cast<u32x4*>(xl + L.zimg * kPairBytes + 16 * i) = z;
-      if (tid < 16) xsl[L.zxs * 16 + tid] = 0.0f;
+      if (tid < XSF) xsl[L.zxs * XSF + tid] = 0.0f;
     }
-    for (int i = tid; i < WGC * 4; i += NT) sbl[(i >> 2) * L.sbs + G + (i & 3)] = 0u;
+    for (int i = tid; i < WGC * 4; i += NT) sbl[(i >> 2) * L.sbs + TG + (i & 3)] = 0u;
   }
   sb_load(0);
 #pragma unroll
@@ -885,9 +914,11 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
 }
 
 template <int ACT, int R, int TILES, int WN, int WK, int D, int KC, bool XALL>
-int lds_bytes_for(int K) {
+int lds_bytes_for(int K, int gs) {
   constexpr int WGC = 16 * TILES * WN;
-  const LdsLayout L = lds_layout<R, ActTraits<ACT>::parts, WK, KC, WGC, XALL>(K >> 6);
+  constexpr int P = ActTraits<ACT>::parts;
+  const LdsLayout L = gs < 0 ? lds_layout<R, P, WK, KC, WGC, XALL, true>(K >> 6)
+                             : lds_layout<R, P, WK, KC, WGC, XALL, false>(K >> 6);
   const int red_bytes = WK * WN * R * TILES * 128 * 4;
   return L.total > red_bytes ? L.total : red_bytes;
 }
@@ -896,9 +927,11 @@ template <int ACT, int R, int TILES, int WN, int WK, int D, int KC, bool XALL>
 hipError_t launch_w4(const void* x, const uint8_t* wq, const uint16_t* scales,
                      const uint16_t* biases, float* y, int M, int K, int N, int cols, int gs,
                      hipStream_t stream) {
-  const int lds_bytes = lds_bytes_for<ACT, R, TILES, WN, WK, D, KC, XALL>(K);
-  auto kern = gs ? qgemm_w4<ACT, R, TILES, WN, WK, D, KC, XALL, 1>
-                 : qgemm_w4<ACT, R, TILES, WN, WK, D, KC, XALL, 0>;
+  const int lds_bytes = lds_bytes_for<ACT, R, TILES, WN, WK, D, KC, XALL>(K, gs);
+  if (lds_bytes > kLdsLimit) return hipErrorInvalidValue;  // never launched
+  auto kern = qgemm_w4<ACT, R, TILES, WN, WK, D, KC, XALL, 0>;
+  if (gs > 0) kern = qgemm_w4<ACT, R, TILES, WN, WK, D, KC, XALL, 1>;
+  if (gs < 0) kern = qgemm_w4<ACT, R, TILES, WN, WK, D, KC, XALL, -1>;
   if (lds_bytes > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -981,51 +1014,54 @@ template <int ACT>
 hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                          const uint16_t* biases, float* y, int M, int K, int N, int gs,
                          hipStream_t s) {
-  if constexpr (ACT != ACT_FP32) if (qgemm_rows_fits(M, K, N, ACT)) {
-    // 17..64 rows at vocabulary widths: all row sets on one weight stream.
-    return launch_qgemm_rows(x, wq, scales, biases, y, M, K, N, ACT, gs, s);
+  // Group 32 (gs < 0) runs on the generic kernel only.
+  if (gs >= 0) {
+    if constexpr (ACT != ACT_FP32) if (qgemm_rows_fits(M, K, N, ACT)) {
+      // 17..64 rows at vocabulary widths: all row sets on one weight stream.
+      return launch_qgemm_rows(x, wq, scales, biases, y, M, K, N, ACT, gs, s);
+    }
+    if (qgemm_wide_fits(M, K, N, ACT)) {
+      // Vocabulary widths: whole-tile waves (the fused verify's projection
+      // takes the same kernel, so the two paths agree bit for bit).
+      const VerifyArgs none{};
+      return launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, ACT, gs, none, s);
+    }
+    if constexpr (ACT != ACT_FP32) if (M <= 8 && m8_fits(K)) {
+      const VerifyArgs none{};
+      return launch_m8_any<ACT>(x, wq, scales, biases, y, M, K, N, gs, none, s);
+    }
+    if (M > 8 && qgemm_m16_fits(M, K, ACT))
+      return launch_qgemm_m16(x, wq, scales, biases, y, M, K, N, ACT, gs, s);
   }
-  if (qgemm_wide_fits(M, K, N, ACT)) {
-    // Vocabulary widths: whole-tile waves (the fused verify's projection
-    // takes the same kernel, so the two paths agree bit for bit).
-    const VerifyArgs none{};
-    return launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, ACT, gs, none, s);
-  }
-  if constexpr (ACT != ACT_FP32) if (M <= 8 && m8_fits(K)) {
-    const VerifyArgs none{};
-    return launch_m8_any<ACT>(x, wq, scales, biases, y, M, K, N, gs, none, s);
-  }
-  if (M > 8 && qgemm_m16_fits(M, K, ACT))
-    return launch_qgemm_m16(x, wq, scales, biases, y, M, K, N, ACT, gs, s);
   if (M <= 8) {
     const int cus = device_cus();
     const int share = ((N + cus - 1) / cus + 3) / 4 * 4;
     if (share > 48 && share <= 80 &&
-        lds_bytes_for<ACT, 1, 1, 5, 2, 8, 1, true>(K) <= kLdsLimit)
+        lds_bytes_for<ACT, 1, 1, 5, 2, 8, 1, true>(K, gs) <= kLdsLimit)
       return launch_w4<ACT, 1, 1, 5, 2, 8, 1, true>(x, wq, scales, biases, y, M, K, N, share, gs, s);
     // Narrow outputs (fewer 64-column groups than CUs, e.g. the W4A32 draft
     // projection): one 16-column tile per work-group, K split over 8 waves,
     // no weight prefetch beyond the current step (measured fastest at
     // K = 5120, N = 1024: 11.1 us against 15.5 us for 64-column groups).
-    if ((N + 63) / 64 < cus && lds_bytes_for<ACT, 1, 1, 1, 8, 1, 1, false>(K) <= kLdsLimit)
+    if ((N + 63) / 64 < cus && lds_bytes_for<ACT, 1, 1, 1, 8, 1, 1, false>(K, gs) <= kLdsLimit)
       return launch_w4<ACT, 1, 1, 1, 8, 1, 1, false>(x, wq, scales, biases, y, M, K, N, 16, gs, s);
-    if (lds_bytes_for<ACT, 1, 1, 4, 2, 8, 1, true>(K) <= kLdsLimit)
+    if (lds_bytes_for<ACT, 1, 1, 4, 2, 8, 1, true>(K, gs) <= kLdsLimit)
       return launch_w4<ACT, 1, 1, 4, 2, 8, 1, true>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
     return launch_w4<ACT, 1, 1, 4, 2, 4, 2, false>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
   }
   // Several row sets: chunked staging; the smaller fallback (32 columns,
   // one K range, one-step chunks) keeps fp32 at large K within LDS.
   if (M <= 16) {
-    if (lds_bytes_for<ACT, 2, 1, 4, 2, 4, 2, false>(K) <= kLdsLimit)
+    if (lds_bytes_for<ACT, 2, 1, 4, 2, 4, 2, false>(K, gs) <= kLdsLimit)
       return launch_w4<ACT, 2, 1, 4, 2, 4, 2, false>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
     return launch_w4<ACT, 2, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, gs, s);
   }
   if (M <= 32) {
-    if (lds_bytes_for<ACT, 4, 1, 4, 1, 4, 1, false>(K) <= kLdsLimit)
+    if (lds_bytes_for<ACT, 4, 1, 4, 1, 4, 1, false>(K, gs) <= kLdsLimit)
       return launch_w4<ACT, 4, 1, 4, 1, 4, 1, false>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
     return launch_w4<ACT, 4, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, gs, s);
   }
-  if (lds_bytes_for<ACT, 8, 1, 4, 1, 2, 1, false>(K) <= kLdsLimit)
+  if (lds_bytes_for<ACT, 8, 1, 4, 1, 2, 1, false>(K, gs) <= kLdsLimit)
     return launch_w4<ACT, 8, 1, 4, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
   return launch_w4<ACT, 8, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, gs, s);
 }
@@ -1043,12 +1079,12 @@ hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales
   }
 }
 
-int qgemm_verify_groups(int M, int K, int N, int act) {
+int qgemm_verify_groups(int M, int K, int N, int act, int gs) {
   // The projection kernel of the fused path writes one partial per
   // work-group and row; verify_finish (verify.hip) reduces them. Vocabulary widths
   // take the persistent whole-tile kernel (one partial per CU and row
-  // instead of one per 80 columns).
-  if (M > 8 || act == ACT_FP32) return 0;
+  // instead of one per 80 columns). Group 32 has no fused kernel.
+  if (M > 8 || act == ACT_FP32 || gs < 0) return 0;
   if (qgemm_wide_fits(M, K, N, act)) return qgemm_wide_groups(M);
   if (!m8_fits(K)) return 0;
   const int cols = m8_cols(N);
@@ -1066,7 +1102,7 @@ hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t*
   else if (act == ACT_FP16)
     e = launch_m8_any<ACT_FP16>(x, wq, scales, biases, y, M, K, N, gs, va, stream);
   if (e != hipSuccess) return e;
-  return launch_verify_finish(va.partials, qgemm_verify_groups(M, K, N, act), va, stream);
+  return launch_verify_finish(va.partials, qgemm_verify_groups(M, K, N, act, gs), va, stream);
 }
 
 }  // namespace vqv

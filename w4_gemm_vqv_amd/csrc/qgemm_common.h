@@ -110,7 +110,9 @@ __device__ __forceinline__ float sum8_lanes(float s) {
 // (GS = 0: group 64, GS = 1: group 128; a template parameter of the kernels).
 // The kernels' tables are per 64-group: a 128-group's entry serves both of
 // its 64-groups, and the per-64-group row sums make the bias term
-// b * (xs0 + xs1) come out as b * xs of the 128-group.
+// b * (xs0 + xs1) come out as b * xs of the 128-group. GS = -1 (group 32,
+// the generic kernel only) keeps one LDS entry per 32-group and takes the
+// group-64 forms below with twice the entries per column.
 // A table unit covers 8 consecutive 64-groups of one column (K/64 a multiple
 // of 8). sb_unit_load reads one unit's entries from byte offset `off` of an
 // array: 16 bytes for group 64, or the 4 entries of group 128 (8 bytes,
@@ -121,7 +123,7 @@ __device__ __forceinline__ float sum8_lanes(float s) {
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 template <int GS>
 __device__ __forceinline__ u32x4 sb_unit_load(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  if constexpr (GS == 0) {
+  if constexpr (GS <= 0) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   } else {
     const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
@@ -131,7 +133,7 @@ __device__ __forceinline__ u32x4 sb_unit_load(__amdgpu_buffer_rsrc_t r, unsigned
 
 template <int GS>
 __device__ __forceinline__ void sb_pairs(const u32x4& s, const u32x4& b, u32x4& lo, u32x4& hi) {
-  if constexpr (GS == 0) {
+  if constexpr (GS <= 0) {
     lo.x = __builtin_amdgcn_perm(b.x, s.x, 0x05040100u);
     lo.y = __builtin_amdgcn_perm(b.x, s.x, 0x07060302u);
     lo.z = __builtin_amdgcn_perm(b.y, s.y, 0x05040100u);

@@ -1230,11 +1230,11 @@ bool qgemm_m16_fits(int M, int K, int act) {
          m16_layout(K >> 6, 16 * kM16Tiles, kM16Waves, kM16XB).total <= kLdsLimit;
 }
 
-bool qgemm_swiglu_fused(int M, int K, int N, int act) {
+bool qgemm_swiglu_fused(int M, int K, int N, int act, int gs) {
   // The fused kernel's weight buffer spans the whole stacked weight from the
   // work-group's first gate row; it must stay below the scalar offset that
-  // reads as zero.
-  return qgemm_m16_fits(M, K, act) && (size_t)N * (size_t)(K / 2) < 0x7F000000u;
+  // reads as zero. Group 32 has no fused kernel.
+  return gs >= 0 && qgemm_m16_fits(M, K, act) && (size_t)N * (size_t)(K / 2) < 0x7F000000u;
 }
 
 hipError_t launch_qgemm_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
@@ -1250,7 +1250,7 @@ hipError_t launch_qgemm_m16(const void* x, const uint8_t* wq, const uint16_t* sc
 hipError_t launch_qgemm_swiglu(const void* x, const uint8_t* wq, const uint16_t* scales,
                                const uint16_t* biases, float* h, int M, int K, int N, int act,
                                int gs, float* scratch_y, hipStream_t stream) {
-  if (qgemm_swiglu_fused(M, K, N, act)) {
+  if (qgemm_swiglu_fused(M, K, N, act, gs)) {
     if (act == ACT_BF16)
       return launch_m16_blocks<ACT_BF16, true>(x, wq, scales, biases, h, M, K, N, gs, stream);
     return launch_m16_blocks<ACT_FP16, true>(x, wq, scales, biases, h, M, K, N, gs, stream);

@@ -21,8 +21,12 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 int act_size(vqv_dtype a) { return a == VQV_FP32 ? 4 : 2; }
 
-// Group shift of a supported group size (64 << gs values per scale), or -1.
-int group_shift(int group) { return group == 64 ? 0 : group == 128 ? 1 : -1; }
+// Group shift of a supported group size: 0 for 64, 1 for 128 (64 << gs values
+// per scale), -1 for 32; kNoGroup for any other size.
+constexpr int kNoGroup = 99;
+int group_shift(int group) {
+  return group == 64 ? 0 : group == 128 ? 1 : group == 32 ? -1 : kNoGroup;
+}
 
 }  // namespace
 
@@ -34,7 +38,7 @@ const char* vqv_status_string(vqv_status s) {
   switch (s) {
     case VQV_OK: return "ok";
     case VQV_ERR_ARG: return "invalid argument (null pointer, size out of range or aliasing)";
-    case VQV_ERR_UNSUPPORTED: return "unsupported request (e.g. group size other than 64 or 128)";
+    case VQV_ERR_UNSUPPORTED: return "unsupported request (e.g. group size other than 32, 64 or 128)";
     case VQV_ERR_ALIGN: return "pointer alignment requirement not met";
     case VQV_ERR_WORKSPACE: return "workspace missing or too small";
     case VQV_ERR_HIP: return "HIP runtime error at launch";
@@ -57,9 +61,10 @@ vqv_status vqv_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
     return VQV_ERR_ARG;
   if (M < 1 || M > kMaxRows || N < 1 || K < kGroup) return VQV_ERR_ARG;
   const int gs = group_shift(group);
-  if (gs < 0) return VQV_ERR_UNSUPPORTED;
+  if (gs == kNoGroup) return VQV_ERR_UNSUPPORTED;
   if (K % group) return VQV_ERR_ARG;
-  if (K > vqv::kMaxK) return VQV_ERR_UNSUPPORTED;
+  if (K % kGroup) return VQV_ERR_UNSUPPORTED;  // group 32 with an odd count of 32-groups
+  if (K > (gs < 0 ? vqv::kMaxK32 : vqv::kMaxK)) return VQV_ERR_UNSUPPORTED;
   const size_t esz = (size_t)act_size(act_dtype);
   const size_t xbytes = (size_t)M * K * esz;
   const size_t wbytes = (size_t)N * (K / 2);
@@ -89,8 +94,9 @@ constexpr size_t kHead = 256;
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 size_t vqv_qgemm_verify_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype) {
-  if (M < 1 || M > kMaxRows || N < 1 || K < kGroup || group_shift(group) < 0) return 0;
-  const int groups = vqv::qgemm_verify_groups(M, K, N, (int)act_dtype);
+  const int gs = group_shift(group);
+  if (M < 1 || M > kMaxRows || N < 1 || K < kGroup || gs == kNoGroup) return 0;
+  const int groups = vqv::qgemm_verify_groups(M, K, N, (int)act_dtype, gs);
   if (groups > 0) return kHead + (size_t)groups * 8 * 16;
   return kHead + align256((size_t)M * N * 4) + (size_t)M * vqv::verify_chunks(N) * 16;
 }
@@ -118,9 +124,10 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
   if (B < 1 || T < 1 || T > kMaxBlock || (long long)B * T != M) return VQV_ERR_ARG;
   if (T > 1 && !draft) return VQV_ERR_ARG;
   const int gs = group_shift(group);
-  if (gs < 0) return VQV_ERR_UNSUPPORTED;
+  if (gs == kNoGroup) return VQV_ERR_UNSUPPORTED;
   if (K % group) return VQV_ERR_ARG;
-  if (K > vqv::kMaxK) return VQV_ERR_UNSUPPORTED;
+  if (K % kGroup) return VQV_ERR_UNSUPPORTED;  // group 32 with an odd count of 32-groups
+  if (K > (gs < 0 ? vqv::kMaxK32 : vqv::kMaxK)) return VQV_ERR_UNSUPPORTED;
   const size_t esz = (size_t)act_size(act_dtype);
   const size_t xbytes = (size_t)M * K * esz;
   const size_t wbytes = (size_t)N * (K / 2);
@@ -154,7 +161,7 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
   vqv::VerifyArgs va{draft, draft_len, B, T, argmax, accept_len, margin,
                      reinterpret_cast<uint4*>(ws + kHead)};
   hipError_t e;
-  if (vqv::qgemm_verify_groups(M, K, N, (int)act_dtype) > 0) {
+  if (vqv::qgemm_verify_groups(M, K, N, (int)act_dtype, gs) > 0) {
     e = vqv::launch_qgemm_verify(x, wq, scales, biases, y, M, K, N, (int)act_dtype, gs, va, st);
   } else {
     float* logits = y ? y : reinterpret_cast<float*>(ws + kHead);
@@ -166,9 +173,9 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
 }
 
 size_t vqv_qgemm_swiglu_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype) {
-  if (M < 1 || M > kMaxRows || N < 2 || (N & 1) || K < kGroup || group_shift(group) < 0)
-    return 0;
-  if (vqv::qgemm_swiglu_fused(M, K, N, (int)act_dtype)) return 0;
+  const int gs = group_shift(group);
+  if (M < 1 || M > kMaxRows || N < 2 || (N & 1) || K < kGroup || gs == kNoGroup) return 0;
+  if (vqv::qgemm_swiglu_fused(M, K, N, (int)act_dtype, gs)) return 0;
   return align256((size_t)M * N * 4);  // the stacked gate/up output
 }
 
@@ -181,9 +188,10 @@ vqv_status vqv_qgemm_swiglu(const void* x, const uint8_t* wq, const uint16_t* sc
     return VQV_ERR_ARG;
   if (M < 1 || M > kMaxRows || N < 2 || (N & 1) || K < kGroup) return VQV_ERR_ARG;
   const int gs = group_shift(group);
-  if (gs < 0) return VQV_ERR_UNSUPPORTED;
+  if (gs == kNoGroup) return VQV_ERR_UNSUPPORTED;
   if (K % group) return VQV_ERR_ARG;
-  if (K > vqv::kMaxK) return VQV_ERR_UNSUPPORTED;
+  if (K % kGroup) return VQV_ERR_UNSUPPORTED;  // group 32 with an odd count of 32-groups
+  if (K > (gs < 0 ? vqv::kMaxK32 : vqv::kMaxK)) return VQV_ERR_UNSUPPORTED;
   const size_t esz = (size_t)act_size(act_dtype);
   const size_t xbytes = (size_t)M * K * esz;
   const size_t wbytes = (size_t)N * (K / 2);

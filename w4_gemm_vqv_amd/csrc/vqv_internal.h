@@ -10,13 +10,16 @@ namespace vqv {
 
 enum ActKind { ACT_BF16 = 0, ACT_FP16 = 1, ACT_FP32 = 2 };
 
-// Largest K: a work-group keeps its columns' scale/bias rows in LDS.
+// Largest K: a work-group keeps its columns' scale/bias rows in LDS (twice
+// as many entries per row for group 32).
 constexpr int kMaxK = 16384;
+constexpr int kMaxK32 = 8192;
 
 // y[M,N] = x[M,K] . W^T for 1 <= M <= 64, 64 <= K <= kMaxK, K % 64 == 0.
 // Every launcher takes the group shift gs: scales and biases hold one entry
-// per 64 << gs values of a row (gs = 0: group 64; gs = 1: group 128, which
-// needs K % 128 == 0).
+// per group of a row, 64 << gs values for gs = 0 (group 64) and gs = 1
+// (group 128, K % 128 == 0), 32 values for gs = -1 (group 32, which only the
+// generic kernel takes).
 hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
                         const uint16_t* biases, float* y, int M, int K, int N, int act, int gs,
                         hipStream_t stream);
@@ -43,7 +46,7 @@ hipError_t launch_verify_finish(const uint4* partials, int groups, const VerifyA
 
 // The number of work-groups the fused projection launches, or 0 when the
 // fused path does not take this problem.
-int qgemm_verify_groups(int M, int K, int N, int act);
+int qgemm_verify_groups(int M, int K, int N, int act, int gs);
 
 hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* scales,
                                const uint16_t* biases, float* y, int M, int K, int N, int act,
@@ -77,7 +80,7 @@ hipError_t launch_qgemm_wide(const void* x, const uint8_t* wq, const uint16_t* s
 // gate/up weight [N, K]. Fused into the 16-row kernel when
 // qgemm_swiglu_fused(); otherwise the projection writes `scratch_y` [M, N]
 // and an elementwise kernel forms h.
-bool qgemm_swiglu_fused(int M, int K, int N, int act);
+bool qgemm_swiglu_fused(int M, int K, int N, int act, int gs);
 hipError_t launch_qgemm_swiglu(const void* x, const uint8_t* wq, const uint16_t* scales,
                                const uint16_t* biases, float* h, int M, int K, int N, int act,
                                int gs, float* scratch_y, hipStream_t stream);
