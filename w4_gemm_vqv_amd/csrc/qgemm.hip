@@ -489,6 +489,17 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
 }
 
 
+// Group 32 in qgemm_w4_m8: lane l and lane l ^ 16 hold the two 32-k halves
+// of one group (k slots 2g and 2g + 1), dwords t = the 8-value blocks t of
+// the half. After the exchange, dword t of every lane holds block
+// 2 (t % 2) + (h % 2) of half t / 2, so MFMAs 0-1 of a step see only the
+// first halves and MFMAs 2-3 only the second.
+__device__ __forceinline__ u32x4 pair_halves(const u32x4& w) {
+  const auto a = __builtin_amdgcn_permlane16_swap(w.x, w.y, false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(w.z, w.w, false, false);
+  return u32x4{a[0], b[0], a[1], b[1]};
+}
+
 // LDS of qgemm_w4_m8: GP activation images and one zero image (more when the
 // staging rounds are padded), the row sums (16 floats per image), the (s, b)
 // table (G + 4 dwords per column), the partial-sum slots (two 8x16 tiles per
@@ -497,15 +508,16 @@ struct M8Layout {
   int xs, sb, sbs, red, runs, total;
 };
 
-__host__ __device__ inline M8Layout m8_layout(int G, int WGC, int NW, int XB) {
+// HV (group 32): row sums and table entries per 32-k half, twice as many.
+__host__ __device__ inline M8Layout m8_layout(int G, int WGC, int NW, int XB, bool HV) {
   const int GP = (G + 1) >> 1;
   const int rounds = (2 * GP + NW - 1) / NW;             // staging rounds per wave
   const int padded = (rounds + XB - 1) / XB * XB * NW;   // groups the staging writes
   const int nimg = GP + 1 > padded / 2 ? GP + 1 : padded / 2;
   M8Layout L{};
   L.xs = nimg * kPairBytes;
-  L.sb = L.xs + nimg * 16 * 4;
-  L.sbs = G + 4;
+  L.sb = L.xs + nimg * (HV ? 32 : 16) * 4;
+  L.sbs = (HV ? 2 * G : G) + 4;
   L.red = L.sb + WGC * L.sbs * 4;
   L.runs = L.red + NW * 2 * 128 * 4;
   L.total = L.runs + NW * 2 * 4;
@@ -546,7 +558,14 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     float* __restrict__ y, int M, int K, int N, int cols, VerifyArgs va) {
   using TR = ActTraits<ACT>;
-  constexpr int gs = GS;                            // group 64 << GS
+  // GS: group 64 << GS for GS >= 0. GS = -1 is group 32: the codes of a
+  // lane pair (lanes l and l + 16) are exchanged so that MFMAs 0-1 of a step
+  // cover the first 32-k half of each group and MFMAs 2-3 the second; each
+  // half accumulates apart and takes its own scale, bias and row sum.
+  constexpr int gs = GS > 0 ? GS : 0;               // table shift of group 128
+  constexpr bool HV = GS < 0;
+  constexpr int NH = HV ? 2 : 1;                    // scaled partial sums per group
+  constexpr int XSF = HV ? 32 : 16;                 // row sums per activation image
   static_assert(TR::parts == 1, "16-bit activations only");
   static_assert(TW <= NW, "a run must span at most two tiles");
   static_assert(NW >= 8, "the partial-sum slots double as an 8 KB write sink");
@@ -569,7 +588,9 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
   const int GP = (G + 1) >> 1;                       // a multiple of DB (host)
   const int bpt = GP / DB;                           // blocks per tile
   const unsigned rowbytes = (unsigned)K >> 1;
-  const M8Layout L = m8_layout(G, WGC, NW, XB);
+  const M8Layout L = m8_layout(G, WGC, NW, XB, HV);
+  const int TG = HV ? 2 * G : G;                     // LDS table entries per column
+  const int ME = HV ? 2 * G : (G >> gs);             // table entries per column in memory
   unsigned char* xl = lds;
   float* xsl = reinterpret_cast<float*>(lds + L.xs);
   unsigned* sbl = reinterpret_cast<unsigned*>(lds + L.sb);
@@ -591,11 +612,9 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
       const_cast<uint8_t*>(wq) + (size_t)wg0 * rowbytes, (short)0, wgcols * rowbytes,
       kBufferFlags);
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(scales) + (size_t)wg0 * (G >> gs), (short)0, wgcols * (G >> gs) * 2,
-      kBufferFlags);
+      const_cast<uint16_t*>(scales) + (size_t)wg0 * ME, (short)0, wgcols * ME * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(biases) + (size_t)wg0 * (G >> gs), (short)0, wgcols * (G >> gs) * 2,
-      kBufferFlags);
+      const_cast<uint16_t*>(biases) + (size_t)wg0 * ME, (short)0, wgcols * ME * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(x), (short)0, M * K * 2, kBufferFlags);
 
@@ -619,17 +638,24 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
           xr, ok ? (unsigned)((mm * K + k) * 2) : kOutOfRange, 0, 0);
     }
   };
-  const unsigned xl_lane = (e8 & 3) * kTRowBytes + ((e8 >> 2) * 8 + mm) * kSlotBytes;
+  // Block e8 feeds MFMA t from k slot h (high bit: the group in the pair):
+  // t = e8 % 4 and h low bit = e8 / 4, or with HV t = 2 (e8 / 4) + (e8 % 4) / 2
+  // and h low bit = e8 % 2 (the order the exchanged codes arrive in).
+  const unsigned xl_lane =
+      HV ? (2 * (e8 >> 2) + ((e8 & 3) >> 1)) * kTRowBytes + ((e8 & 1) * 8 + mm) * kSlotBytes
+         : (e8 & 3) * kTRowBytes + ((e8 >> 2) * 8 + mm) * kSlotBytes;
   // The image area is padded (m8_layout) so that every round of every batch
   // has a slot: rounds past the last group stage zeros (their loads read
   // past K) into images that are never read, or into the zero image.
   auto x_store_round = [&](int bb, int i) {
     const int g = wave + NW * (bb + i);               // uniform
-    // Sum of the row's 64 values: the eight lanes of (row, group) all hold it.
-    const float s8 = sum8_lanes(block_sum<ACT>(xv[i]));
+    // Sum of the row's 64 values (the eight lanes of (row, group) all hold
+    // it), or with HV of a half's 32 values (the four lanes of (row, group,
+    // half)).
+    const float s8 = HV ? sum4_lanes(block_sum<ACT>(xv[i])) : sum8_lanes(block_sum<ACT>(xv[i]));
     *reinterpret_cast<u32x4*>(xl + (g >> 1) * kPairBytes + (g & 1) * 16 * kSlotBytes +
                               xl_lane) = permute_pairs(xv[i]);
-    xsl[g * 8 + mm] = s8;
+    xsl[HV ? (g * 2 + (e8 >> 2)) * 8 + mm : g * 8 + mm] = s8;
   };
   auto x_store = [&](int bb) {
 #pragma unroll
@@ -637,9 +663,9 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
   };
 
   // ---- scale/bias table (as in qgemm_w4).
-  const bool sb_vec = (G % 8) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
-                                        reinterpret_cast<uintptr_t>(biases)) & 15) == 0;
-  const int sb_units = sb_vec ? wgcols * G / 8 : wgcols * G;
+  const bool sb_vec = (TG % 8) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
+                                         reinterpret_cast<uintptr_t>(biases)) & 15) == 0;
+  const int sb_units = sb_vec ? wgcols * TG / 8 : wgcols * TG;
   u32x4 sbs[SBU], sbb[SBU];
   auto sb_load = [&](int round) {
 #pragma unroll
@@ -656,10 +682,10 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
       }
     }
   };
-  // n = e / G as a high product with ceil(2^32 / G) (exact for e < 2^32 / G);
-  // G = 1 has no 32-bit reciprocal and is handled directly.
-  const unsigned g_recip = 0xFFFFFFFFu / (unsigned)G + 1u;
-  auto div_g = [&](unsigned e) { return G == 1 ? e : __umulhi(e, g_recip); };
+  // n = e / TG as a high product with ceil(2^32 / TG) (exact for
+  // e < 2^32 / TG); TG = 1 has no 32-bit reciprocal and is handled directly.
+  const unsigned g_recip = 0xFFFFFFFFu / (unsigned)TG + 1u;
+  auto div_g = [&](unsigned e) { return TG == 1 ? e : __umulhi(e, g_recip); };
   auto sb_store = [&](int round) {
 #pragma unroll
     for (int u = 0; u < SBU; ++u) {
@@ -667,7 +693,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
       const bool ok = i < sb_units;
       if (sb_vec) {
         const unsigned e0 = 8u * (unsigned)i;         // first element of the unit
-        const unsigned n = div_g(e0), g = e0 - n * (unsigned)G;
+        const unsigned n = div_g(e0), g = e0 - n * (unsigned)TG;
         u32x4 lo, hi;                                 // (s_g | b_g << 16) for g .. g+7
         sb_pairs<GS>(sbs[u], sbb[u], lo, hi);
         // Units past the table write into the partial-sum slots (8 KB, not
@@ -677,7 +703,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
         *reinterpret_cast<u32x4*>(lds + o) = lo;
         *reinterpret_cast<u32x4*>(lds + o + 16) = hi;
       } else if (ok) {
-        const unsigned n = div_g((unsigned)i), g = (unsigned)i - n * (unsigned)G;
+        const unsigned n = div_g((unsigned)i), g = (unsigned)i - n * (unsigned)TG;
         sbl[n * L.sbs + g] = (sbs[u].x & 0xFFFFu) | (sbb[u].x << 16);
       }
     }
@@ -724,8 +750,8 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
                                 32 * kSlotBytes) = z;
     for (int i = tid; i < kPairBytes / 16; i += NT)
       *reinterpret_cast<u32x4*>(xl + GP * kPairBytes + 16 * i) = z;
-    if (tid < 16) xsl[GP * 16 + tid] = 0.0f;
-    for (int i = tid; i < WGC * 4; i += NT) sbl[(i >> 2) * L.sbs + G + (i & 3)] = 0u;
+    if (tid < XSF) xsl[GP * XSF + tid] = 0.0f;
+    for (int i = tid; i < WGC * 4; i += NT) sbl[(i >> 2) * L.sbs + TG + (i & 3)] = 0u;
   }
   // The first batch is staged round by round, one more ring slot issued
   // before each round, so the weight stream starts while staging runs.
@@ -753,9 +779,9 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
 
   // ---- main loop.
   const unsigned char* abase = xl + aslot * kSlotBytes;
-  const float* xsbase = xsl + half * 8 + 4 * (h & 1);
-  const unsigned* sbbase = sbl + j * L.sbs + half;
-  struct Ops { u32x4 A[4]; f32x4 xs; unsigned sb; };
+  const float* xsbase = xsl + half * (XSF / 2) + 4 * (h & 1);
+  const unsigned* sbbase = sbl + j * L.sbs + NH * half;
+  struct Ops { u32x4 A[4]; f32x4 xs[NH]; unsigned sb[NH]; };
   // LDS bases of block k (the zero image and pad past the run); step d of a
   // block reads at immediate offsets from them.
   struct Base {
@@ -768,16 +794,19 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
     const int img = in ? k.p : GP;
     Base b;
     b.a = abase + img * kPairBytes;
-    b.xs = xsbase + img * 16;
-    b.sb = sbbase + (in ? k.t * 16 * L.sbs + 2 * k.p : G + 2);
+    b.xs = xsbase + img * XSF;
+    b.sb = sbbase + (in ? k.t * 16 * L.sbs + 2 * NH * k.p : (HV ? TG : G + 2));
     return b;
   };
   auto fetch = [&](const Base& b, int d, Ops& o) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       o.A[t] = *reinterpret_cast<const u32x4*>(b.a + d * kPairBytes + t * kTRowBytes);
-    o.xs = *reinterpret_cast<const f32x4*>(b.xs + d * 16);
-    o.sb = b.sb[2 * d];
+#pragma unroll
+    for (int hv = 0; hv < NH; ++hv) {
+      o.xs[hv] = *reinterpret_cast<const f32x4*>(b.xs + d * XSF + 8 * hv);
+      o.sb[hv] = b.sb[2 * NH * d + hv];
+    }
   };
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   int acc_tile = tfirst;
@@ -789,17 +818,26 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
       acc[e] = 0.0f;
     }
   };
-  auto epilogue = [&](const f32x4& C, const Ops& o) {
-    const float sv = half_lo(o.sb);
-    const float bb = fmaf(-TR::c0, sv, half_hi(o.sb));
+  struct Acc { f32x4 c[NH]; };                      // a step's partial sums
+  auto epilogue = [&](const Acc& C, const Ops& o) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = fmaf(sv, C[e], fmaf(bb, o.xs[e], acc[e]));
+    for (int hv = 0; hv < NH; ++hv) {
+      const float sv = half_lo(o.sb[hv]);
+      const float bb = fmaf(-TR::c0, sv, half_hi(o.sb[hv]));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(sv, C.c[hv][e], fmaf(bb, o.xs[hv][e], acc[e]));
+    }
   };
 
   Ops cur, prev;
-  f32x4 Cprev = {0.0f, 0.0f, 0.0f, 0.0f};
-  prev.sb = 0u;                                       // step -1 adds exactly nothing
-  prev.xs = Cprev;
+  const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  Acc Cprev;
+#pragma unroll
+  for (int hv = 0; hv < NH; ++hv) {
+    Cprev.c[hv] = zero4;
+    prev.sb[hv] = 0u;                                 // step -1 adds exactly nothing
+    prev.xs[hv] = zero4;
+  }
   int prev_tile = tfirst;
   Blk kc = kfirst;                                    // the block being computed
   Base bc = base_of(kc);
@@ -813,11 +851,22 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
       u32x4 bq[4];
+      Acc C;
+      if constexpr (HV) {
+        const u32x4 w = pair_halves(st[r * DB + d]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) bq[t] = unpack_codes(st[r * DB + d][t], magic);
-      f32x4 C = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int t = 0; t < 4; ++t) bq[t] = unpack_codes(w[t], magic);
+        C.c[0] = mfma16x16x32<TR::f16>(cur.A[0], bq[0], zero4);
+        C.c[0] = mfma16x16x32<TR::f16>(cur.A[1], bq[1], C.c[0]);
+        C.c[1] = mfma16x16x32<TR::f16>(cur.A[2], bq[2], zero4);
+        C.c[1] = mfma16x16x32<TR::f16>(cur.A[3], bq[3], C.c[1]);
+      } else {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) C = mfma16x16x32<TR::f16>(cur.A[t], bq[t], C);
+        for (int t = 0; t < 4; ++t) bq[t] = unpack_codes(st[r * DB + d][t], magic);
+        C.c[0] = zero4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) C.c[0] = mfma16x16x32<TR::f16>(cur.A[t], bq[t], C.c[0]);
+      }
       Ops nxt;
       if (d + 1 < DB) fetch(bc, d + 1, nxt);
       else fetch(bn, 0, nxt);
@@ -949,11 +998,17 @@ hipError_t launch_m8(const void* x, const uint8_t* wq, const uint16_t* scales,
                      const uint16_t* biases, float* y, int M, int K, int N, int cols, int gs,
                      const VerifyArgs& va, hipStream_t stream) {
   constexpr int TW = 5;
-  const M8Layout L = m8_layout(K >> 6, 16 * TW, NW, XB);
-  auto kern = va.argmax ? (gs ? qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, true, 1>
-                           : qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, true, 0>)
-                        : (gs ? qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, false, 1>
-                              : qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, false, 0>);
+  const M8Layout L = m8_layout(K >> 6, 16 * TW, NW, XB, gs < 0);
+  if (L.total > kLdsLimit) return hipErrorInvalidValue;  // never launched
+  auto kern = qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, false, 0>;
+  if (va.argmax) {
+    kern = qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, true, 0>;
+    if (gs > 0) kern = qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, true, 1>;
+    if (gs < 0) kern = qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, true, -1>;
+  } else {
+    if (gs > 0) kern = qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, false, 1>;
+    if (gs < 0) kern = qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, false, -1>;
+  }
   if (L.total > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -994,7 +1049,9 @@ int m8_cols(int N) {
   const int share = ((N + cus - 1) / cus + 3) / 4 * 4;
   return share < 80 ? share : 80;
 }
-bool m8_fits(int K) { return m8_layout(K >> 6, 80, 8, m8_xb(K)).total <= kLdsLimit; }
+bool m8_fits(int K, int gs) {
+  return m8_layout(K >> 6, 80, 8, m8_xb(K), gs < 0).total <= kLdsLimit;
+}
 
 template <int ACT>
 hipError_t launch_m8_any(const void* x, const uint8_t* wq, const uint16_t* scales,
@@ -1014,7 +1071,7 @@ template <int ACT>
 hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                          const uint16_t* biases, float* y, int M, int K, int N, int gs,
                          hipStream_t s) {
-  // Group 32 (gs < 0) runs on the generic kernel only.
+  // Group 32 (gs < 0) runs on qgemm_w4_m8 (M <= 8) or the generic kernel.
   if (gs >= 0) {
     if constexpr (ACT != ACT_FP32) if (qgemm_rows_fits(M, K, N, ACT)) {
       // 17..64 rows at vocabulary widths: all row sets on one weight stream.
@@ -1026,13 +1083,13 @@ hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scale
       const VerifyArgs none{};
       return launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, ACT, gs, none, s);
     }
-    if constexpr (ACT != ACT_FP32) if (M <= 8 && m8_fits(K)) {
-      const VerifyArgs none{};
-      return launch_m8_any<ACT>(x, wq, scales, biases, y, M, K, N, gs, none, s);
-    }
-    if (M > 8 && qgemm_m16_fits(M, K, ACT))
-      return launch_qgemm_m16(x, wq, scales, biases, y, M, K, N, ACT, gs, s);
   }
+  if constexpr (ACT != ACT_FP32) if (M <= 8 && m8_fits(K, gs)) {
+    const VerifyArgs none{};
+    return launch_m8_any<ACT>(x, wq, scales, biases, y, M, K, N, gs, none, s);
+  }
+  if (gs >= 0 && M > 8 && qgemm_m16_fits(M, K, ACT))
+    return launch_qgemm_m16(x, wq, scales, biases, y, M, K, N, ACT, gs, s);
   if (M <= 8) {
     const int cus = device_cus();
     const int share = ((N + cus - 1) / cus + 3) / 4 * 4;
@@ -1083,10 +1140,10 @@ int qgemm_verify_groups(int M, int K, int N, int act, int gs) {
   // The projection kernel of the fused path writes one partial per
   // work-group and row; verify_finish (verify.hip) reduces them. Vocabulary widths
   // take the persistent whole-tile kernel (one partial per CU and row
-  // instead of one per 80 columns). Group 32 has no fused kernel.
-  if (M > 8 || act == ACT_FP32 || gs < 0) return 0;
-  if (qgemm_wide_fits(M, K, N, act)) return qgemm_wide_groups(M);
-  if (!m8_fits(K)) return 0;
+  // instead of one per 80 columns). Group 32 takes qgemm_w4_m8 only.
+  if (M > 8 || act == ACT_FP32) return 0;
+  if (gs >= 0 && qgemm_wide_fits(M, K, N, act)) return qgemm_wide_groups(M);
+  if (!m8_fits(K, gs)) return 0;
   const int cols = m8_cols(N);
   return (N + cols - 1) / cols;
 }
@@ -1095,7 +1152,7 @@ hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t*
                                const uint16_t* biases, float* y, int M, int K, int N, int act,
                                int gs, const VerifyArgs& va, hipStream_t stream) {
   hipError_t e = hipErrorInvalidValue;
-  if (qgemm_wide_fits(M, K, N, act))
+  if (gs >= 0 && qgemm_wide_fits(M, K, N, act))
     e = launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, act, gs, va, stream);
   else if (act == ACT_BF16)
     e = launch_m8_any<ACT_BF16>(x, wq, scales, biases, y, M, K, N, gs, va, stream);

@@ -94,6 +94,15 @@ __device__ __forceinline__ float block_sum(const u32x4& v) {
   return s;
 }
 
+// Sum over the four lanes 4i..4i+3 (DPP: swap neighbours, then swap pairs).
+__device__ __forceinline__ float sum4_lanes(float s) {
+  s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                     0, __builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
+  s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                     0, __builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, false));
+  return s;
+}
+
 // Sum over the eight lanes 8i..8i+7 (DPP: swap neighbours, swap pairs, then
 // mirror within the half row).
 __device__ __forceinline__ float sum8_lanes(float s) {
