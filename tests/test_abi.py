@@ -184,7 +184,8 @@ def test_swiglu_workspace_queries(L):
     # invalid: odd N, group, M
     assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1001, 64, BF16) == 0
     assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1000, 16, BF16) == 0
-    assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1000, 32, BF16) >= 16 * 1000 * 4
+    assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1000, 32, BF16) == 0  # fused too
+    assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1000, 32, FP32) >= 16 * 1000 * 4
     assert L.vqv_qgemm_swiglu_workspace_bytes(64, 512, 1000, 128, BF16) == 0
     assert L.vqv_qgemm_swiglu_workspace_bytes(16, 512, 1000, 256, BF16) == 0
     assert L.vqv_qgemm_swiglu_workspace_bytes(0, 512, 1000, 64, BF16) == 0

@@ -109,7 +109,8 @@ def test_group128_equals_group64_twice(vqv, act, M, K, N):
     np.testing.assert_array_equal(y128, run(vqv, c64))
 
 
-# Group 32 runs on the generic kernel in every configuration its dispatch
+# Group 32 runs on the 8-row kernel (M <= 8), the 16-row kernel (9..64 rows,
+# K <= 2560) and the generic kernel in every configuration its dispatch
 # takes: one row set with the whole K range staged (64-80 column shares and
 # wide N), narrow outputs, chunked staging at large K, two, four and eight row
 # sets, the small fallbacks, and an odd count of 64-groups.
@@ -117,6 +118,12 @@ SHAPES_G32 = [
     (8, 5120, 17408), (8, 5120, 1024), (1, 640, 300), (4, 1280, 30000), (5, 192, 65),
     (8, 8192, 300), (16, 640, 300), (12, 8192, 100), (9, 448, 777), (32, 256, 96),
     (20, 1280, 500), (64, 512, 130), (40, 8192, 70), (64, 64, 99),
+    # The 8-row kernel at its edges: one 64-group, an odd group count with a
+    # ragged tail, runs across tiles, and K at its staging limit.
+    (8, 64, 3), (3, 64, 1000), (7, 320, 4001), (8, 1088, 129), (2, 2560, 66001),
+    # The 16-row kernel: one to four row sets, several tiles per work-group,
+    # K at its staging limit, 16-bit table loads (K/32 not a multiple of 8).
+    (16, 512, 5000), (12, 2560, 17408), (64, 2560, 5000), (48, 1280, 3001), (33, 384, 9000),
 ]
 
 

@@ -1071,7 +1071,8 @@ template <int ACT>
 hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                          const uint16_t* biases, float* y, int M, int K, int N, int gs,
                          hipStream_t s) {
-  // Group 32 (gs < 0) runs on qgemm_w4_m8 (M <= 8) or the generic kernel.
+  // Group 32 (gs < 0) runs on qgemm_w4_m8 (M <= 8), qgemm_w4_m16 or the
+  // generic kernel.
   if (gs >= 0) {
     if constexpr (ACT != ACT_FP32) if (qgemm_rows_fits(M, K, N, ACT)) {
       // 17..64 rows at vocabulary widths: all row sets on one weight stream.
@@ -1088,7 +1089,7 @@ hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scale
     const VerifyArgs none{};
     return launch_m8_any<ACT>(x, wq, scales, biases, y, M, K, N, gs, none, s);
   }
-  if (gs >= 0 && M > 8 && qgemm_m16_fits(M, K, ACT))
+  if (M > 8 && qgemm_m16_fits(M, K, ACT, gs))
     return launch_qgemm_m16(x, wq, scales, biases, y, M, K, N, ACT, gs, s);
   if (M <= 8) {
     const int cus = device_cus();

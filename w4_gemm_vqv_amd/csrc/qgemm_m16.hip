@@ -59,15 +59,17 @@ struct M16Layout {
 // The staging writes whole batches of XB rounds of NW groups, so the image
 // area is padded to that many pairs; image GP (the last, or a padding image
 // that the loads fill with zeros) is the zero image of steps past a run.
-__host__ __device__ inline M16Layout m16_layout(int G, int WGC, int NW, int XB) {
+// HV (group 32, qgemm_w4_m16 only): row sums and table entries per 32-k
+// half, twice as many; table rows a multiple of 4 entries for 16-byte reads.
+__host__ __device__ inline M16Layout m16_layout(int G, int WGC, int NW, int XB, bool HV = false) {
   const int GP = (G + 1) >> 1;
   const int rounds = (2 * GP + NW - 1) / NW;
   const int padded = (rounds + XB - 1) / XB * XB * NW;
   const int nimg = GP + 1 > padded / 2 ? GP + 1 : padded / 2;
   M16Layout L{};
   L.xs = nimg * kPair16;
-  L.sb = L.xs + nimg * 32 * 4;                          // 2 groups x 16 rows per image
-  L.sbs = (G + 5) & ~1;                                  // >= G + 4, even: 8-byte reads
+  L.sb = L.xs + nimg * (HV ? 64 : 32) * 4;              // 2 groups (x 2 halves) x 16 rows
+  L.sbs = HV ? (2 * G + 7) & ~3 : (G + 5) & ~1;          // >= entries + 4; 16- or 8-byte reads
   L.red = L.sb + WGC * L.sbs * 4;
   L.runs = L.red + NW * 2 * 256 * 4;
   L.total = L.runs + NW * 2 * 4;
@@ -94,6 +96,24 @@ __device__ __forceinline__ u32x4 split_groups(const u32x4& w) {
 // One group pair for 16 rows: A[t] holds the activations whose codes sit in
 // dword t after split_groups (all 16 rows real). C0 collects group 2p, C1
 // group 2p+1.
+// Group 32: after split_groups one more swap, between lanes l and l + 16
+// (k slots 2i and 2i + 1), leaves every MFMA a single 32-k half of one group,
+// with k slot h holding k = 32 hh + 8h .. of half hh. A[t] holds the
+// activations of half t % 2 of group 2p + t / 2; C[t] collects them.
+template <bool F16>
+__device__ __forceinline__ void pair_step_halves(const u32x4 (&A)[4], const u32x4& w,
+                                                 unsigned magic, f32x4 (&C)[4]) {
+  const u32x4 v = split_groups(w);
+  const auto a = __builtin_amdgcn_permlane16_swap(v.x, v.y, false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(v.z, v.w, false, false);
+  const u32x4 bq0 = unpack_codes(a[0], magic), bq1 = unpack_codes(a[1], magic);
+  const u32x4 bq2 = unpack_codes(b[0], magic), bq3 = unpack_codes(b[1], magic);
+  C[0] = mfma16x16x32<F16>(A[0], bq0, C[0]);
+  C[2] = mfma16x16x32<F16>(A[2], bq2, C[2]);
+  C[1] = mfma16x16x32<F16>(A[1], bq1, C[1]);
+  C[3] = mfma16x16x32<F16>(A[3], bq3, C[3]);
+}
+
 template <bool F16>
 __device__ __forceinline__ void pair_step(const u32x4 (&A)[4], const u32x4& w, unsigned magic,
                                           f32x4& C0, f32x4& C1) {
@@ -114,7 +134,12 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     float* __restrict__ y, int M, int K, int N, int cols, int rsets, int workers) {
   using TR = ActTraits<ACT>;
-  constexpr int gs = GS;                            // group 64 << GS
+  // GS: group 64 << GS for GS >= 0; GS = -1 is group 32 (pair_step_halves:
+  // four partial sums per group pair, each with its own scale, bias and
+  // row sum).
+  constexpr int gs = GS > 0 ? GS : 0;               // table shift of group 128
+  constexpr bool HV = GS < 0;
+  constexpr int XSF = HV ? 64 : 32;                 // row sums per activation image
   static_assert(TR::parts == 1, "16-bit activations only");
   static_assert(TW <= NW, "a run must span at most two tiles");
   static_assert(NW >= 8, "the partial-sum slots double as a write sink");
@@ -151,7 +176,9 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
   const int bpt = GP / DB;
   const unsigned rowbytes = (unsigned)K >> 1;
   const int Nh = N >> 1;
-  const M16Layout L = m16_layout(G, WGC, NW, XB);
+  const M16Layout L = m16_layout(G, WGC, NW, XB, HV);
+  const int TG = HV ? 2 * G : G;                     // LDS table entries per column
+  const int ME = HV ? 2 * G : (G >> gs);             // table entries per row in memory
   unsigned char* xl = lds;
   float* xsl = reinterpret_cast<float*>(lds + L.xs);
   unsigned* sbl = reinterpret_cast<unsigned*>(lds + L.sb);
@@ -185,15 +212,20 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
   };
   // Values k = 8e8.. of group g feed MFMA t = 2(g&1) + e8%2 in the k slot h
   // whose lanes hold those codes after split_groups: sigma(h) = e8/2.
-  const unsigned xl_lane = (e8 & 1) * kTRow16 + (sigma_slot(e8 >> 1) * 16 + mm) * kSlot16;
+  // With HV (pair_step_halves) they feed MFMA 2(g&1) + e8/4 from k slot e8%4.
+  const unsigned xl_lane =
+      HV ? (e8 >> 2) * kTRow16 + ((e8 & 3) * 16 + mm) * kSlot16
+         : (e8 & 1) * kTRow16 + (sigma_slot(e8 >> 1) * 16 + mm) * kSlot16;
   auto x_store_round = [&](int bb, int i) {
     const int g = wave + NW * (bb + i);               // uniform
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const float s8 = sum8_lanes(block_sum<ACT>(xv[i][r]));
+      // Row sum over the group (8 lanes) or, with HV, over its half (4 lanes).
+      const float s8 = HV ? sum4_lanes(block_sum<ACT>(xv[i][r]))
+                          : sum8_lanes(block_sum<ACT>(xv[i][r]));
       *reinterpret_cast<u32x4*>(xl + (g >> 1) * kPair16 + (g & 1) * 2 * kTRow16 + xl_lane +
                                 r * 8 * kSlot16) = permute_pairs(xv[i][r]);
-      xsl[g * 16 + mm + 8 * r] = s8;
+      xsl[HV ? (g * 2 + (e8 >> 2)) * 16 + mm + 8 * r : g * 16 + mm + 8 * r] = s8;
     }
   };
   // SBV (host): K/64 a multiple of 8 and 16-byte aligned scale and bias
@@ -201,14 +233,14 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
   // a runtime branch: loads on either side of a branch make the compiler wait
   // for every load in flight, the staging loads included.
   constexpr bool sb_vec = SBV;
-  const unsigned g_recip = 0xFFFFFFFFu / (unsigned)G + 1u;
-  auto div_g = [&](unsigned e) { return G == 1 ? e : __umulhi(e, g_recip); };
+  const unsigned g_recip = 0xFFFFFFFFu / (unsigned)TG + 1u;
+  auto div_g = [&](unsigned e) { return TG == 1 ? e : __umulhi(e, g_recip); };
   const unsigned char* abase = xl + (h * 16 + j) * kSlot16;
   const float* xsbase = xsl + 4 * h;
   const unsigned* sbbase = sbl + j * L.sbs;
-  // Past a run: the zero image's row sums double as a zero (s, b) pair
-  // (8-byte aligned whatever G is).
-  const unsigned* sbzero = reinterpret_cast<const unsigned*>(xsl + GP * 32);
+  // Past a run: the zero image's row sums double as zero (s, b) entries
+  // (16-byte aligned whatever G is).
+  const unsigned* sbzero = reinterpret_cast<const unsigned*>(xsl + GP * XSF);
   auto rel_row = [&](int c) { return SWIGLU ? (c & 1) * Nh + (c >> 1) : c; };
   // Lane j of tile t reads logical column 16t + j: weight row rel_row(j) plus
   // the tile's rows (16 per tile, or 8 gate and 8 up rows with SWIGLU).
@@ -229,8 +261,12 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int i = tid; i < kPair16 / 16; i += NT)      // the zero image
       *reinterpret_cast<u32x4*>(xl + GP * kPair16 + 16 * i) = z;
-    if (tid < 32) xsl[GP * 32 + tid] = 0.0f;
-    for (int i = tid; i < WGC * 2; i += NT) sbl[(i >> 1) * L.sbs + G + (i & 1)] = 0u;
+    if (tid < XSF) xsl[GP * XSF + tid] = 0.0f;
+    if constexpr (HV) {
+      for (int i = tid; i < WGC * 4; i += NT) sbl[(i >> 2) * L.sbs + TG + (i & 3)] = 0u;
+    } else {
+      for (int i = tid; i < WGC * 2; i += NT) sbl[(i >> 1) * L.sbs + G + (i & 1)] = 0u;
+    }
   }
 
   for (int cg = wk; cg < ngroups; cg += workers) {
@@ -248,14 +284,14 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
         const_cast<uint8_t*>(wq) + (size_t)row0 * rowbytes, (short)0, nrows * rowbytes,
         kBufferFlags);
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(scales) + (size_t)row0 * (G >> gs), (short)0,
-        nrows * (G >> gs) * 2, kBufferFlags);
+        const_cast<uint16_t*>(scales) + (size_t)row0 * ME, (short)0, nrows * ME * 2,
+        kBufferFlags);
     const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(biases) + (size_t)row0 * (G >> gs), (short)0,
-        nrows * (G >> gs) * 2, kBufferFlags);
+        const_cast<uint16_t*>(biases) + (size_t)row0 * ME, (short)0, nrows * ME * 2,
+        kBufferFlags);
 
     // ---- scale/bias table: row n of the table is logical column n.
-    const int sb_units = sb_vec ? wgcols * G / 8 : wgcols * G;
+    const int sb_units = sb_vec ? wgcols * TG / 8 : wgcols * TG;
     u32x4 sbs[SBU], sbb[SBU];
     auto sb_load = [&](int round) {
 #pragma unroll
@@ -263,16 +299,16 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
         const int i = (round * SBU + u) * NT + tid;
         if constexpr (sb_vec) {
           const unsigned e0 = 8u * (unsigned)i;
-          const unsigned n = div_g(e0), g = e0 - n * (unsigned)G;
+          const unsigned n = div_g(e0), g = e0 - n * (unsigned)TG;
           const unsigned off =
-              i < sb_units ? 2u * (((unsigned)rel_row((int)n) * (unsigned)G + g) >> gs)
+              i < sb_units ? 2u * (((unsigned)rel_row((int)n) * (unsigned)TG + g) >> gs)
                            : kOutOfRange;
           sbs[u] = sb_unit_load<GS>(sr, off);
           sbb[u] = sb_unit_load<GS>(br, off);
         } else {
-          const unsigned n = div_g((unsigned)i), g = (unsigned)i - n * (unsigned)G;
+          const unsigned n = div_g((unsigned)i), g = (unsigned)i - n * (unsigned)TG;
           const unsigned off =
-              i < sb_units ? 2u * (((unsigned)rel_row((int)n) * (unsigned)G + g) >> gs)
+              i < sb_units ? 2u * (((unsigned)rel_row((int)n) * (unsigned)TG + g) >> gs)
                            : kOutOfRange;
           sbs[u].x = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
           sbb[u].x = __builtin_amdgcn_raw_buffer_load_b16(br, off, 0, 0);
@@ -286,7 +322,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
         const bool ok = i < sb_units;
         if constexpr (sb_vec) {
           const unsigned e0 = 8u * (unsigned)i;
-          const unsigned n = div_g(e0), g = e0 - n * (unsigned)G;
+          const unsigned n = div_g(e0), g = e0 - n * (unsigned)TG;
           u32x4 lo, hi;                               // (s_g | b_g << 16) for g .. g+7
           sb_pairs<GS>(sbs[u], sbb[u], lo, hi);
           // Units past the table write into the partial-sum slots (16 KB,
@@ -296,7 +332,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
           *reinterpret_cast<u32x4*>(lds + o) = lo;
           *reinterpret_cast<u32x4*>(lds + o + 16) = hi;
         } else if (ok) {
-          const unsigned n = div_g((unsigned)i), g = (unsigned)i - n * (unsigned)G;
+          const unsigned n = div_g((unsigned)i), g = (unsigned)i - n * (unsigned)TG;
           sbl[n * L.sbs + g] = (sbs[u].x & 0xFFFFu) | (sbb[u].x << 16);
         }
       }
@@ -358,10 +394,13 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
     __syncthreads();
 
     // ---- main loop.
+    // Row sums and (s, b) words of the step: of groups 2p, 2p+1, or with HV
+    // of their four halves.
+    constexpr int NQ = HV ? 4 : 2;
     struct Ops {
       u32x4 A[4];
-      f32x4 xs0, xs1;
-      u32x2 sb;
+      f32x4 xs[NQ];
+      unsigned sb[NQ];
     };
     struct Base {
       const unsigned char* a;
@@ -373,17 +412,26 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
       const int img = in ? k.p : GP;
       Base bs;
       bs.a = abase + img * kPair16;
-      bs.xs = xsbase + img * 32;
-      bs.sb = in ? sbbase + k.t * 16 * L.sbs + 2 * k.p : sbzero;
+      bs.xs = xsbase + img * XSF;
+      bs.sb = in ? sbbase + k.t * 16 * L.sbs + NQ * k.p : sbzero;
       return bs;
     };
     auto fetch = [&](const Base& bs, int d, Ops& o) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         o.A[t] = *reinterpret_cast<const u32x4*>(bs.a + d * kPair16 + t * kTRow16);
-      o.xs0 = *reinterpret_cast<const f32x4*>(bs.xs + d * 32);
-      o.xs1 = *reinterpret_cast<const f32x4*>(bs.xs + d * 32 + 16);
-      o.sb = *reinterpret_cast<const u32x2*>(bs.sb + 2 * d);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        o.xs[q] = *reinterpret_cast<const f32x4*>(bs.xs + d * XSF + 16 * q);
+      if constexpr (HV) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(bs.sb + 4 * d);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) o.sb[q] = v[q];
+      } else {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(bs.sb + 2 * d);
+        o.sb[0] = v.x;
+        o.sb[1] = v.y;
+      }
     };
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     int acc_tile = tfirst;
@@ -394,23 +442,29 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
         acc[e] = 0.0f;
       }
     };
-    auto epilogue = [&](const f32x4& C0, const f32x4& C1, const Ops& o) {
-      const float s0 = half_lo(o.sb.x), s1 = half_lo(o.sb.y);
-      const float c0 = fmaf(-TR::c0, s0, half_hi(o.sb.x));
-      const float c1 = fmaf(-TR::c0, s1, half_hi(o.sb.y));
+    struct Acc { f32x4 c[NQ]; };                    // a step's partial sums
+    auto epilogue = [&](const Acc& C, const Ops& o) {
+      float s[NQ], c[NQ];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] = fmaf(s0, C0[e], fmaf(c0, o.xs0[e], acc[e]));
-        acc[e] = fmaf(s1, C1[e], fmaf(c1, o.xs1[e], acc[e]));
+      for (int q = 0; q < NQ; ++q) {
+        s[q] = half_lo(o.sb[q]);
+        c[q] = fmaf(-TR::c0, s[q], half_hi(o.sb[q]));
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) acc[e] = fmaf(s[q], C.c[q][e], fmaf(c[q], o.xs[q][e], acc[e]));
     };
 
     Ops cur, prev;
     const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4 P0 = zero4, P1 = zero4;
-    prev.sb = u32x2{0u, 0u};                         // step -1 adds exactly nothing
-    prev.xs0 = zero4;
-    prev.xs1 = zero4;
+    Acc P;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      P.c[q] = zero4;
+      prev.sb[q] = 0u;                                // step -1 adds exactly nothing
+      prev.xs[q] = zero4;
+    }
     int prev_tile = tfirst;
     Blk kc = kfirst;
     Base bc = base_of(kc);
@@ -421,22 +475,26 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
       const unsigned so = codes_at(kl);
 #pragma unroll
       for (int d = 0; d < DB; ++d) {
-        f32x4 C0 = zero4, C1 = zero4;
-        pair_step<TR::f16>(cur.A, st[r * DB + d], magic, C0, C1);
+        Acc C;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) C.c[q] = zero4;
+        if constexpr (HV)
+          pair_step_halves<TR::f16>(cur.A, st[r * DB + d], magic, C.c);
+        else
+          pair_step<TR::f16>(cur.A, st[r * DB + d], magic, C.c[0], C.c[1]);
         Ops nxt;
         if (d + 1 < DB) fetch(bc, d + 1, nxt);
         else fetch(bn, 0, nxt);
         if (d == 0 && kc.t != prev_tile) {            // uniform: the last step ended a tile
-          epilogue(P0, P1, prev);
+          epilogue(P, prev);
           flush(0);
           acc_tile = kc.t;
           prev_tile = kc.t;
         } else {
-          epilogue(P0, P1, prev);
+          epilogue(P, prev);
         }
         if (reload) load(so, d, st[r * DB + d]);
-        P0 = C0;
-        P1 = C1;
+        P = C;
         prev = cur;
         cur = nxt;
       }
@@ -452,7 +510,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
 #pragma unroll
     for (int r = 0; r < RB - 1; ++r)
       if (i + r < nb) run_block(r, false);
-    epilogue(P0, P1, prev);
+    epilogue(P, prev);
     flush(acc_tile > tfirst ? 1 : 0);
 
     // ---- reduce: each output tile adds the flushed partials of the runs
@@ -842,16 +900,23 @@ hipError_t launch_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
   int workers = rsets > 1 ? (cus / rsets) / 8 * 8 : cus;
   if (workers < 8) workers = 8;
   if (rsets == 1 && workers > groups) workers = groups;
-  const M16Layout L = m16_layout(K >> 6, 16 * kM16Tiles, kM16Waves, kM16XB);
+  const M16Layout L = m16_layout(K >> 6, 16 * kM16Tiles, kM16Waves, kM16XB, gs < 0);
+  if (L.total > kLdsLimit) return hipErrorInvalidValue;  // never launched
   constexpr int D0 = DB;                                // one block ahead of the staging
-  const bool sbv = ((K >> 6) % 8) == 0 &&
+  const int tg = gs < 0 ? 2 * (K >> 6) : (K >> 6);      // table entries per column
+  const bool sbv = tg % 8 == 0 &&
                    ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(biases)) &
                     15) == 0;
-  auto kern =
-      sbv ? (gs ? qgemm_w4_m16<ACT, kM16Waves, kM16Tiles, DB, RB, D0, kM16XB, SWIGLU, true, 1>
-                : qgemm_w4_m16<ACT, kM16Waves, kM16Tiles, DB, RB, D0, kM16XB, SWIGLU, true, 0>)
-          : (gs ? qgemm_w4_m16<ACT, kM16Waves, kM16Tiles, DB, RB, D0, kM16XB, SWIGLU, false, 1>
-                : qgemm_w4_m16<ACT, kM16Waves, kM16Tiles, DB, RB, D0, kM16XB, SWIGLU, false, 0>);
+  constexpr int W = kM16Waves, T = kM16Tiles, X = kM16XB;
+  auto kern = qgemm_w4_m16<ACT, W, T, DB, RB, D0, X, SWIGLU, false, 0>;
+  if (sbv) {
+    kern = qgemm_w4_m16<ACT, W, T, DB, RB, D0, X, SWIGLU, true, 0>;
+    if (gs > 0) kern = qgemm_w4_m16<ACT, W, T, DB, RB, D0, X, SWIGLU, true, 1>;
+    if (gs < 0) kern = qgemm_w4_m16<ACT, W, T, DB, RB, D0, X, SWIGLU, true, -1>;
+  } else {
+    if (gs > 0) kern = qgemm_w4_m16<ACT, W, T, DB, RB, D0, X, SWIGLU, false, 1>;
+    if (gs < 0) kern = qgemm_w4_m16<ACT, W, T, DB, RB, D0, X, SWIGLU, false, -1>;
+  }
   if (L.total > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1224,17 +1289,17 @@ hipError_t launch_qgemm_wide(const void* x, const uint8_t* wq, const uint16_t* s
   return hipErrorInvalidValue;
 }
 
-bool qgemm_m16_fits(int M, int K, int act) {
+bool qgemm_m16_fits(int M, int K, int act, int gs) {
   // One batch of staging (K <= 64 * waves * XB) keeps the padded image small.
   return M <= 64 && act != ACT_FP32 && K <= 64 * kM16Waves * kM16XB &&
-         m16_layout(K >> 6, 16 * kM16Tiles, kM16Waves, kM16XB).total <= kLdsLimit;
+         m16_layout(K >> 6, 16 * kM16Tiles, kM16Waves, kM16XB, gs < 0).total <= kLdsLimit;
 }
 
 bool qgemm_swiglu_fused(int M, int K, int N, int act, int gs) {
   // The fused kernel's weight buffer spans the whole stacked weight from the
   // work-group's first gate row; it must stay below the scalar offset that
-  // reads as zero. Group 32 has no fused kernel.
-  return gs >= 0 && qgemm_m16_fits(M, K, act) && (size_t)N * (size_t)(K / 2) < 0x7F000000u;
+  // reads as zero.
+  return qgemm_m16_fits(M, K, act, gs) && (size_t)N * (size_t)(K / 2) < 0x7F000000u;
 }
 
 hipError_t launch_qgemm_m16(const void* x, const uint8_t* wq, const uint16_t* scales,

@@ -55,7 +55,7 @@ hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t*
 // 9..64 rows in row sets of 16 (bf16/fp16, K within the kernel's LDS
 // budget): qgemm_w4_m16 (qgemm_m16.hip). Whether it takes the problem, and
 // the launch.
-bool qgemm_m16_fits(int M, int K, int act);
+bool qgemm_m16_fits(int M, int K, int act, int gs);
 hipError_t launch_qgemm_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
                             const uint16_t* biases, float* y, int M, int K, int N, int act,
                             int gs, hipStream_t stream);
