@@ -70,9 +70,9 @@ def projection_kernel(M, K, N, act, cus, group=64):
     if act == "fp32":
         return "qgemm_w4"
     tpw = (T + cus - 1) // cus
-    if group != 32:  # group 32 takes qgemm_w4_m8, qgemm_w4_m16 or the generic kernel
-        if 16 < M <= 64 and K % 128 == 0 and N * (K // 2) < 0x7F000000 and 8 <= tpw <= 40:
-            return "qgemm_w4_rows"
+    if 16 < M <= 64 and K % 128 == 0 and N * (K // 2) < 0x7F000000 and 8 <= tpw <= 40:
+        return "qgemm_w4_rows"
+    if group != 32:  # group 32 has no whole-tile kernel
         workers = max(8, (cus // rsets) // 8 * 8) if rsets > 1 else cus
         if (M <= 64 and K <= 2560 and G % 8 == 0 and N * (K // 2) < 0x7F000000
                 and T >= 16 * workers):

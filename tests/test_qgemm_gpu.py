@@ -109,8 +109,8 @@ def test_group128_equals_group64_twice(vqv, act, M, K, N):
     np.testing.assert_array_equal(y128, run(vqv, c64))
 
 
-# Group 32 runs on the 8-row kernel (M <= 8), the 16-row kernel (9..64 rows,
-# K <= 2560) and the generic kernel in every configuration its dispatch
+# Group 32 runs on the 8-row kernel (M <= 8), the 16-row and row-set kernels
+# (9..64 rows) and the generic kernel in every configuration its dispatch
 # takes: one row set with the whole K range staged (64-80 column shares and
 # wide N), narrow outputs, chunked staging at large K, two, four and eight row
 # sets, the small fallbacks, and an odd count of 64-groups.
@@ -124,6 +124,9 @@ SHAPES_G32 = [
     # The 16-row kernel: one to four row sets, several tiles per work-group,
     # K at its staging limit, 16-bit table loads (K/32 not a multiple of 8).
     (16, 512, 5000), (12, 2560, 17408), (64, 2560, 5000), (48, 1280, 3001), (33, 384, 9000),
+    # The row-set kernel at vocabulary widths: two, three and four row sets,
+    # whole and partial chunks, ragged last tile and row set.
+    (64, 2560, 70000), (40, 1280, 40001), (17, 768, 33000), (33, 384, 36000),
 ]
 
 

@@ -1071,19 +1071,17 @@ template <int ACT>
 hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                          const uint16_t* biases, float* y, int M, int K, int N, int gs,
                          hipStream_t s) {
-  // Group 32 (gs < 0) runs on qgemm_w4_m8 (M <= 8), qgemm_w4_m16 or the
-  // generic kernel.
-  if (gs >= 0) {
-    if constexpr (ACT != ACT_FP32) if (qgemm_rows_fits(M, K, N, ACT)) {
-      // 17..64 rows at vocabulary widths: all row sets on one weight stream.
-      return launch_qgemm_rows(x, wq, scales, biases, y, M, K, N, ACT, gs, s);
-    }
-    if (qgemm_wide_fits(M, K, N, ACT)) {
-      // Vocabulary widths: whole-tile waves (the fused verify's projection
-      // takes the same kernel, so the two paths agree bit for bit).
-      const VerifyArgs none{};
-      return launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, ACT, gs, none, s);
-    }
+  if constexpr (ACT != ACT_FP32) if (qgemm_rows_fits(M, K, N, ACT)) {
+    // 17..64 rows at vocabulary widths: all row sets on one weight stream.
+    return launch_qgemm_rows(x, wq, scales, biases, y, M, K, N, ACT, gs, s);
+  }
+  // Group 32 (gs < 0) has no whole-tile kernel: vocabulary widths at M <= 8
+  // take qgemm_w4_m8.
+  if (gs >= 0 && qgemm_wide_fits(M, K, N, ACT)) {
+    // Vocabulary widths: whole-tile waves (the fused verify's projection
+    // takes the same kernel, so the two paths agree bit for bit).
+    const VerifyArgs none{};
+    return launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, ACT, gs, none, s);
   }
   if constexpr (ACT != ACT_FP32) if (M <= 8 && m8_fits(K, gs)) {
     const VerifyArgs none{};

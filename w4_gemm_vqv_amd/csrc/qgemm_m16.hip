@@ -36,6 +36,8 @@
 // gate and up values of one hidden unit land in adjacent output columns of
 // the same tile and the final reduction pairs them.
 
+#include <type_traits>
+
 #include "argmax.h"
 #include "qgemm_common.h"
 #include "vqv_internal.h"
@@ -989,7 +991,13 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     float* __restrict__ y, int M, int K, int N, int tpw) {
   using TR = ActTraits<ACT>;
-  constexpr int gs = GS;                            // group 64 << GS
+  // GS: group 64 << GS for GS >= 0; GS = -1 is group 32 (as in
+  // qgemm_w4_m16: four partial sums per pair and row set, one per group
+  // half, each with its own scale, bias and row sum).
+  constexpr int gs = GS > 0 ? GS : 0;               // table shift of group 128
+  constexpr bool HV = GS < 0;
+  constexpr int NQ = HV ? 4 : 2;                    // scaled partial sums per pair
+  constexpr int XSF = 16 * NQ;                      // row sums per image
   static_assert(TR::parts == 1, "16-bit activations only");
   constexpr int NW = 8;
   constexpr int RH = RS >= 4 ? 1 : (RS < 2 ? RS : 2);  // row sets whose A stays in registers
@@ -1002,8 +1010,8 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
 
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char* ximg = lds;                                        // [KCP][RS] images
-  float* xsl = reinterpret_cast<float*>(lds + KCP * RS * kPair16);  // [KCP][RS][2][16]
-  unsigned* tab_all = reinterpret_cast<unsigned*>(lds + KCP * RS * (kPair16 + 128));
+  float* xsl = reinterpret_cast<float*>(lds + KCP * RS * kPair16);  // [KCP][RS][NQ][16]
+  unsigned* tab_all = reinterpret_cast<unsigned*>(lds + KCP * RS * (kPair16 + 4 * XSF));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1017,7 +1025,8 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
   const int T = (N + 15) >> 4;
   const int tbeg = blockIdx.x * tpw;
   const int tend = min(T, tbeg + tpw);
-  unsigned* tab = tab_all + wave * KT * 16 * GC;     // [KT][16 columns][GC] of (s | b << 16)
+  // [KT][16 columns][NQ * KCP] of (s | b << 16)
+  unsigned* tab = tab_all + wave * KT * 16 * NQ * KCP;
 
   unsigned magic;
   asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(TR::magic));
@@ -1025,10 +1034,11 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
       const_cast<void*>(x), (short)0, M * K * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(wq), (short)0, (unsigned)N * rowbytes, kBufferFlags);
+  const unsigned ME = HV ? 2u * (unsigned)G : (unsigned)(G >> gs);  // table entries per row
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(scales), (short)0, (unsigned)N * (G >> gs) * 2, kBufferFlags);
+      const_cast<uint16_t*>(scales), (short)0, (unsigned)N * ME * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(biases), (short)0, (unsigned)N * (G >> gs) * 2, kBufferFlags);
+      const_cast<uint16_t*>(biases), (short)0, (unsigned)N * ME * 2, kBufferFlags);
 
   // This wave's tiles (uniform): tile k is tbeg + wave + 8k while below tend.
   int tile[KT];
@@ -1058,7 +1068,9 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
 
   const int e8 = lane & 7;
   const int mm = lane >> 3;
-  const unsigned xl_lane = (e8 & 1) * kTRow16 + (sigma_slot(e8 >> 1) * 16 + mm) * kSlot16;
+  const unsigned xl_lane =
+      HV ? (e8 >> 2) * kTRow16 + ((e8 & 3) * 16 + mm) * kSlot16
+         : (e8 & 1) * kTRow16 + (sigma_slot(e8 >> 1) * 16 + mm) * kSlot16;
 
   for (int c = 0; c < nch; ++c) {
     if (c > 0) __syncthreads();                      // chunk c-1's image and tables are read
@@ -1075,23 +1087,33 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
       xv[i] = __builtin_amdgcn_raw_buffer_load_b128(
           xr, ok ? (unsigned)((row * K + kk) * 2) : kOutOfRange, 0, 0);
     }
-    unsigned ts[TABL], tb[TABL];
+    // One dword per entry pair, two with HV (four entries).
+    using TabWord = std::conditional_t<HV, u32x2, unsigned>;
+    TabWord ts[TABL], tb[TABL];
 #pragma unroll
     for (int n = 0; n < TABL; ++n) {
       const int e = 64 * n + lane;
       const int k = e / (16 * KCP), jj = (e / KCP) % 16, d = e % KCP;
       const int col = (tbeg + wave + NW * k) * 16 + jj;
       const bool ok = e < TABD && tbeg + wave + NW * k < tend && col < N && c * KCP + d < GP;
-      // Entries of groups 2d and 2d+1 of the chunk: one 32-bit load, or the
-      // one entry of their 128-group twice.
-      const unsigned e0 = ((unsigned)col * (unsigned)G + (unsigned)(c * GC + 2 * d)) >> gs;
-      const unsigned off = ok ? 2u * e0 : kOutOfRange;
-      if constexpr (GS == 0) {
-        ts[n] = __builtin_amdgcn_raw_buffer_load_b32(sr, off, 0, 0);
-        tb[n] = __builtin_amdgcn_raw_buffer_load_b32(br, off, 0, 0);
+      // Entries of groups 2d and 2d+1 of the chunk: one 32-bit load, the one
+      // entry of their 128-group twice, or (HV) the four entries of their
+      // halves in one 64-bit load.
+      if constexpr (HV) {
+        const unsigned e0 = (unsigned)col * ME + 4u * (unsigned)(c * KCP + d);
+        const unsigned off = ok ? 2u * e0 : kOutOfRange;
+        ts[n] = __builtin_amdgcn_raw_buffer_load_b64(sr, off, 0, 0);
+        tb[n] = __builtin_amdgcn_raw_buffer_load_b64(br, off, 0, 0);
       } else {
-        ts[n] = 0x10001u * (unsigned)__builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
-        tb[n] = 0x10001u * (unsigned)__builtin_amdgcn_raw_buffer_load_b16(br, off, 0, 0);
+        const unsigned e0 = ((unsigned)col * (unsigned)G + (unsigned)(c * GC + 2 * d)) >> gs;
+        const unsigned off = ok ? 2u * e0 : kOutOfRange;
+        if constexpr (GS == 0) {
+          ts[n] = __builtin_amdgcn_raw_buffer_load_b32(sr, off, 0, 0);
+          tb[n] = __builtin_amdgcn_raw_buffer_load_b32(br, off, 0, 0);
+        } else {
+          ts[n] = 0x10001u * (unsigned)__builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
+          tb[n] = 0x10001u * (unsigned)__builtin_amdgcn_raw_buffer_load_b16(br, off, 0, 0);
+        }
       }
     }
 #pragma unroll
@@ -1100,19 +1122,27 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
       if (it >= ITEMS) continue;                     // uniform: the last round is partial
       const int gl = it / (2 * RS), ro = it % (2 * RS);
       const int r = ro >> 1, r8 = ro & 1;
-      const float s8 = sum8_lanes(block_sum<ACT>(xv[i]));
+      const float s8 = HV ? sum4_lanes(block_sum<ACT>(xv[i])) : sum8_lanes(block_sum<ACT>(xv[i]));
       *reinterpret_cast<u32x4*>(ximg + ((gl >> 1) * RS + r) * kPair16 + (gl & 1) * 2 * kTRow16 +
                                 xl_lane + r8 * 8 * kSlot16) = permute_pairs(xv[i]);
-      xsl[((gl >> 1) * RS + r) * 32 + (gl & 1) * 16 + mm + 8 * r8] = s8;
+      const int q = HV ? (gl & 1) * 2 + (e8 >> 2) : (gl & 1);  // partial sum of the values
+      xsl[((gl >> 1) * RS + r) * XSF + q * 16 + mm + 8 * r8] = s8;
     }
 #pragma unroll
     for (int n = 0; n < TABL; ++n) {
       const int e = 64 * n + lane;
       if (e < TABD) {
         const int k = e / (16 * KCP), jj = (e / KCP) % 16, d = e % KCP;
-        unsigned* q = tab + (k * 16 + jj) * GC + 2 * d;
-        q[0] = __builtin_amdgcn_perm(tb[n], ts[n], 0x05040100u);
-        q[1] = __builtin_amdgcn_perm(tb[n], ts[n], 0x07060302u);
+        unsigned* q = tab + (k * 16 + jj) * (NQ * KCP) + NQ * d;
+        if constexpr (HV) {
+          q[0] = __builtin_amdgcn_perm(tb[n].x, ts[n].x, 0x05040100u);
+          q[1] = __builtin_amdgcn_perm(tb[n].x, ts[n].x, 0x07060302u);
+          q[2] = __builtin_amdgcn_perm(tb[n].y, ts[n].y, 0x05040100u);
+          q[3] = __builtin_amdgcn_perm(tb[n].y, ts[n].y, 0x07060302u);
+        } else {
+          q[0] = __builtin_amdgcn_perm(tb[n], ts[n], 0x05040100u);
+          q[1] = __builtin_amdgcn_perm(tb[n], ts[n], 0x07060302u);
+        }
       }
     }
     __syncthreads();
@@ -1142,29 +1172,60 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
             wr, woff, p + 1 < KCP ? codes_at(c, p + 1, k) : codes_at(c + 1, 0, k), 0);
         const u32x4 v = split_groups(w);
         u32x4 bq[4];
+        float sq[NQ], cq[NQ];
+        if constexpr (HV) {
+          // One more swap per group: MFMA q sees half q % 2 of group 2p + q / 2.
+          const auto a = __builtin_amdgcn_permlane16_swap(v.x, v.y, false, false);
+          const auto b = __builtin_amdgcn_permlane16_swap(v.z, v.w, false, false);
+          bq[0] = unpack_codes(a[0], magic);
+          bq[1] = unpack_codes(a[1], magic);
+          bq[2] = unpack_codes(b[0], magic);
+          bq[3] = unpack_codes(b[1], magic);
+          const u32x4 sb = *reinterpret_cast<const u32x4*>(tab + (k * 16 + j) * (NQ * KCP) + NQ * p);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) bq[t] = unpack_codes(v[t], magic);
-        const u32x2 sb = *reinterpret_cast<const u32x2*>(tab + (k * 16 + j) * GC + 2 * p);
-        const float s0 = half_lo(sb.x), s1 = half_lo(sb.y);
-        const float c0 = fmaf(-TR::c0, s0, half_hi(sb.x));
-        const float c1 = fmaf(-TR::c0, s1, half_hi(sb.y));
+          for (int q = 0; q < NQ; ++q) {
+            sq[q] = half_lo(sb[q]);
+            cq[q] = fmaf(-TR::c0, sq[q], half_hi(sb[q]));
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) bq[t] = unpack_codes(v[t], magic);
+          const u32x2 sb = *reinterpret_cast<const u32x2*>(tab + (k * 16 + j) * GC + 2 * p);
+          sq[0] = half_lo(sb.x);
+          sq[1] = half_lo(sb.y);
+          cq[0] = fmaf(-TR::c0, sq[0], half_hi(sb.x));
+          cq[1] = fmaf(-TR::c0, sq[1], half_hi(sb.y));
+        }
 #pragma unroll
         for (int r = 0; r < RS; ++r) {
           const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
           u32x4 Ar[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) Ar[t] = r < RH ? A[r < RH ? r : 0][t] : a_of(r, t, a_step);
-          f32x4 C0 = mfma16x16x32<TR::f16>(Ar[0], bq[0], zero4);
-          f32x4 C1 = mfma16x16x32<TR::f16>(Ar[2], bq[2], zero4);
-          C0 = mfma16x16x32<TR::f16>(Ar[1], bq[1], C0);
-          C1 = mfma16x16x32<TR::f16>(Ar[3], bq[3], C1);
-          const float* xs = xsl + (p * RS + r) * 32 + x_step;
-          const f32x4 xs0 = *reinterpret_cast<const f32x4*>(xs);
-          const f32x4 xs1 = *reinterpret_cast<const f32x4*>(xs + 16);
+          const float* xs = xsl + (p * RS + r) * XSF + x_step;
+          if constexpr (HV) {
+            f32x4 C[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[k][r][e] = fmaf(s0, C0[e], fmaf(c0, xs0[e], acc[k][r][e]));
-            acc[k][r][e] = fmaf(s1, C1[e], fmaf(c1, xs1[e], acc[k][r][e]));
+            for (int q = 0; q < 4; ++q) C[q] = mfma16x16x32<TR::f16>(Ar[q], bq[q], zero4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 xq = *reinterpret_cast<const f32x4*>(xs + 16 * q);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[k][r][e] = fmaf(sq[q], C[q][e], fmaf(cq[q], xq[e], acc[k][r][e]));
+            }
+          } else {
+            f32x4 C0 = mfma16x16x32<TR::f16>(Ar[0], bq[0], zero4);
+            f32x4 C1 = mfma16x16x32<TR::f16>(Ar[2], bq[2], zero4);
+            C0 = mfma16x16x32<TR::f16>(Ar[1], bq[1], C0);
+            C1 = mfma16x16x32<TR::f16>(Ar[3], bq[3], C1);
+            const f32x4 xs0 = *reinterpret_cast<const f32x4*>(xs);
+            const f32x4 xs1 = *reinterpret_cast<const f32x4*>(xs + 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[k][r][e] = fmaf(sq[0], C0[e], fmaf(cq[0], xs0[e], acc[k][r][e]));
+              acc[k][r][e] = fmaf(sq[1], C1[e], fmaf(cq[1], xs1[e], acc[k][r][e]));
+            }
           }
         }
       }
@@ -1186,9 +1247,9 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
   }
 }
 
-template <int RS, int KT, int KCP>
+template <int RS, int KT, int KCP, bool HV>
 constexpr int rows_lds_bytes() {
-  return KCP * RS * (kPair16 + 128) + 8 * KT * 16 * 2 * KCP * 4;
+  return KCP * RS * (kPair16 + (HV ? 256 : 128)) + 8 * KT * 16 * (HV ? 4 : 2) * KCP * 4;
 }
 
 constexpr int kRowsKT = 5;
@@ -1198,9 +1259,12 @@ template <int ACT, int RS>
 hipError_t launch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                        const uint16_t* biases, float* y, int M, int K, int N, int gs,
                        hipStream_t stream) {
-  constexpr int lds_bytes = rows_lds_bytes<RS, kRowsKT, kRowsKCP>();
-  auto kern = gs ? qgemm_w4_rows<ACT, RS, kRowsKT, kRowsKCP, 1>
-                 : qgemm_w4_rows<ACT, RS, kRowsKT, kRowsKCP, 0>;
+  const int lds_bytes = gs < 0 ? rows_lds_bytes<RS, kRowsKT, kRowsKCP, true>()
+                              : rows_lds_bytes<RS, kRowsKT, kRowsKCP, false>();
+  static_assert(rows_lds_bytes<4, kRowsKT, kRowsKCP, true>() <= kLdsLimit, "LDS budget");
+  auto kern = qgemm_w4_rows<ACT, RS, kRowsKT, kRowsKCP, 0>;
+  if (gs > 0) kern = qgemm_w4_rows<ACT, RS, kRowsKT, kRowsKCP, 1>;
+  if (gs < 0) kern = qgemm_w4_rows<ACT, RS, kRowsKT, kRowsKCP, -1>;
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
