@@ -72,11 +72,10 @@ def projection_kernel(M, K, N, act, cus, group=64):
     tpw = (T + cus - 1) // cus
     if 16 < M <= 64 and K % 128 == 0 and N * (K // 2) < 0x7F000000 and 8 <= tpw <= 40:
         return "qgemm_w4_rows"
-    if group != 32:  # group 32 has no whole-tile kernel
-        workers = max(8, (cus // rsets) // 8 * 8) if rsets > 1 else cus
-        if (M <= 64 and K <= 2560 and G % 8 == 0 and N * (K // 2) < 0x7F000000
-                and T >= 16 * workers):
-            return "qgemm_w4_wide"
+    workers = max(8, (cus // rsets) // 8 * 8) if rsets > 1 else cus
+    if (M <= 64 and K <= 2560 and G % 8 == 0 and N * (K // 2) < 0x7F000000
+            and T >= 16 * workers and (group != 32 or (G // 2) % 4 == 0)):
+        return "qgemm_w4_wide"
     if M <= 8 and K <= 5120:
         return "qgemm_w4_m8"
     if M <= 64 and K <= 2560:

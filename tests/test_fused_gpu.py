@@ -105,10 +105,12 @@ def test_group128_matches_separate(vqv, M, K, N, act, B, T):
 @pytest.mark.parametrize("M,K,N,act,B,T", [
     (8, 512, 1024, "bf16", 1, 8), (8, 5120, 17408, "bf16", 1, 8), (4, 1280, 3000, "fp16", 2, 2),
     (16, 512, 1000, "fp32", 1, 16), (8, 2560, 151936, "fp16", 1, 8), (1, 64, 17, "bf16", 1, 1),
+    (8, 512, 70000, "bf16", 2, 4), (8, 1280, 70000, "bf16", 1, 8),
 ])
 def test_group32_matches_separate(vqv, M, K, N, act, B, T):
-    """Group 32: the 8-row kernel's fused epilogue (M <= 8, 16-bit activations, at
-    vocabulary widths too) or the two-kernel path (fp32, M > 8)."""
+    """Group 32: the fused epilogue of the whole-tile kernel (vocabulary widths,
+    K/128 a multiple of 4) or of the 8-row kernel (M <= 8, 16-bit activations),
+    or the two-kernel path (fp32, M > 8)."""
     c = case(M, K, N, act, seed=M * 13 + K + N, group=32)
     y, _, _ = compare(vqv, c, B, T)
     ref = qgemm_ref(c["x"], act, c["wq"], c["scales"], c["biases"], group=32)

@@ -109,8 +109,8 @@ def test_group128_equals_group64_twice(vqv, act, M, K, N):
     np.testing.assert_array_equal(y128, run(vqv, c64))
 
 
-# Group 32 runs on the 8-row kernel (M <= 8), the 16-row and row-set kernels
-# (9..64 rows) and the generic kernel in every configuration its dispatch
+# Group 32 runs on the 8-row kernel (M <= 8), the 16-row, row-set and
+# whole-tile kernels and the generic kernel in every configuration its dispatch
 # takes: one row set with the whole K range staged (64-80 column shares and
 # wide N), narrow outputs, chunked staging at large K, two, four and eight row
 # sets, the small fallbacks, and an odd count of 64-groups.
@@ -127,6 +127,9 @@ SHAPES_G32 = [
     # The row-set kernel at vocabulary widths: two, three and four row sets,
     # whole and partial chunks, ragged last tile and row set.
     (64, 2560, 70000), (40, 1280, 40001), (17, 768, 33000), (33, 384, 36000),
+    # The whole-tile kernel (K/128 a multiple of 4): one row set, a ragged
+    # last tile.
+    (8, 512, 70000), (16, 1024, 66000), (12, 2560, 66001),
 ]
 
 

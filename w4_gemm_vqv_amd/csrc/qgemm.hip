@@ -1075,9 +1075,7 @@ hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scale
     // 17..64 rows at vocabulary widths: all row sets on one weight stream.
     return launch_qgemm_rows(x, wq, scales, biases, y, M, K, N, ACT, gs, s);
   }
-  // Group 32 (gs < 0) has no whole-tile kernel: vocabulary widths at M <= 8
-  // take qgemm_w4_m8.
-  if (gs >= 0 && qgemm_wide_fits(M, K, N, ACT)) {
+  if (qgemm_wide_fits(M, K, N, ACT, gs)) {
     // Vocabulary widths: whole-tile waves (the fused verify's projection
     // takes the same kernel, so the two paths agree bit for bit).
     const VerifyArgs none{};
@@ -1139,9 +1137,9 @@ int qgemm_verify_groups(int M, int K, int N, int act, int gs) {
   // The projection kernel of the fused path writes one partial per
   // work-group and row; verify_finish (verify.hip) reduces them. Vocabulary widths
   // take the persistent whole-tile kernel (one partial per CU and row
-  // instead of one per 80 columns). Group 32 takes qgemm_w4_m8 only.
+  // instead of one per 80 columns).
   if (M > 8 || act == ACT_FP32) return 0;
-  if (gs >= 0 && qgemm_wide_fits(M, K, N, act)) return qgemm_wide_groups(M);
+  if (qgemm_wide_fits(M, K, N, act, gs)) return qgemm_wide_groups(M);
   if (!m8_fits(K, gs)) return 0;
   const int cols = m8_cols(N);
   return (N + cols - 1) / cols;
@@ -1151,7 +1149,7 @@ hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t*
                                const uint16_t* biases, float* y, int M, int K, int N, int act,
                                int gs, const VerifyArgs& va, hipStream_t stream) {
   hipError_t e = hipErrorInvalidValue;
-  if (gs >= 0 && qgemm_wide_fits(M, K, N, act))
+  if (qgemm_wide_fits(M, K, N, act, gs))
     e = launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, act, gs, va, stream);
   else if (act == ACT_BF16)
     e = launch_m8_any<ACT_BF16>(x, wq, scales, biases, y, M, K, N, gs, va, stream);

@@ -582,7 +582,13 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
     float* __restrict__ y, int M, int K, int N, int rsets, int workers, int tpw,
     VerifyArgs va) {
   using TR = ActTraits<ACT>;
-  constexpr int gs = GS;                            // group 64 << GS
+  // GS: group 64 << GS for GS >= 0; GS = -1 is group 32 (as in
+  // qgemm_w4_m16: pair_step_halves, four partial sums per group pair).
+  constexpr int gs = GS > 0 ? GS : 0;               // table shift of group 128
+  constexpr bool HV = GS < 0;
+  constexpr int NQ = HV ? 4 : 2;                    // scaled partial sums per pair
+  constexpr int XSF = 16 * NQ;                      // row sums per activation image
+  constexpr int NTR = HV ? 3 : 2;                   // table load rounds (K <= 2560, host)
   static_assert(TR::parts == 1, "16-bit activations only");
   constexpr int NW = 8, NT = 512, XB = 5;
   const bool fused = va.argmax != nullptr;           // uniform
@@ -616,11 +622,12 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
   const int GP = G >> 1;
   const int bpt = GP / DB;
   const unsigned rowbytes = (unsigned)K >> 1;
-  const M16Layout L = m16_layout(G, 16, NW, XB);
+  const M16Layout L = m16_layout(G, 16, NW, XB, HV);
+  const int TG = HV ? 2 * G : G;                      // table entries per column
   unsigned char* xl = lds;
   float* xsl = reinterpret_cast<float*>(lds + L.xs);
-  // Per-wave table: [16 columns][G] of (s | b << 16), after the row sums.
-  unsigned* tab = reinterpret_cast<unsigned*>(lds + L.sb) + wave * 16 * G;
+  // Per-wave table: [16 columns][TG] of (s | b << 16), after the row sums.
+  unsigned* tab = reinterpret_cast<unsigned*>(lds + L.sb) + wave * 16 * TG;
 
   unsigned magic;
   asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(TR::magic));
@@ -628,10 +635,11 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
       const_cast<void*>(x), (short)0, M * K * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(wq), (short)0, (unsigned)N * rowbytes, kBufferFlags);
+  const unsigned ME = HV ? 2u * (unsigned)G : (unsigned)(G >> gs);  // table entries per row
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(scales), (short)0, (unsigned)N * (G >> gs) * 2, kBufferFlags);
+      const_cast<uint16_t*>(scales), (short)0, (unsigned)N * ME * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(biases), (short)0, (unsigned)N * (G >> gs) * 2, kBufferFlags);
+      const_cast<uint16_t*>(biases), (short)0, (unsigned)N * ME * 2, kBufferFlags);
 
   // ---- this wave's tiles and blocks: tile ordinal k is column tile
   // tbeg + wave + 8k; block (k, p) covers pairs p .. p + DB - 1.
@@ -656,25 +664,25 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
   auto load = [&](unsigned so, int d, u32x4& w) {
     w = __builtin_amdgcn_raw_buffer_load_b128(wr, woff + 64u * d, so, 0);
   };
-  // A tile's table: 16 columns x G groups, contiguous in memory; unit u (16
-  // bytes, groups 8(u % (G/8)) ..) of each array per lane and round.
-  const int tunits = 2 * G;                           // 16 * G / 8
-  u32x4 ts[2], tb[2];
+  // A tile's table: 16 columns x TG entries, contiguous in memory; unit u
+  // (16 bytes, entries 8(u % (TG/8)) ..) of each array per lane and round.
+  const int tunits = 2 * TG;                          // 16 * TG / 8
+  u32x4 ts[NTR], tb[NTR];
   auto tab_load = [&](int k) {                        // k may be past the run: zeros
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < NTR; ++r) {
       const int u = r * 64 + lane;
-      const int c = col0(k) + (8 * u) / G;
+      const int c = col0(k) + (8 * u) / TG;
       const bool ok = k < ntile && u < tunits && c < N;
       const unsigned off =
-          ok ? 2u * (((unsigned)col0(k) * (unsigned)G + 8u * (unsigned)u) >> gs) : kOutOfRange;
+          ok ? 2u * (((unsigned)col0(k) * (unsigned)TG + 8u * (unsigned)u) >> gs) : kOutOfRange;
       ts[r] = sb_unit_load<GS>(sr, off);
       tb[r] = sb_unit_load<GS>(br, off);
     }
   };
   auto tab_store = [&]() {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < NTR; ++r) {
       const int u = r * 64 + lane;
       if (u < tunits) {
         u32x4 lo, hi;
@@ -713,23 +721,26 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
     if (d % DB == DB - 1) kl = next(kl);
   }
   (void)rounds;
-  const unsigned xl_lane = (e8 & 1) * kTRow16 + (sigma_slot(e8 >> 1) * 16 + mm) * kSlot16;
+  const unsigned xl_lane =
+      HV ? (e8 >> 2) * kTRow16 + ((e8 & 3) * 16 + mm) * kSlot16
+         : (e8 & 1) * kTRow16 + (sigma_slot(e8 >> 1) * 16 + mm) * kSlot16;
 #pragma unroll
   for (int i = 0; i < XB; ++i) {
     const int g = wave + NW * i;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const float s8 = sum8_lanes(block_sum<ACT>(xv[i][r]));
+      const float s8 = HV ? sum4_lanes(block_sum<ACT>(xv[i][r]))
+                          : sum8_lanes(block_sum<ACT>(xv[i][r]));
       *reinterpret_cast<u32x4*>(xl + (g >> 1) * kPair16 + (g & 1) * 2 * kTRow16 + xl_lane +
                                 r * 8 * kSlot16) = permute_pairs(xv[i][r]);
-      xsl[g * 16 + mm + 8 * r] = s8;
+      xsl[HV ? (g * 2 + (e8 >> 2)) * 16 + mm + 8 * r : g * 16 + mm + 8 * r] = s8;
     }
   }
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int i = tid; i < kPair16 / 16; i += NT)      // the zero image
       *reinterpret_cast<u32x4*>(xl + GP * kPair16 + 16 * i) = z;
-    if (tid < 32) xsl[GP * 32 + tid] = 0.0f;
+    if (tid < XSF) xsl[GP * XSF + tid] = 0.0f;
   }
   tab_store();
   tab_load(1);
@@ -738,13 +749,20 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
   // ---- main loop (the step, ring and deferred epilogue of qgemm_w4_m16).
   const unsigned char* abase = xl + (h * 16 + j) * kSlot16;
   const float* xsbase = xsl + 4 * h;
-  const unsigned* tbase = tab + j * G;
-  const unsigned* sbzero = reinterpret_cast<const unsigned*>(xsl + GP * 32);
-  struct Ops {
+  const unsigned* tbase = tab + j * TG;
+  const unsigned* sbzero = reinterpret_cast<const unsigned*>(xsl + GP * XSF);
+  // The step's operands: of groups 2p and 2p+1, or (HV) of their halves.
+  struct OpsG {
     u32x4 A[4];
     f32x4 xs0, xs1;
     u32x2 sb;
   };
+  struct OpsH {
+    u32x4 A[4];
+    f32x4 xs[4];
+    u32x4 sb;
+  };
+  using Ops = std::conditional_t<HV, OpsH, OpsG>;
   struct Base {
     const unsigned char* a;
     const float* xs;
@@ -755,17 +773,24 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
     const int img = in ? b.p : GP;
     Base bs;
     bs.a = abase + img * kPair16;
-    bs.xs = xsbase + img * 32;
-    bs.sb = in ? tbase + 2 * b.p : sbzero;
+    bs.xs = xsbase + img * XSF;
+    bs.sb = in ? tbase + NQ * b.p : sbzero;
     return bs;
   };
   auto fetch = [&](const Base& bs, int d, Ops& o) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       o.A[t] = *reinterpret_cast<const u32x4*>(bs.a + d * kPair16 + t * kTRow16);
-    o.xs0 = *reinterpret_cast<const f32x4*>(bs.xs + d * 32);
-    o.xs1 = *reinterpret_cast<const f32x4*>(bs.xs + d * 32 + 16);
-    o.sb = *reinterpret_cast<const u32x2*>(bs.sb + 2 * d);
+    if constexpr (HV) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o.xs[q] = *reinterpret_cast<const f32x4*>(bs.xs + d * XSF + 16 * q);
+      o.sb = *reinterpret_cast<const u32x4*>(bs.sb + 4 * d);
+    } else {
+      o.xs0 = *reinterpret_cast<const f32x4*>(bs.xs + d * 32);
+      o.xs1 = *reinterpret_cast<const f32x4*>(bs.xs + d * 32 + 16);
+      o.sb = *reinterpret_cast<const u32x2*>(bs.sb + 2 * d);
+    }
   };
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   Top2 best[4] = {top2_none(), top2_none(), top2_none(), top2_none()};
@@ -783,23 +808,45 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
       acc[e] = 0.0f;
     }
   };
-  auto epilogue = [&](const f32x4& C0, const f32x4& C1, const Ops& o) {
-    const float s0 = half_lo(o.sb.x), s1 = half_lo(o.sb.y);
-    const float c0 = fmaf(-TR::c0, s0, half_hi(o.sb.x));
-    const float c1 = fmaf(-TR::c0, s1, half_hi(o.sb.y));
+  struct Acc { f32x4 c[NQ]; };                      // a step's partial sums
+  auto epilogue = [&](const Acc& C, const Ops& o) {
+    if constexpr (HV) {
+      float s[4], c[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] = fmaf(s0, C0[e], fmaf(c0, o.xs0[e], acc[e]));
-      acc[e] = fmaf(s1, C1[e], fmaf(c1, o.xs1[e], acc[e]));
+      for (int q = 0; q < 4; ++q) {
+        s[q] = half_lo(o.sb[q]);
+        c[q] = fmaf(-TR::c0, s[q], half_hi(o.sb[q]));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[e] = fmaf(s[q], C.c[q][e], fmaf(c[q], o.xs[q][e], acc[e]));
+    } else {
+      const float s0 = half_lo(o.sb.x), s1 = half_lo(o.sb.y);
+      const float c0 = fmaf(-TR::c0, s0, half_hi(o.sb.x));
+      const float c1 = fmaf(-TR::c0, s1, half_hi(o.sb.y));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = fmaf(s0, C.c[0][e], fmaf(c0, o.xs0[e], acc[e]));
+        acc[e] = fmaf(s1, C.c[1][e], fmaf(c1, o.xs1[e], acc[e]));
+      }
     }
   };
 
   Ops cur, prev;
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-  f32x4 P0 = zero4, P1 = zero4;
-  prev.sb = u32x2{0u, 0u};                           // step -1 adds exactly nothing
-  prev.xs0 = zero4;
-  prev.xs1 = zero4;
+  Acc P;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) P.c[q] = zero4;
+  if constexpr (HV) {                                // step -1 adds exactly nothing
+    prev.sb = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) prev.xs[q] = zero4;
+  } else {
+    prev.sb = u32x2{0u, 0u};
+    prev.xs0 = zero4;
+    prev.xs1 = zero4;
+  }
   Blk kc = kfirst;
   Base bc = base_of(kc);
   fetch(bc, 0, cur);
@@ -808,8 +855,13 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
     const unsigned so = codes_at(kl);
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
-      f32x4 C0 = zero4, C1 = zero4;
-      pair_step<TR::f16>(cur.A, st[r * DB + d], magic, C0, C1);
+      Acc C;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) C.c[q] = zero4;
+      if constexpr (HV)
+        pair_step_halves<TR::f16>(cur.A, st[r * DB + d], magic, C.c);
+      else
+        pair_step<TR::f16>(cur.A, st[r * DB + d], magic, C.c[0], C.c[1]);
       Ops nxt;
       if (d + 1 < DB) {
         fetch(bc, d + 1, nxt);
@@ -823,11 +875,10 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
         }
         fetch(base_of(kn), 0, nxt);
       }
-      epilogue(P0, P1, prev);
+      epilogue(P, prev);
       if (d == 0 && kc.p == 0 && kc.k > 0) store_tile(kc.k - 1);  // uniform
       if (reload) load(so, d, st[r * DB + d]);
-      P0 = C0;
-      P1 = C1;
+      P = C;
       prev = cur;
       cur = nxt;
     }
@@ -843,7 +894,7 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
 #pragma unroll
   for (int r = 0; r < RB - 1; ++r)
     if (i + r < nb) run_block(r, false);
-  epilogue(P0, P1, prev);
+  epilogue(P, prev);
   if (ntile > 0) store_tile(ntile - 1);
 
   if (fused) {
@@ -950,9 +1001,16 @@ hipError_t launch_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
                        const uint16_t* biases, float* y, int M, int K, int N, int rsets,
                        int workers, int gs, const VerifyArgs& va, hipStream_t stream) {
   const int G = K >> 6;
-  const M16Layout L = m16_layout(G, 16, 8, 5);
-  const int lds_bytes = L.sb + 8 * 16 * G * 4;
-  auto kern = gs ? qgemm_w4_wide<ACT, DB, RB, 1> : qgemm_w4_wide<ACT, DB, RB, 0>;
+  const M16Layout L = m16_layout(G, 16, 8, 5, gs < 0);
+  const int lds_bytes = L.sb + 8 * 16 * (gs < 0 ? 2 * G : G) * 4;
+  if (lds_bytes > kLdsLimit) return hipErrorInvalidValue;  // never launched
+  auto kern = qgemm_w4_wide<ACT, DB, RB, 0>;
+  if (gs > 0) kern = qgemm_w4_wide<ACT, DB, RB, 1>;
+  if constexpr (DB == 4 && RB == 1) {
+    if (gs < 0) kern = qgemm_w4_wide<ACT, DB, RB, -1>;
+  } else {
+    if (gs < 0) return hipErrorInvalidValue;         // never launched
+  }
   if (lds_bytes > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1292,6 +1350,10 @@ hipError_t launch_wide_any(const void* x, const uint8_t* wq, const uint16_t* sca
   const int rsets = (M + 15) / 16;
   const int workers = wide_workers(rsets);
   const int GP = (K >> 6) >> 1;
+  // Group 32 keeps four partial sums per step: only the 4-pair block with a
+  // one-block ring stays within 256 registers (qgemm_wide_fits).
+  if (gs < 0)
+    return launch_wide<ACT, 4, 1>(x, wq, scales, biases, y, M, K, N, rsets, workers, gs, va, s);
   if (GP % 5 == 0)
     return launch_wide<ACT, 5, 1>(x, wq, scales, biases, y, M, K, N, rsets, workers, gs, va, s);
   if (GP % 4 == 0)
@@ -1331,14 +1393,16 @@ hipError_t launch_qgemm_rows(const void* x, const uint8_t* wq, const uint16_t* s
   return hipErrorInvalidValue;
 }
 
-bool qgemm_wide_fits(int M, int K, int N, int act) {
+bool qgemm_wide_fits(int M, int K, int N, int act, int gs) {
   // Whole tiles per wave need many of them: at least two per wave.
   const int G = K >> 6;
   const int T = (N + 15) / 16;
   const int rsets = (M + 15) / 16;
+  // Group 32 runs the 4-pair block only (launch_wide_any): K/128 a multiple of 4.
   return M <= 64 && act != ACT_FP32 && K <= 64 * 8 * 5 && G % 8 == 0 &&
+         (gs >= 0 || (G / 2) % 4 == 0) &&
          (size_t)N * (size_t)(K / 2) < 0x7F000000u && T >= 16 * wide_workers(rsets) &&
-         m16_layout(G, 16, 8, 5).sb + 8 * 16 * G * 4 <= kLdsLimit;
+         m16_layout(G, 16, 8, 5, gs < 0).sb + 8 * 16 * (gs < 0 ? 2 * G : G) * 4 <= kLdsLimit;
 }
 
 int qgemm_wide_groups(int M) { return wide_workers((M + 15) / 16) * ((M + 15) / 16); }

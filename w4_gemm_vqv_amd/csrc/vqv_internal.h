@@ -70,7 +70,7 @@ bool qgemm_rows_fits(int M, int K, int N, int act);
 hipError_t launch_qgemm_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                              const uint16_t* biases, float* y, int M, int K, int N, int act,
                              int gs, hipStream_t stream);
-bool qgemm_wide_fits(int M, int K, int N, int act);
+bool qgemm_wide_fits(int M, int K, int N, int act, int gs);
 int qgemm_wide_groups(int M);
 hipError_t launch_qgemm_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
                              const uint16_t* biases, float* y, int M, int K, int N, int act,
