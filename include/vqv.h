@@ -99,9 +99,9 @@ const char* vqv_status_string(vqv_status s);
  *   group      32, 64 or 128 contiguous k per scale and bias (else
  *              VQV_ERR_UNSUPPORTED). The pages name no group size; 64 is the
  *              layout of the tuned kernels, 32 and 128 the other common W4
- *              layouts. Group 128 runs on the same kernels as group 64;
- *              group 32 runs on the generic kernel only (slower: it forms
- *              each step's products once per 32-value half).
+ *              layouts. All three run on the same kernels; group 32 keeps
+ *              twice the partial sums per step and reads twice the scale
+ *              and bias entries, so it runs somewhat slower.
  *   act_dtype  a vqv_dtype (else VQV_ERR_ARG).
  *   workspace  device scratch of at least vqv_qgemm_workspace_bytes(...)
  *              bytes; may be NULL when that is 0.
@@ -109,7 +109,8 @@ const char* vqv_status_string(vqv_status s);
  * Numerics: products of x and the 4-bit codes are exact; sums are fp32; the
  * scale and bias are applied in fp32 after each 64-value partial sum (a
  * 128-group's scale and bias apply to each of its two halves), or after each
- * 32-value partial sum with group 32. NaN/Inf in x, scales or biases propagate by IEEE rules.
+ * 32-value partial sum with group 32. NaN/Inf in x, scales or biases
+ * propagate by IEEE rules.
  */
 size_t vqv_qgemm_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype);
 
@@ -174,8 +175,8 @@ vqv_status vqv_verify_ex(const float* logits, const int32_t* draft, const int32_
 /*
  * Projection and greedy verify in one call: y = x . W^T as vqv_qgemm, then
  * argmax and accept_len of y as vqv_verify with B*T == M. Where it applies
- * (M <= 8, bf16/fp16 activations, group 64 or 128, K within the
- * single-row-set kernel's LDS budget: K <= 5120 for every N), the argmax is fused into the projection's
+ * (M <= 8, bf16/fp16 activations, K within the single-row-set kernel's LDS
+ * budget: K <= 5120 for every N), the argmax is fused into the projection's
  * epilogue, so the logits are never read back ("dspark: fold first-token
  * forward into verify + bit-exact M5 Metal decode wins", first commit: the
  * fused argmax of the CUDA path and the single accept loop; "perf: tune
@@ -238,7 +239,7 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
  *   workspace  at least vqv_qgemm_swiglu_workspace_bytes(...) bytes,
  *              256-byte aligned; may be NULL when that is 0. It is 0 where
  *              the activation is fused into the projection (bf16/fp16
- *              activations, group 64 or 128, K <= 2560); elsewhere the projection's output
+ *              activations, K <= 2560); elsewhere the projection's output
  *              goes there first (M*N fp32).
  *
  * Numerics: the gate and up sums are those of vqv_qgemm (fp32); silu uses
