@@ -61,8 +61,8 @@ struct M16Layout {
 // The staging writes whole batches of XB rounds of NW groups, so the image
 // area is padded to that many pairs; image GP (the last, or a padding image
 // that the loads fill with zeros) is the zero image of steps past a run.
-// HV (group 32, qgemm_w4_m16 only): row sums and table entries per 32-k
-// half, twice as many; table rows a multiple of 4 entries for 16-byte reads.
+// HV (group 32): row sums and table entries per 32-k half, twice as many;
+// table rows a multiple of 4 entries for 16-byte reads.
 __host__ __device__ inline M16Layout m16_layout(int G, int WGC, int NW, int XB, bool HV = false) {
   const int GP = (G + 1) >> 1;
   const int rounds = (2 * GP + NW - 1) / NW;

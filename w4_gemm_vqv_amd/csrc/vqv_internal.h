@@ -18,8 +18,8 @@ constexpr int kMaxK32 = 8192;
 // y[M,N] = x[M,K] . W^T for 1 <= M <= 64, 64 <= K <= kMaxK, K % 64 == 0.
 // Every launcher takes the group shift gs: scales and biases hold one entry
 // per group of a row, 64 << gs values for gs = 0 (group 64) and gs = 1
-// (group 128, K % 128 == 0), 32 values for gs = -1 (group 32, which only the
-// generic kernel takes).
+// (group 128, K % 128 == 0), 32 values for gs = -1 (group 32, K <= kMaxK32;
+// the whole-tile kernel takes it only where K/128 is a multiple of 4).
 hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
                         const uint16_t* biases, float* y, int M, int K, int N, int act, int gs,
                         hipStream_t stream);
@@ -60,16 +60,17 @@ hipError_t launch_qgemm_m16(const void* x, const uint8_t* wq, const uint16_t* sc
                             const uint16_t* biases, float* y, int M, int K, int N, int act,
                             int gs, hipStream_t stream);
 
-// Wide outputs (at least two column tiles per wave of one work-group per
-// CU): qgemm_w4_wide (qgemm_m16.hip), waves own whole tiles over all of K.
-// With va.argmax (M <= 8) it is the fused verify's projection, one partial
-// per row and work-group (qgemm_wide_groups(M) work-groups).
 // 17..64 rows at vocabulary widths: one weight stream for every row set
 // (qgemm_w4_rows, qgemm_m16.hip).
 bool qgemm_rows_fits(int M, int K, int N, int act);
 hipError_t launch_qgemm_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                              const uint16_t* biases, float* y, int M, int K, int N, int act,
                              int gs, hipStream_t stream);
+
+// Wide outputs (at least two column tiles per wave of one work-group per
+// CU): qgemm_w4_wide (qgemm_m16.hip), waves own whole tiles over all of K.
+// With va.argmax (M <= 8) it is the fused verify's projection, one partial
+// per row and work-group (qgemm_wide_groups(M) work-groups).
 bool qgemm_wide_fits(int M, int K, int N, int act, int gs);
 int qgemm_wide_groups(int M);
 hipError_t launch_qgemm_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
