@@ -232,6 +232,9 @@ def main():
                     choices=["tiny", "target", "draft_w4a32", "vocab_verify", "batched_vocab",
                              "gate_up"])
     ap.add_argument("--m", type=int, default=None, help="rows (default: the workload's M)")
+    ap.add_argument("--n", type=int, default=None,
+                    help="output columns (default: the workload's N), e.g. one GPU's column "
+                         "share of a sharded projection")
     ap.add_argument("--group", type=int, choices=[32, 64, 128], default=64,
                     help="k per scale and bias (the workloads are quoted at 64)")
     ap.add_argument("--rotate", type=int, default=None, help="weight copies cycled per step")
@@ -268,7 +271,8 @@ def main():
     vqv.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    c = gen.make_config(args.workload, group=args.group)
+    c = gen.make_config(args.workload, group=args.group,
+                        **({"N": args.n} if args.n else {}))
     M = args.m or c["M"]
     K, N, act = c["K"], c["N"], c["act"]
     esz = 4 if act == "fp32" else 2
@@ -511,7 +515,8 @@ def main():
         "qgemm_by_M": by_m or None,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "frac_of_copy_probe": achieved / copy_gbs,
-                     "traffic": None if use_swiglu else traffic_record(args.workload, M, group),
+                     "traffic": None if use_swiglu or args.n else
+                                traffic_record(args.workload, M, group),
                      "kernel": kname, "bytes_per_launch": qb, "us_per_launch": k_us},
         "cpu_baseline": None,
     }
