@@ -227,6 +227,47 @@ def test_binding_has_no_cpu_path():
                 assert "import gen" not in text, f
 
 
+def test_binding_checks_tensor_sizes(L):
+    """The binding refuses a caller's tensor of the wrong size, dtype or device
+    before the call: the library sees only its pointer, so a short buffer would
+    be read or written past its end on the GPU."""
+    import torch
+    from w4_gemm_vqv_amd import vqv
+    M, K, N = 8, 128, 64
+    x = torch.zeros(M, K, dtype=torch.bfloat16)
+    wq = torch.zeros(N, K // 2, dtype=torch.uint8)
+    s = torch.zeros(N, K // 64, dtype=torch.float16)
+    dr = torch.zeros(1, 7, dtype=torch.int32)
+    logits = torch.zeros(M, N)
+    bad = [
+        (lambda: vqv.vqv_qgemm(x, wq, s, s, y=torch.empty(M, N - 1)), "y must hold"),
+        (lambda: vqv.vqv_qgemm(x, wq, s, s, y=torch.empty(M, N, dtype=torch.float16)),
+         "y must hold"),
+        (lambda: vqv.vqv_qgemm(x, wq, s, s, y=torch.empty(M, N, device="meta")), "y is on meta"),
+        (lambda: vqv.vqv_qgemm(x, wq.to("meta"), s, s), "wq is on meta"),
+        (lambda: vqv.vqv_qgemm_swiglu(x, wq, s, s, h=torch.empty(M, N)), "h must hold"),
+        (lambda: vqv.vqv_verify(logits, dr, 2, 8), "logits must hold"),
+        (lambda: vqv.vqv_verify(logits, dr[:, :6], 1, 8), "draft must hold"),
+        (lambda: vqv.vqv_verify(logits, dr.long(), 1, 8), "draft must hold"),
+        (lambda: vqv.vqv_verify(logits, dr, 1, 8, accept_len=torch.empty(2, dtype=torch.int32)),
+         "accept_len must hold"),
+        (lambda: vqv.vqv_verify_ex(logits, dr, 1, 8, draft_len=torch.zeros(2, dtype=torch.int32)),
+         "draft_len must hold"),
+        (lambda: vqv.vqv_qgemm_verify(x, wq, s, s, dr, 1, 8,
+                                      argmax=torch.empty(4, dtype=torch.int32)), "argmax must hold"),
+        (lambda: vqv.vqv_qgemm_verify(x, wq, s, s, dr, 1, 8, y=torch.empty(M * N + 1)),
+         "y must hold"),
+        (lambda: vqv.vqv_qgemm_verify_ex(x, wq, s, s, dr, 1, 8, margin=torch.empty(7)),
+         "margin must hold"),
+    ]
+    for call, msg in bad:
+        with pytest.raises(ValueError, match=msg):
+            call()
+    # Right sizes on the CPU get as far as the device check.
+    with pytest.raises(ValueError, match="device tensor"):
+        vqv.vqv_qgemm(x, wq, s, s, y=torch.empty(M, N))
+
+
 # ---------------------------------------------------------------- on the GPU
 
 
@@ -252,3 +293,4 @@ def test_rejected_calls_write_nothing():
     assert st == ARG
     torch.cuda.synchronize()
     assert (y == 7.0).all() and (am == -3).all() and (ac == -3).all()
+

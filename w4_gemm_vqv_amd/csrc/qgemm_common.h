@@ -119,9 +119,10 @@ __device__ __forceinline__ float sum8_lanes(float s) {
 // (GS = 0: group 64, GS = 1: group 128; a template parameter of the kernels).
 // The kernels' tables are per 64-group: a 128-group's entry serves both of
 // its 64-groups, and the per-64-group row sums make the bias term
-// b * (xs0 + xs1) come out as b * xs of the 128-group. GS = -1 (group 32,
-// the generic kernel only) keeps one LDS entry per 32-group and takes the
-// group-64 forms below with twice the entries per column.
+// b * (xs0 + xs1) come out as b * xs of the 128-group. GS = -1 (group 32)
+// keeps one LDS entry per 32-group, twice the entries per column, takes the
+// group-64 forms below, and the kernels apply each entry to its own 32-k
+// half of a 64-k step.
 // A table unit covers 8 consecutive 64-groups of one column (K/64 a multiple
 // of 8). sb_unit_load reads one unit's entries from byte offset `off` of an
 // array: 16 bytes for group 64, or the 4 entries of group 128 (8 bytes,

@@ -91,6 +91,20 @@ def _dev(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
+def _need(t: torch.Tensor | None, name: str, numel: int, dtype: torch.dtype,
+          device: torch.device) -> None:
+    """A tensor the library reads or writes must hold exactly what the call
+    covers, in the stated dtype and on the device of the call's main input:
+    the library sees only a pointer, so a shorter buffer would be accessed past
+    its end on the GPU."""
+    if t is None:
+        return
+    if t.dtype != dtype or t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} {dtype} values, got {t.numel()} {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call's inputs on {device}")
+
+
 def _check_weight(wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, K: int,
                   group: int) -> None:
     """The library reads N*K/2 code bytes and N*K/group table entries: the
@@ -128,6 +142,9 @@ def vqv_qgemm(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: t
     M, K = x.shape
     N = wq.shape[0]
     _check_weight(wq, scales, biases, K, group)
+    for t, name in ((wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _need(t, name, t.numel(), t.dtype, x.device)
+    _need(y, "y", M * N, torch.float32, x.device)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
     act = _DTYPES[x.dtype]
@@ -146,6 +163,19 @@ def vqv_verify_workspace_bytes(B: int, T: int, N: int) -> int:
     return lib().vqv_verify_workspace_bytes(B, T, N)
 
 
+def _verify_io(logits, draft, B, T, N, dev, argmax, accept_len, draft_len=None, margin=None):
+    """Sizes of the verify's tensors: logits [B*T, N] fp32, drafts [B, T-1]
+    int32, valid counts [B] int32, argmax and margin [B*T], accept_len [B]."""
+    if logits is not None:
+        _need(logits, "logits", B * T * N, torch.float32, dev)
+    if draft is not None and draft.numel():
+        _need(draft, "draft", B * (T - 1), torch.int32, dev)
+    _need(draft_len, "draft_len", B, torch.int32, dev)
+    _need(argmax, "argmax", B * T, torch.int32, dev)
+    _need(accept_len, "accept_len", B, torch.int32, dev)
+    _need(margin, "margin", B * T, torch.float32, dev)
+
+
 def vqv_verify(logits: torch.Tensor, draft: torch.Tensor | None, B: int, T: int,
                argmax: torch.Tensor | None = None, accept_len: torch.Tensor | None = None,
                workspace: torch.Tensor | None = None, stream=None):
@@ -153,6 +183,7 @@ def vqv_verify(logits: torch.Tensor, draft: torch.Tensor | None, B: int, T: int,
     against int32 drafts [B, T-1]."""
     N = logits.shape[-1]
     dev = logits.device
+    _verify_io(logits, draft, B, T, N, dev, argmax, accept_len)
     if argmax is None:
         argmax = torch.empty(B * T, dtype=torch.int32, device=dev)
     if accept_len is None:
@@ -178,6 +209,7 @@ def vqv_verify_ex(logits: torch.Tensor, draft: torch.Tensor | None, B: int, T: i
     the top-1 minus top-2 margin of each row."""
     N = logits.shape[-1]
     dev = logits.device
+    _verify_io(logits, draft, B, T, N, dev, argmax, accept_len, draft_len, margin)
     if argmax is None:
         argmax = torch.empty(B * T, dtype=torch.int32, device=dev)
     if accept_len is None:
@@ -217,6 +249,10 @@ def vqv_qgemm_verify(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor,
     _check_weight(wq, scales, biases, K, group)
     dev = x.device
     act = _DTYPES[x.dtype]
+    for t, name in ((wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _need(t, name, t.numel(), t.dtype, dev)
+    _need(y, "y", M * N, torch.float32, dev)
+    _verify_io(None, draft, B, T, N, dev, argmax, accept_len)
     if y is None and want_y:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
     if argmax is None:
@@ -253,6 +289,10 @@ def vqv_qgemm_verify_ex(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor,
     _check_weight(wq, scales, biases, K, group)
     dev = x.device
     act = _DTYPES[x.dtype]
+    for t, name in ((wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _need(t, name, t.numel(), t.dtype, dev)
+    _need(y, "y", M * N, torch.float32, dev)
+    _verify_io(None, draft, B, T, N, dev, argmax, accept_len, draft_len, margin)
     if y is None and want_y:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
     if argmax is None:
@@ -292,6 +332,9 @@ def vqv_qgemm_swiglu(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor,
     N = wq.shape[0]
     _check_weight(wq, scales, biases, K, group)
     act = _DTYPES[x.dtype]
+    for t, name in ((wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _need(t, name, t.numel(), t.dtype, x.device)
+    _need(h, "h", M * (N // 2), torch.float32, x.device)
     if h is None:
         h = torch.empty((M, N // 2), dtype=torch.float32, device=x.device)
     need = vqv_qgemm_swiglu_workspace_bytes(M, K, N, group, act)
