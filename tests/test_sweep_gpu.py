@@ -7,7 +7,8 @@ kernel and every ragged tail it meets are exercised in combinations nobody
 picked. Each case checks vqv_qgemm against the oracle element by element and,
 on a factorisation M = B*T, vqv_qgemm_verify's logits against the oracle and
 its argmax and accept lengths bit for bit against the oracle's verify of the
-same logits.
+same logits. Where N is even, vqv_qgemm_swiglu's h is checked against the
+oracle's silu(gate) * up of the same projection, N/2 columns each.
 """
 
 import numpy as np
@@ -15,8 +16,9 @@ import pytest
 import torch
 
 import gen
-from oracle import argmax_ref, qgemm_ref, verify_ref
+from oracle import argmax_ref, qgemm_ref, silu_ref, verify_ref
 from tests.devutil import assert_close, to_device
+from tests.test_swiglu_gpu import assert_swiglu_close
 
 pytestmark = pytest.mark.gpu
 
@@ -84,3 +86,9 @@ def test_sweep(vqv, M, K, N, group, act, B, T, i):
     ra, rl = verify_ref(y2_np, draft, B, T)
     np.testing.assert_array_equal(am.cpu().numpy(), ra, err_msg=what)
     np.testing.assert_array_equal(al.cpu().numpy(), rl, err_msg=what)
+
+    if N % 2 == 0:
+        h = vqv.vqv_qgemm_swiglu(d["x"], d["wq"], d["scales"], d["biases"], group=group)
+        torch.cuda.synchronize()
+        g, u = ref[:, :N // 2], ref[:, N // 2:]
+        assert_swiglu_close(h.cpu().numpy(), g, u, silu_ref(g) * u, act, what + " (SwiGLU)")
