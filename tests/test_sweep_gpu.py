@@ -7,7 +7,8 @@ kernel and every ragged tail it meets are exercised in combinations nobody
 picked. Each case checks vqv_qgemm against the oracle element by element and,
 on a factorisation M = B*T, vqv_qgemm_verify's logits against the oracle and
 its argmax and accept lengths bit for bit against the oracle's verify of the
-same logits. Where N is even, vqv_qgemm_swiglu's h is checked against the
+same logits; vqv_qgemm_verify_ex the same, with random valid draft counts
+(some outside 0..T-1) and the margins bit for bit. Where N is even, vqv_qgemm_swiglu's h is checked against the
 oracle's silu(gate) * up of the same projection, N/2 columns each.
 """
 
@@ -19,6 +20,7 @@ import gen
 from oracle import argmax_ref, qgemm_ref, silu_ref, verify_ref
 from tests.devutil import assert_close, to_device
 from tests.test_swiglu_gpu import assert_swiglu_close
+from tests.test_verify_ex_gpu import bits
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +88,18 @@ def test_sweep(vqv, M, K, N, group, act, B, T, i):
     ra, rl = verify_ref(y2_np, draft, B, T)
     np.testing.assert_array_equal(am.cpu().numpy(), ra, err_msg=what)
     np.testing.assert_array_equal(al.cpu().numpy(), rl, err_msg=what)
+
+    draft_len = rng.integers(-1, T + 1, size=B).astype(np.int32)
+    lt = torch.from_numpy(draft_len).cuda()
+    y3, am3, al3, mg3 = vqv.vqv_qgemm_verify_ex(d["x"], d["wq"], d["scales"], d["biases"], dt,
+                                                B, T, draft_len=lt, group=group)
+    torch.cuda.synchronize()
+    y3_np = y3.cpu().numpy()
+    assert_close(y3_np, ref, act, what + " (fused call with margins)")
+    ra, rl, rm = verify_ref(y3_np, draft, B, T, draft_len=draft_len, margin=True)
+    np.testing.assert_array_equal(am3.cpu().numpy(), ra, err_msg=what)
+    np.testing.assert_array_equal(al3.cpu().numpy(), rl, err_msg=what)
+    np.testing.assert_array_equal(bits(mg3.cpu().numpy()), bits(rm), err_msg=what)
 
     if N % 2 == 0:
         h = vqv.vqv_qgemm_swiglu(d["x"], d["wq"], d["scales"], d["biases"], group=group)
