@@ -48,6 +48,9 @@
 // with the weights of its first step so that storing it never drains the
 // ring.
 
+#include <stdlib.h>
+#include <string.h>
+
 #include "argmax.h"
 #include "qgemm_common.h"
 #include "vqv_internal.h"
@@ -1063,6 +1066,12 @@ hipError_t launch_m8_any(const void* x, const uint8_t* wq, const uint16_t* scale
   return launch_m8_blocks<ACT, 10>(x, wq, scales, biases, y, M, K, N, cols, gs, va, s);
 }
 
+// The whole-line kernel for one row set, unless a profiling run pins the
+// half-line one.
+bool use_m8q(int M, int K, int act, int gs) {
+  return forced_variant() != kVariantM8 && qgemm_m8q_fits(M, K, act, gs);
+}
+
 // Configuration per problem. M <= 8 (one row set): when the work-group's
 // whole activation range fits in LDS, the barrier-free XALL kernel; narrow N
 // is split into exactly one work-group per CU (columns rounded up to 4, up
@@ -1080,6 +1089,10 @@ hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scale
     // takes the same kernel, so the two paths agree bit for bit).
     const VerifyArgs none{};
     return launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, ACT, gs, none, s);
+  }
+  if constexpr (ACT != ACT_FP32) if (M <= 8 && use_m8q(M, K, ACT, gs)) {
+    const VerifyArgs none{};
+    return launch_qgemm_m8q(x, wq, scales, biases, y, M, K, N, ACT, gs, none, s);
   }
   if constexpr (ACT != ACT_FP32) if (M <= 8 && m8_fits(K, gs)) {
     const VerifyArgs none{};
@@ -1140,6 +1153,10 @@ int qgemm_verify_groups(int M, int K, int N, int act, int gs) {
   // instead of one per 80 columns).
   if (M > 8 || act == ACT_FP32) return 0;
   if (qgemm_wide_fits(M, K, N, act, gs)) return qgemm_wide_groups(M);
+  if (use_m8q(M, K, act, gs)) {
+    const int cols = qgemm_m8q_cols(N);
+    return (N + cols - 1) / cols;
+  }
   if (!m8_fits(K, gs)) return 0;
   const int cols = m8_cols(N);
   return (N + cols - 1) / cols;
@@ -1151,12 +1168,25 @@ hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t*
   hipError_t e = hipErrorInvalidValue;
   if (qgemm_wide_fits(M, K, N, act, gs))
     e = launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, act, gs, va, stream);
+  else if (use_m8q(M, K, act, gs))
+    e = launch_qgemm_m8q(x, wq, scales, biases, y, M, K, N, act, gs, va, stream);
   else if (act == ACT_BF16)
     e = launch_m8_any<ACT_BF16>(x, wq, scales, biases, y, M, K, N, gs, va, stream);
   else if (act == ACT_FP16)
     e = launch_m8_any<ACT_FP16>(x, wq, scales, biases, y, M, K, N, gs, va, stream);
   if (e != hipSuccess) return e;
   return launch_verify_finish(va.partials, qgemm_verify_groups(M, K, N, act, gs), va, stream);
+}
+
+Variant forced_variant() {
+  static const Variant v = [] {
+    const char* e = getenv("VQV_FORCE_VARIANT");
+    if (!e) return kVariantAuto;
+    if (!strcmp(e, "m8")) return kVariantM8;
+    if (!strcmp(e, "m8q")) return kVariantM8Q;
+    return kVariantAuto;
+  }();
+  return v;
 }
 
 }  // namespace vqv

@@ -52,6 +52,22 @@ hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t*
                                const uint16_t* biases, float* y, int M, int K, int N, int act,
                                int gs, const VerifyArgs& va, hipStream_t stream);
 
+// M <= 8 with 16-bit activations, group 64 or 128 (gs 0 or 1), K % 256 == 0:
+// qgemm_w4_m8q (qgemm_m8.hip), codes read in whole 128-byte lines. With
+// va.argmax it is the fused verify's projection (one partial per row and
+// work-group, qgemm_m8q_cols(N) columns per work-group).
+bool qgemm_m8q_fits(int M, int K, int act, int gs);
+int qgemm_m8q_cols(int N);
+hipError_t launch_qgemm_m8q(const void* x, const uint8_t* wq, const uint16_t* scales,
+                            const uint16_t* biases, float* y, int M, int K, int N, int act,
+                            int gs, const VerifyArgs& va, hipStream_t stream);
+
+// The kernel family a bench or profiler run pins through the environment
+// variable VQV_FORCE_VARIANT (read once per process): kVariantAuto when it is
+// unset or names no family. Only the M <= 8 projection honours it.
+enum Variant { kVariantAuto = 0, kVariantM8 = 1, kVariantM8Q = 2 };
+Variant forced_variant();
+
 // 9..64 rows in row sets of 16 (bf16/fp16, K within the kernel's LDS
 // budget): qgemm_w4_m16 (qgemm_m16.hip). Whether it takes the problem, and
 // the launch.
