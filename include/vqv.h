@@ -34,8 +34,11 @@
  *
  * Errors
  *   Arguments are checked on the host before anything is launched. A call
- *   that returns anything but VQV_OK has launched nothing and written
- *   nothing. VQV_ERR_HIP means the launch itself failed (hipGetLastError).
+ *   that returns VQV_ERR_ARG, VQV_ERR_UNSUPPORTED, VQV_ERR_ALIGN or
+ *   VQV_ERR_WORKSPACE has launched nothing and written nothing. VQV_ERR_HIP
+ *   means the HIP runtime refused a launch (hipGetLastError); in the calls
+ *   that launch two kernels it can come after the first was enqueued, which
+ *   may then write its outputs and scratch.
  */
 #ifndef VQV_H
 #define VQV_H
@@ -47,7 +50,7 @@
 extern "C" {
 #endif
 
-#define VQV_ABI_VERSION 4
+#define VQV_ABI_VERSION 5
 
 typedef enum {
   VQV_BF16 = 0, /* bfloat16 activations                                  */
@@ -218,6 +221,33 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
                                const int32_t* draft_len, int B, int T, int32_t* argmax,
                                int32_t* accept_len, float* margin, void* workspace,
                                size_t workspace_bytes, void* hip_stream);
+
+/*
+ * vqv_qgemm_verify_ex for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It takes no workspace: its scratch (the fused kernel's per-row
+ * partials, or the two-stage verify's partials, plus the logits when y is
+ * NULL) lives in a static device array of VQV_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds on each GPU it runs on until the process ends. The
+ * arguments and results are those of vqv_qgemm_verify_ex.
+ *   A problem whose scratch exceeds VQV_NOALLOC_SCRATCH_BYTES returns
+ *   VQV_ERR_WORKSPACE with nothing launched (at M <= 8 with 16-bit
+ *   activations that is N above roughly 650,000; with y NULL on the two-stage
+ *   path, M*N*4 above about 1 MB).
+ *   The first call on a device looks the array up (hipGetSymbolAddress);
+ *   VQV_ERR_HIP if that fails. No call allocates or frees anything.
+ *   All calls on one GPU share that GPU's array: calls that overlap in time
+ *   on one GPU (different streams, or different host threads without
+ *   synchronization) race on it and their results are undefined. Nothing in
+ *   it needs to start at zero, and each call overwrites what it uses.
+ */
+#define VQV_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+vqv_status vqv_qgemm_verify_ex_noalloc(const void* x, const uint8_t* wq, const uint16_t* scales,
+                                       const uint16_t* biases, float* y, int M, int K, int N,
+                                       int group, vqv_dtype act_dtype, const int32_t* draft,
+                                       const int32_t* draft_len, int B, int T, int32_t* argmax,
+                                       int32_t* accept_len, float* margin, void* hip_stream);
 
 /*
  * Gate/up projection with its SwiGLU activation: y = x . W^T as vqv_qgemm over

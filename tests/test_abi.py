@@ -38,7 +38,7 @@ def test_header_declares_the_calls():
         ["vqv_abi_version", "vqv_status_string", "vqv_qgemm_workspace_bytes", "vqv_qgemm",
          "vqv_verify_workspace_bytes", "vqv_verify", "vqv_verify_ex",
          "vqv_qgemm_verify_workspace_bytes", "vqv_qgemm_verify", "vqv_qgemm_verify_ex",
-         "vqv_qgemm_swiglu_workspace_bytes", "vqv_qgemm_swiglu"])
+         "vqv_qgemm_swiglu_workspace_bytes", "vqv_qgemm_swiglu", "vqv_qgemm_verify_ex_noalloc"])
 
 
 def test_exports_every_declared_symbol(L):
@@ -53,7 +53,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.vqv_abi_version() == 4
+    assert L.vqv_abi_version() == 5
     for s in range(6):
         assert L.vqv_status_string(s)
     assert L.vqv_status_string(99) == b"unknown status"
@@ -170,6 +170,25 @@ def test_fused_ex_rejects(L, kw, status):
     assert L.vqv_qgemm_verify_ex(a["x"], a["wq"], a["s"], a["b"], a["y"], a["M"], a["K"], a["N"],
                                  a["group"], a["act"], a["dr"], a["dl"], a["B"], a["T"], a["am"],
                                  a["ac"], a["mg"], a["ws"], a["wsb"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), ARG), (dict(B=2), ARG), (dict(group=16), UNSUP), (dict(am=AM + 2), ALIGN),
+    (dict(mg=Y), ARG), (dict(dl=AM), ARG), (dict(y=X), ARG), (dict(K=16384 + 64), UNSUP),
+    # scratch beyond VQV_NOALLOC_SCRATCH_BYTES: the fused partials of a very wide
+    # projection, and the logits of a two-stage call without y
+    (dict(K=5120, N=1_000_000, wq=1 << 36, s=2 << 36, b=3 << 36, y=4 << 36), WS),
+    (dict(M=16, B=2, y=None, N=20000), WS),
+])
+def test_noalloc_rejects(L, kw, status):
+    """Rejections of the allocation-free call come before it looks up its
+    scratch or launches anything (so they run without a GPU)."""
+    a = dict(x=X, wq=W, s=S, b=B_, y=Y, M=8, K=512, N=1024, group=64, act=BF16, dr=DR, dl=LEN,
+             B=1, T=8, am=AM, ac=AC, mg=MG)
+    a.update(kw)
+    assert L.vqv_qgemm_verify_ex_noalloc(a["x"], a["wq"], a["s"], a["b"], a["y"], a["M"], a["K"],
+                                         a["N"], a["group"], a["act"], a["dr"], a["dl"], a["B"],
+                                         a["T"], a["am"], a["ac"], a["mg"], None) == status
 
 
 def test_swiglu_workspace_queries(L):

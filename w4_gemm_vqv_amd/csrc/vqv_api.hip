@@ -3,6 +3,8 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/vqv.h"
 #include "vqv_internal.h"
 
@@ -111,12 +113,22 @@ vqv_status vqv_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* sc
                              workspace_bytes, hip_stream);
 }
 
-vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t* scales,
-                               const uint16_t* biases, float* y, int M, int K, int N, int group,
-                               vqv_dtype act_dtype, const int32_t* draft,
-                               const int32_t* draft_len, int B, int T, int32_t* argmax,
-                               int32_t* accept_len, float* margin, void* workspace,
-                               size_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Everything vqv_qgemm_verify_ex checks except the workspace; fills the sizes
+// the workspace and overlap checks use.
+struct FusedSizes {
+  size_t xbytes, wbytes, sbytes, ybytes;
+  int gs;
+};
+
+vqv_status check_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* scales,
+                              const uint16_t* biases, const float* y, int M, int K, int N,
+                              int group, vqv_dtype act_dtype, const int32_t* draft,
+                              const int32_t* draft_len, int B, int T, const int32_t* argmax,
+                              const int32_t* accept_len, const float* margin, FusedSizes* fs) {
   if (!x || !wq || !scales || !biases || !argmax || !accept_len) return VQV_ERR_ARG;
   if (act_dtype != VQV_BF16 && act_dtype != VQV_FP16 && act_dtype != VQV_FP32)
     return VQV_ERR_ARG;
@@ -129,35 +141,52 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
   if (K % kGroup) return VQV_ERR_UNSUPPORTED;  // group 32 with an odd count of 32-groups
   if (K > (gs < 0 ? vqv::kMaxK32 : vqv::kMaxK)) return VQV_ERR_UNSUPPORTED;
   const size_t esz = (size_t)act_size(act_dtype);
-  const size_t xbytes = (size_t)M * K * esz;
-  const size_t wbytes = (size_t)N * (K / 2);
-  const size_t sbytes = (size_t)N * (K / group) * 2;
-  const size_t ybytes = (size_t)M * N * 4;
-  if (xbytes >= (1ull << 31) || wbytes >= (1ull << 32) || (size_t)N * (K / kGroup) >= (1ull << 31) ||
-      ybytes >= (1ull << 31))
+  fs->xbytes = (size_t)M * K * esz;
+  fs->wbytes = (size_t)N * (K / 2);
+  fs->sbytes = (size_t)N * (K / group) * 2;
+  fs->ybytes = (size_t)M * N * 4;
+  fs->gs = gs;
+  if (fs->xbytes >= (1ull << 31) || fs->wbytes >= (1ull << 32) ||
+      (size_t)N * (K / kGroup) >= (1ull << 31) || fs->ybytes >= (1ull << 31))
     return VQV_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(scales, 2) || !aligned(biases, 2) ||
       (y && !aligned(y, 16)) || !aligned(argmax, 4) || !aligned(accept_len, 4) ||
       (draft && !aligned(draft, 4)) || (draft_len && !aligned(draft_len, 4)) ||
       (margin && !aligned(margin, 4)))
     return VQV_ERR_ALIGN;
-  const size_t need = vqv_qgemm_verify_workspace_bytes(M, K, N, group, act_dtype);
-  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return VQV_ERR_WORKSPACE;
   const void* ins[6] = {x, wq, scales, biases, draft, draft_len};
-  const size_t insz[6] = {xbytes, wbytes, sbytes, sbytes, draft ? (size_t)B * (T - 1) * 4 : 0,
-                          draft_len ? (size_t)B * 4 : 0};
-  void* outs[5] = {y, argmax, accept_len, margin, workspace};
-  const size_t outsz[5] = {y ? ybytes : 0, (size_t)M * 4, (size_t)B * 4,
-                           margin ? (size_t)M * 4 : 0, need};
-  for (int o = 0; o < 5; ++o) {
+  const size_t insz[6] = {fs->xbytes, fs->wbytes, fs->sbytes, fs->sbytes,
+                          draft ? (size_t)B * (T - 1) * 4 : 0, draft_len ? (size_t)B * 4 : 0};
+  const void* outs[4] = {y, argmax, accept_len, margin};
+  const size_t outsz[4] = {y ? fs->ybytes : 0, (size_t)M * 4, (size_t)B * 4,
+                           margin ? (size_t)M * 4 : 0};
+  for (int o = 0; o < 4; ++o) {
     for (int i = 0; i < 6; ++i)
       if (overlaps(outs[o], outsz[o], ins[i], insz[i])) return VQV_ERR_ARG;
-    for (int o2 = o + 1; o2 < 5; ++o2)
+    for (int o2 = o + 1; o2 < 4; ++o2)
       if (overlaps(outs[o], outsz[o], outs[o2], outsz[o2])) return VQV_ERR_ARG;
   }
+  return VQV_OK;
+}
+
+// Scratch bytes the call needs: the fused kernel's partials, or the two-stage
+// verify's partials after room for the logits (logits_room bytes, used when y
+// is NULL).
+size_t qgemm_verify_scratch(int M, int K, int N, int gs, vqv_dtype act, size_t logits_room) {
+  const int groups = vqv::qgemm_verify_groups(M, K, N, (int)act, gs);
+  if (groups > 0) return kHead + (size_t)groups * 8 * 16;
+  return kHead + logits_room + (size_t)M * vqv::verify_chunks(N) * 16;
+}
+
+// The launch sequence of a checked call, with its scratch at ws (laid out as
+// qgemm_verify_scratch describes).
+vqv_status launch_qgemm_verify_at(const void* x, const uint8_t* wq, const uint16_t* scales,
+                                  const uint16_t* biases, float* y, int M, int K, int N, int gs,
+                                  vqv_dtype act_dtype, const int32_t* draft,
+                                  const int32_t* draft_len, int B, int T, int32_t* argmax,
+                                  int32_t* accept_len, float* margin, unsigned char* ws,
+                                  size_t logits_room, hipStream_t st) {
   (void)hipGetLastError();
-  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
   vqv::VerifyArgs va{draft, draft_len, B, T, argmax, accept_len, margin,
                      reinterpret_cast<uint4*>(ws + kHead)};
   hipError_t e;
@@ -165,11 +194,93 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
     e = vqv::launch_qgemm_verify(x, wq, scales, biases, y, M, K, N, (int)act_dtype, gs, va, st);
   } else {
     float* logits = y ? y : reinterpret_cast<float*>(ws + kHead);
-    va.partials = reinterpret_cast<uint4*>(ws + kHead + align256(ybytes));
+    va.partials = reinterpret_cast<uint4*>(ws + kHead + logits_room);
     e = vqv::launch_qgemm(x, wq, scales, biases, logits, M, K, N, (int)act_dtype, gs, st);
     if (e == hipSuccess) e = vqv::launch_verify(logits, N, va, st);
   }
   return e == hipSuccess ? VQV_OK : VQV_ERR_HIP;
+}
+
+// The scratch of vqv_qgemm_verify_ex_noalloc: one array per GPU, held until
+// the process ends. Host code uses it only through the address
+// hipGetSymbolAddress returns for the current device, kept per device.
+constexpr int kMaxDevices = 64;
+std::atomic<unsigned char*> g_scratch[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[VQV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// The address of `scratch` on the current device, looked up on the first call
+// on that device (concurrent first calls look it up twice, harmlessly).
+hipError_t scratch_of_current_device(unsigned char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  unsigned char* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    p = static_cast<unsigned char*>(q);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t* scales,
+                               const uint16_t* biases, float* y, int M, int K, int N, int group,
+                               vqv_dtype act_dtype, const int32_t* draft,
+                               const int32_t* draft_len, int B, int T, int32_t* argmax,
+                               int32_t* accept_len, float* margin, void* workspace,
+                               size_t workspace_bytes, void* hip_stream) {
+  FusedSizes fs;
+  const vqv_status st = check_qgemm_verify(x, wq, scales, biases, y, M, K, N, group, act_dtype,
+                                           draft, draft_len, B, T, argmax, accept_len, margin, &fs);
+  if (st != VQV_OK) return st;
+  const size_t need = vqv_qgemm_verify_workspace_bytes(M, K, N, group, act_dtype);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return VQV_ERR_WORKSPACE;
+  const void* ins[6] = {x, wq, scales, biases, draft, draft_len};
+  const size_t insz[6] = {fs.xbytes, fs.wbytes, fs.sbytes, fs.sbytes,
+                          draft ? (size_t)B * (T - 1) * 4 : 0, draft_len ? (size_t)B * 4 : 0};
+  const void* outs[4] = {y, argmax, accept_len, margin};
+  const size_t outsz[4] = {y ? fs.ybytes : 0, (size_t)M * 4, (size_t)B * 4,
+                           margin ? (size_t)M * 4 : 0};
+  for (int i = 0; i < 6; ++i)
+    if (overlaps(workspace, need, ins[i], insz[i])) return VQV_ERR_ARG;
+  for (int o = 0; o < 4; ++o)
+    if (overlaps(workspace, need, outs[o], outsz[o])) return VQV_ERR_ARG;
+  return launch_qgemm_verify_at(x, wq, scales, biases, y, M, K, N, fs.gs, act_dtype, draft,
+                                draft_len, B, T, argmax, accept_len, margin,
+                                static_cast<unsigned char*>(workspace), align256(fs.ybytes),
+                                static_cast<hipStream_t>(hip_stream));
+}
+
+vqv_status vqv_qgemm_verify_ex_noalloc(const void* x, const uint8_t* wq, const uint16_t* scales,
+                                       const uint16_t* biases, float* y, int M, int K, int N,
+                                       int group, vqv_dtype act_dtype, const int32_t* draft,
+                                       const int32_t* draft_len, int B, int T, int32_t* argmax,
+                                       int32_t* accept_len, float* margin, void* hip_stream) {
+  FusedSizes fs;
+  const vqv_status st = check_qgemm_verify(x, wq, scales, biases, y, M, K, N, group, act_dtype,
+                                           draft, draft_len, B, T, argmax, accept_len, margin, &fs);
+  if (st != VQV_OK) return st;
+  const size_t room = y ? 0 : align256(fs.ybytes);
+  if (qgemm_verify_scratch(M, K, N, fs.gs, act_dtype, room) > VQV_NOALLOC_SCRATCH_BYTES)
+    return VQV_ERR_WORKSPACE;
+  unsigned char* ws = nullptr;
+  if (scratch_of_current_device(&ws) != hipSuccess) return VQV_ERR_HIP;
+  return launch_qgemm_verify_at(x, wq, scales, biases, y, M, K, N, fs.gs, act_dtype, draft,
+                                draft_len, B, T, argmax, accept_len, margin, ws, room,
+                                static_cast<hipStream_t>(hip_stream));
 }
 
 size_t vqv_qgemm_swiglu_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype) {

@@ -21,7 +21,8 @@ VQV_OK, VQV_ERR_ARG, VQV_ERR_UNSUPPORTED, VQV_ERR_ALIGN, VQV_ERR_WORKSPACE, VQV_
 EXPORTS = ("vqv_abi_version", "vqv_status_string", "vqv_qgemm_workspace_bytes", "vqv_qgemm",
            "vqv_verify_workspace_bytes", "vqv_verify", "vqv_verify_ex",
            "vqv_qgemm_verify_workspace_bytes", "vqv_qgemm_verify", "vqv_qgemm_verify_ex",
-           "vqv_qgemm_swiglu_workspace_bytes", "vqv_qgemm_swiglu")
+           "vqv_qgemm_swiglu_workspace_bytes", "vqv_qgemm_swiglu", "vqv_qgemm_verify_ex_noalloc")
+VQV_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 _DTYPES = {torch.bfloat16: VQV_BF16, torch.float16: VQV_FP16, torch.float32: VQV_FP32}
 _lib = None
@@ -68,6 +69,9 @@ def lib() -> ctypes.CDLL:
         L.vqv_qgemm_verify_ex.restype = i
         L.vqv_qgemm_verify_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, i, i, vp, vp,
                                           vp, vp, sz, vp]
+        L.vqv_qgemm_verify_ex_noalloc.restype = i
+        L.vqv_qgemm_verify_ex_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, i, i,
+                                                  vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -313,6 +317,43 @@ def vqv_qgemm_verify_ex(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor,
         _dev(argmax, "argmax"), _dev(accept_len, "accept_len"), mptr,
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream_handle(stream)))
+    return y, argmax, accept_len, margin
+
+
+def vqv_qgemm_verify_ex_noalloc(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor,
+                                biases: torch.Tensor, draft: torch.Tensor | None, B: int, T: int,
+                                draft_len: torch.Tensor | None = None,
+                                y: torch.Tensor | None = None,
+                                argmax: torch.Tensor | None = None,
+                                accept_len: torch.Tensor | None = None,
+                                margin: torch.Tensor | None = None, group: int = 64,
+                                stream=None):
+    """(y, argmax, accept_len, margin) as vqv_qgemm_verify_ex, with the
+    library's static per-GPU scratch instead of a workspace. Outputs the
+    caller leaves as None are not produced (y, margin) or are allocated here
+    (argmax, accept_len) -- pass them in to allocate nothing."""
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported activation dtype {x.dtype}")
+    M, K = x.shape
+    N = wq.shape[0]
+    _check_weight(wq, scales, biases, K, group)
+    dev = x.device
+    act = _DTYPES[x.dtype]
+    for t, name in ((wq, "wq"), (scales, "scales"), (biases, "biases")):
+        _need(t, name, t.numel(), t.dtype, dev)
+    _need(y, "y", M * N, torch.float32, dev)
+    _verify_io(None, draft, B, T, N, dev, argmax, accept_len, draft_len, margin)
+    if argmax is None:
+        argmax = torch.empty(B * T, dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    dptr = _dev(draft, "draft") if (draft is not None and draft.numel()) else None
+    lptr = _dev(draft_len, "draft_len") if draft_len is not None else None
+    mptr = _dev(margin, "margin") if margin is not None else None
+    _check(lib().vqv_qgemm_verify_ex_noalloc(
+        _dev(x, "x"), _dev(wq, "wq"), _dev(scales, "scales"), _dev(biases, "biases"),
+        _dev(y, "y") if y is not None else None, M, K, N, group, act, dptr, lptr, B, T,
+        _dev(argmax, "argmax"), _dev(accept_len, "accept_len"), mptr, _stream_handle(stream)))
     return y, argmax, accept_len, margin
 
 
