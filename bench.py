@@ -21,6 +21,14 @@ by its mean launch time (HIP events around a graph of back-to-back QMM
 launches, on the stream they run on) against the 8 TB/s HBM peak;
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
+`--variant m8|m8q` pins the projection kernel family of the M <= 8 path
+(through VQV_FORCE_VARIANT) so that a profiler trace holds one variant only.
+On the target workload the line also carries the M=8 versus M=4 verified-row
+throughput at K=5120, N=1024 (the shape of the pages' 1.811133x figure); on
+the batched workload, the committed tokens per round with per-row accepts
+against a round clamped to the shortest sequence, for drafts planted at
+accept lengths drawn uniformly from 0..T-1.
+
 Two further modes serve rocprofv3 counter runs: `--counter-pass` launches the
 QMM and a copy kernel of known size eagerly, and `--write-traffic` turns a
 FETCH_SIZE run and a WRITE_SIZE run of it into per-launch HBM bytes.
@@ -59,10 +67,10 @@ def qgemm_bytes(M, K, N, esz, group=64):
     return K * N // 2 + 4 * N * (K // group) + M * K * esz + 4 * M * N
 
 
-KERNEL_SOURCES = ("qgemm.hip", "qgemm_common.h", "qgemm_m16.hip")
+KERNEL_SOURCES = ("qgemm.hip", "qgemm_common.h", "qgemm_m16.hip", "qgemm_m8.hip")
 
 
-def projection_kernel(M, K, N, act, cus, group=64):
+def projection_kernel(M, K, N, act, cus, group=64, variant="auto"):
     """Name of the projection kernel the library launches for this shape (the
     order of the library's dispatch; a label for the bench line only)."""
     G, T = K // 64, (N + 15) // 16
@@ -76,6 +84,8 @@ def projection_kernel(M, K, N, act, cus, group=64):
     if (M <= 64 and K <= 2560 and G % 8 == 0 and N * (K // 2) < 0x7F000000
             and T >= 16 * workers and (group != 32 or (G // 2) % 4 == 0)):
         return "qgemm_w4_wide"
+    if M <= 8 and K % 256 == 0 and group in (64, 128) and variant != "m8":
+        return "qgemm_w4_m8q"
     if M <= 8 and K <= 5120:
         return "qgemm_w4_m8"
     if M <= 64 and K <= 2560:
@@ -181,11 +191,13 @@ def _counter_rows(run_dir):
 
 
 def _fused_kernel(kname):
-    """qgemm_w4_m8 with the verify epilogue (its eighth template argument)."""
-    if "qgemm_w4_m8<" not in kname:
-        return False
-    args = kname.split("qgemm_w4_m8<", 1)[1].split(">", 1)[0].split(",")
-    return len(args) > 7 and args[7].strip() == "true"
+    """The M <= 8 projection kernels' instances with the verify epilogue (the
+    eighth template argument of qgemm_w4_m8, the fifth of qgemm_w4_m8q)."""
+    for name, pos in (("qgemm_w4_m8<", 7), ("qgemm_w4_m8q<", 4)):
+        if name in kname:
+            args = kname.split(name, 1)[1].split(">", 1)[0].split(",")
+            return len(args) > pos and args[pos].strip() == "true"
+    return False
 
 
 def write_traffic(fetch_dir, write_dir, workload, M, group=64):
@@ -244,6 +256,9 @@ def main():
                     help="one step: the projection with the verify fused into its epilogue, "
                          "the two calls back to back, or (gate/up) the projection with its "
                          "SwiGLU epilogue")
+    ap.add_argument("--variant", choices=["auto", "m8", "m8q"], default="auto",
+                    help="pin the M <= 8 projection kernel (sets VQV_FORCE_VARIANT): m8q is "
+                         "the whole-line kernel, m8 the half-line one")
     ap.add_argument("--counter-pass", action="store_true",
                     help="eager QMM launches + a copy kernel, for one rocprofv3 --pmc pass")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -262,6 +277,8 @@ def main():
                   f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
 
+    if args.variant != "auto":
+        os.environ["VQV_FORCE_VARIANT"] = args.variant
     import numpy as np
     import torch
 
@@ -304,6 +321,15 @@ def main():
         rng = np.random.default_rng((c["seed"], 5))
         draft = torch.from_numpy(rng.integers(0, N, size=(B, max(T - 1, 1))).astype(np.int32)
                                  [:, :T - 1].copy()).to(dev)
+        if B > 1:
+            # Drafts planted around the library's own argmax at accept
+            # lengths drawn from 0..T-1, so that the rounds' accept counts
+            # vary per sequence (the batched workload's recipe).
+            a0 = vqv.vqv_verify(vqv.vqv_qgemm(x0, wq0, s0, b0, group=args.group),
+                                draft, B, T)[0].cpu().numpy()
+            planted = rng.integers(0, T, size=B)
+            draft = torch.from_numpy(gen.make_drafts(a0, B, T, N, seed=c["seed"],
+                                                     accept=planted).astype(np.int32)).to(dev)
         am = torch.empty(B * T, dtype=torch.int32, device=dev)
         al = torch.empty(B, dtype=torch.int32, device=dev)
         vws = torch.empty(max(vqv.vqv_verify_workspace_bytes(B, T, N), 8), dtype=torch.uint8,
@@ -397,7 +423,8 @@ def main():
     # Whole-step throughput: the K steps as one graph, replayed once untimed
     # (upload) and once timed, with nothing else queued.
     g_steps = graph_of(step, args.steps)
-    g_steps.replay()
+    for _ in range(3):                  # upload, then clocks and caches in steady state
+        g_steps.replay()
     ms_step = timed(g_steps) / args.steps
 
     # The same K steps launched one by one from Python, for reference.
@@ -445,7 +472,7 @@ def main():
 
     # Rows/s against M with the same weights (the first M rows of x): the
     # plain projection's per-launch time at M = 1 and 4 as well.
-    by_m = {}
+    by_m, n1024 = {}, None
     if args.workload == "target":
         for m_sub in (1, 4):
             xs_sub = [cp[0][:m_sub].contiguous() for cp in copies]
@@ -459,6 +486,42 @@ def main():
             t_m = statistics.fmean(timed(g_m) * 1e3 / nq for _ in range(3))
             by_m[m_sub] = {"us_per_launch": t_m, "rows_per_s": m_sub / (t_m * 1e-6)}
         by_m[M] = {"us_per_launch": q_mean, "rows_per_s": M / (q_mean * 1e-6)}
+        # The pages' figure is measured at K=5120, N=1024: the same K with a
+        # narrow output, rotated past the Infinity Cache.
+        rng_n = np.random.default_rng((c["seed"], 1024))
+        wn, sn, bn = gen.make_weights(rng_n, 1024, K, group)
+        Rn = math.ceil(2 * MALL_BYTES / (1024 * K // 2 + 4 * 1024 * (K // group))) + 1
+        narrow = [(torch.from_numpy(wn).to(dev),
+                   torch.from_numpy(sn.view(np.int16)).view(torch.float16).to(dev),
+                   torch.from_numpy(bn.view(np.int16)).view(torch.float16).to(dev))
+                  for _ in range(Rn)]
+        n1024 = {}
+        for m_sub in (4, 8):
+            xs_n = x0[:m_sub].contiguous()
+            ys_n = torch.empty((m_sub, 1024), dtype=torch.float32, device=dev)
+
+            def qn(i, st, xs_n=xs_n, ys_n=ys_n):
+                wc, sc, bc = narrow[i % Rn]
+                vqv.vqv_qgemm(xs_n, wc, sc, bc, y=ys_n, group=group, stream=st)
+            ln = Rn * max(1, math.ceil(QMM_LAUNCHES / Rn))
+            g_n = graph_of(qn, ln)
+            g_n.replay()
+            t_n = statistics.fmean(timed(g_n) * 1e3 / ln for _ in range(3))
+            n1024[m_sub] = {"us_per_launch": t_n, "rows_per_s": m_sub / (t_n * 1e-6)}
+        n1024["m8_over_m4_rows"] = n1024[8]["rows_per_s"] / n1024[4]["rows_per_s"]
+        n1024["pages_m8_over_m4_rows"] = 1.811133
+        del narrow
+
+    clamp = None
+    if T and B > 1:
+        ver(stream)
+        torch.cuda.synchronize()
+        acc = al.cpu().numpy().astype(int)
+        # Committed tokens per round: every sequence keeps its own accept count
+        # plus its bonus token, against a round clamped to the shortest one.
+        clamp = {"accept_len": acc.tolist(), "min_accept_len": int(acc.min()),
+                 "tokens_per_round_per_row": int((acc + 1).sum()),
+                 "tokens_per_round_clamped": int(B * (acc.min() + 1))}
 
     props = torch.cuda.get_device_properties(dev)
     device = {"name": props.name, "cus": props.multi_processor_count,
@@ -472,7 +535,7 @@ def main():
     # epilogue, 8 bytes per row and work-group, and is timed with the finish
     # kernel in fused_us_mean).
     k_us = q_mean
-    kname = projection_kernel(M, K, N, act, props.multi_processor_count, group)
+    kname = projection_kernel(M, K, N, act, props.multi_processor_count, group, args.variant)
     if use_swiglu:
         # The step's kernel is the projection with the SwiGLU epilogue: it
         # writes h [M, N/2] instead of y [M, N].
@@ -510,9 +573,17 @@ def main():
         "swiglu_us_mean": statistics.fmean(s_runs) if s_runs else None,
         "step_path": "fused" if use_fused else ("swiglu" if use_swiglu else "separate"),
         "step_hbm_gbs": (qb + (4 * M * N if T and not use_fused else 0)) / (ms_step * 1e-3) / 1e9,
+        # The step's own projection instance carries the argmax epilogue and is
+        # followed by the finishing kernel: the fused call's mean launch time
+        # bounds it from above (rocprofv3 separates the two kernels).
+        "fused_call_frac": (qb / (statistics.fmean(f_runs) * 1e-6) / 1e9 / HBM_PEAK_GBS
+                            if f_runs else None),
         "device": device,
         "copy_probe_gbs": copy_gbs,
         "qgemm_by_M": by_m or None,
+        "k5120_n1024_by_M": n1024,
+        "batched_accepts": clamp,
+        "variant": args.variant,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "frac_of_copy_probe": achieved / copy_gbs,
                      "traffic": None if use_swiglu or args.n else

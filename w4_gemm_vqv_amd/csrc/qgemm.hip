@@ -985,9 +985,7 @@ hipError_t launch_w4(const void* x, const uint8_t* wq, const uint16_t* scales,
   if (gs > 0) kern = qgemm_w4<ACT, R, TILES, WN, WK, D, KC, XALL, 1>;
   if (gs < 0) kern = qgemm_w4<ACT, R, TILES, WN, WK, D, KC, XALL, -1>;
   if (lds_bytes > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             lds_bytes);
+    const hipError_t e = allow_lds(reinterpret_cast<const void*>(kern));
     if (e != hipSuccess) return e;
   }
   const dim3 grid((N + cols - 1) / cols);
@@ -1013,9 +1011,7 @@ hipError_t launch_m8(const void* x, const uint8_t* wq, const uint16_t* scales,
     if (gs < 0) kern = qgemm_w4_m8<ACT, NW, TW, DB, RB, D0, XB, false, -1>;
   }
   if (L.total > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             L.total);
+    const hipError_t e = allow_lds(reinterpret_cast<const void*>(kern));
     if (e != hipSuccess) return e;
   }
   const dim3 grid((N + cols - 1) / cols);

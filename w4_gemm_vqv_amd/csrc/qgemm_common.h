@@ -6,6 +6,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+#include <unordered_map>
+
 #include "vqv_internal.h"
 
 namespace vqv {
@@ -161,14 +165,48 @@ __device__ __forceinline__ void sb_pairs(const u32x4& s, const u32x4& b, u32x4& 
 }
 
 constexpr int kLdsLimit = 160 * 1024;
+constexpr int kMaxDevices = 64;
+
+// The launchers' two per-device facts, looked up once per device (or per
+// kernel and device) and kept for the life of the process: the CU count that
+// sizes the grids, and the dynamic LDS limit a kernel may launch with.
+inline int current_device() {
+  int dev = 0;
+  return hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices ? dev : -1;
+}
 
 inline int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+  static std::atomic<int> known[kMaxDevices];
+  const int dev = current_device();
+  if (dev < 0) return 256;
+  int cus = known[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     return 256;
+  known[dev].store(cus, std::memory_order_relaxed);
   return cus;
+}
+
+// Lets `kern` launch with up to kLdsLimit bytes of dynamic LDS on the current
+// device (hipFuncSetAttribute once per kernel and device).
+inline hipError_t allow_lds(const void* kern) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, unsigned long long> done;  // device bits
+  const int dev = current_device();
+  const unsigned long long bit = 1ull << (dev < 0 ? kMaxDevices - 1 : dev);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = done.find(kern);
+    if (dev >= 0 && it != done.end() && (it->second & bit)) return hipSuccess;
+  }
+  const hipError_t e =
+      hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+  if (e == hipSuccess && dev >= 0) {
+    std::lock_guard<std::mutex> lock(mu);
+    done[kern] |= bit;
+  }
+  return e;
 }
 
 }  // namespace vqv

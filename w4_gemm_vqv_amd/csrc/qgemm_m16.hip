@@ -971,9 +971,7 @@ hipError_t launch_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
     if (gs < 0) kern = qgemm_w4_m16<ACT, W, T, DB, RB, D0, X, SWIGLU, false, -1>;
   }
   if (L.total > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             L.total);
+    const hipError_t e = allow_lds(reinterpret_cast<const void*>(kern));
     if (e != hipSuccess) return e;
   }
   const dim3 grid(workers * rsets);
@@ -1012,9 +1010,7 @@ hipError_t launch_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
     if (gs < 0) return hipErrorInvalidValue;         // never launched
   }
   if (lds_bytes > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             lds_bytes);
+    const hipError_t e = allow_lds(reinterpret_cast<const void*>(kern));
     if (e != hipSuccess) return e;
   }
   const int T = (N + 15) / 16;
@@ -1323,8 +1319,7 @@ hipError_t launch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
   auto kern = qgemm_w4_rows<ACT, RS, kRowsKT, kRowsKCP, 0>;
   if (gs > 0) kern = qgemm_w4_rows<ACT, RS, kRowsKT, kRowsKCP, 1>;
   if (gs < 0) kern = qgemm_w4_rows<ACT, RS, kRowsKT, kRowsKCP, -1>;
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(kern));
   if (e != hipSuccess) return e;
   const int cus = device_cus();
   const int T = (N + 15) / 16;

@@ -488,9 +488,7 @@ hipError_t launch_q8(const void* x, const uint8_t* wq, const uint16_t* scales,
     kern = va.argmax ? qgemm_w4_m8q<ACT, kQ8D, XB, kQ8Aux, true, 1>
                      : qgemm_w4_m8q<ACT, kQ8D, XB, kQ8Aux, false, 1>;
   if (L.total > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             L.total);
+    const hipError_t e = allow_lds(reinterpret_cast<const void*>(kern));
     if (e != hipSuccess) return e;
   }
   const dim3 grid((N + cols - 1) / cols);
