@@ -340,10 +340,6 @@ def main():
         fws = torch.zeros(vqv.vqv_qgemm_verify_workspace_bytes(M, K, N, group, vqv_act),
                           dtype=torch.uint8, device=dev)
     use_fused = fused_ok and args.path == "fused"
-    # The call fuses the argmax into the projection's epilogue when its
-    # workspace holds only per-group partials; otherwise (M > 8, fp32
-    # activations, group 32) it runs the projection and the two-stage verify.
-    epilogue_fused = use_fused and fws.numel() < M * N * 4
     use_swiglu = args.path == "swiglu"
     if use_swiglu:
         if T or N % 2:
@@ -559,9 +555,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: W4 group-{group} QMM M={M} K={K} N={N} {act} "
                                + (f"+ greedy verify B={B} T={T}" if T else "(no verify)")
-                               + (" (verify fused into the QMM epilogue)" if epilogue_fused
-                                  else " (one vqv_qgemm_verify call: projection, then the "
-                                       "two-stage verify)" if use_fused else "")
+                               + (" (verify fused into the QMM epilogue)" if use_fused
+                                  else "")
                                + (" with the SwiGLU epilogue, h[M, N/2]" if use_swiglu else ""),
                    "M": M, "K": K, "N": N, "group": group, "act": act, "verify_B": B,
                    "verify_T": T, "weight_copies": R},

@@ -33,12 +33,15 @@
  *   output bits on every call.
  *
  * Errors
- *   Arguments are checked on the host before anything is launched. A call
- *   that returns VQV_ERR_ARG, VQV_ERR_UNSUPPORTED, VQV_ERR_ALIGN or
- *   VQV_ERR_WORKSPACE has launched nothing and written nothing. VQV_ERR_HIP
- *   means the HIP runtime refused a launch (hipGetLastError); in the calls
- *   that launch two kernels it can come after the first was enqueued, which
- *   may then write its outputs and scratch.
+ *   Arguments are checked on the host before anything is launched, and so
+ *   is the choice of kernel (a problem no kernel's LDS image takes returns
+ *   VQV_ERR_UNSUPPORTED). A call that returns VQV_ERR_ARG,
+ *   VQV_ERR_UNSUPPORTED, VQV_ERR_ALIGN or VQV_ERR_WORKSPACE has launched
+ *   nothing and written nothing. VQV_ERR_HIP means the HIP runtime refused a
+ *   launch (hipGetLastError); in the calls that launch two kernels it can
+ *   come after the first was enqueued, which may then write its outputs and
+ *   scratch. Each call clears the calling thread's HIP error state
+ *   (hipGetLastError) before its first launch.
  */
 #ifndef VQV_H
 #define VQV_H
@@ -50,7 +53,7 @@
 extern "C" {
 #endif
 
-#define VQV_ABI_VERSION 5
+#define VQV_ABI_VERSION 6
 
 typedef enum {
   VQV_BF16 = 0, /* bfloat16 activations                                  */
@@ -177,14 +180,15 @@ vqv_status vqv_verify_ex(const float* logits, const int32_t* draft, const int32_
 
 /*
  * Projection and greedy verify in one call: y = x . W^T as vqv_qgemm, then
- * argmax and accept_len of y as vqv_verify with B*T == M. Where it applies
- * (M <= 8, bf16/fp16 activations, K within the single-row-set kernel's LDS
- * budget: K <= 5120 for every N), the argmax is fused into the projection's
- * epilogue, so the logits are never read back ("dspark: fold first-token
- * forward into verify + bit-exact M5 Metal decode wins", first commit: the
- * fused argmax of the CUDA path and the single accept loop; "perf: tune
- * DFlash2 M=8 verification for M1 and M2", PR description: the verify
- * projection at M=8). Elsewhere the two operations run back to back.
+ * argmax and accept_len of y as vqv_verify with B*T == M. The argmax is
+ * fused into the projection's epilogue (every row count 1..64, activation
+ * type and group size): each work-group of the projection keeps the two
+ * best values of each row over its columns, and one small kernel per
+ * sequence reduces them and walks the drafts, so the logits are never read
+ * back ("dspark: fold first-token forward into verify + bit-exact M5 Metal
+ * decode wins", first commit: the fused argmax of the CUDA path and the
+ * single accept loop; "perf(speculative): commit per-row accepts in batched
+ * DFlash", commit message: the batched verify of B = 4 blocks of 16).
  *
  * Arguments
  *   x, wq, scales, biases, M, K, N, group, act_dtype
@@ -194,9 +198,12 @@ vqv_status vqv_verify_ex(const float* logits, const int32_t* draft, const int32_
  *   draft, B, T, argmax, accept_len
  *              as vqv_verify, with B*T == M (else VQV_ERR_ARG).
  *   workspace  at least vqv_qgemm_verify_workspace_bytes(M, K, N, group,
- *              act_dtype) bytes, 256-byte aligned. Calls that share a
- *              workspace must not overlap in time (same stream, or
- *              synchronized).
+ *              act_dtype) bytes, 256-byte aligned: 256 bytes and one 16-byte
+ *              partial per row and projection work-group (at most 64 x 256
+ *              partials on the vocabulary kernels, N/16 to N/80 per row on
+ *              the others); 0 for arguments the call rejects. Its contents
+ *              on entry do not matter. Calls that share a workspace must not
+ *              overlap in time (same stream, or synchronized).
  * The results are bit-identical to vqv_qgemm followed by vqv_verify on the
  * same inputs.
  */
@@ -225,15 +232,16 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
 /*
  * vqv_qgemm_verify_ex for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
- * hipMalloc. It takes no workspace: its scratch (the fused kernel's per-row
- * partials, or the two-stage verify's partials, plus the logits when y is
- * NULL) lives in a static device array of VQV_NOALLOC_SCRATCH_BYTES bytes
- * that the library holds on each GPU it runs on until the process ends. The
- * arguments and results are those of vqv_qgemm_verify_ex.
+ * hipMalloc. It takes no workspace: its scratch (the projection's per-row
+ * partials, vqv_qgemm_verify_workspace_bytes of them) lives in a static
+ * device array of VQV_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * each GPU it runs on until the process ends. The arguments and results are
+ * those of vqv_qgemm_verify_ex.
  *   A problem whose scratch exceeds VQV_NOALLOC_SCRATCH_BYTES returns
- *   VQV_ERR_WORKSPACE with nothing launched (at M <= 8 with 16-bit
- *   activations that is N above roughly 650,000; with y NULL on the two-stage
- *   path, M*N*4 above about 1 MB).
+ *   VQV_ERR_WORKSPACE with nothing launched (on 80-column work-groups, M <= 8
+ *   with 16-bit activations, that is N above roughly 650,000; on 64-column
+ *   work-groups at M = 64, N above about 65,000 where the vocabulary kernels
+ *   do not apply).
  *   The first call on a device looks the array up (hipGetSymbolAddress);
  *   VQV_ERR_HIP if that fails. No call allocates or frees anything.
  *   All calls on one GPU share that GPU's array: calls that overlap in time

@@ -53,7 +53,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.vqv_abi_version() == 5
+    assert L.vqv_abi_version() == 6
     for s in range(6):
         assert L.vqv_status_string(s)
     assert L.vqv_status_string(99) == b"unknown status"
@@ -69,16 +69,26 @@ def test_workspace_queries(L):
 
 
 def test_fused_workspace_queries(L):
+    """The fused call's scratch is a 256-byte head and one 16-byte top-two
+    partial per (row, work-group covering the row): never room for logits.
+    Without a GPU the library plans for 256 CUs."""
     head = 256
     fused = L.vqv_qgemm_verify_workspace_bytes(8, 5120, 17408, 64, BF16)
-    assert head < fused <= head + 128 * 1024  # per-group partials only
-    fallback = L.vqv_qgemm_verify_workspace_bytes(16, 512, 1000, 64, BF16)
-    assert fallback >= head + 16 * 1000 * 4  # room for the logits
-    assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 64, FP32) >= head + 8 * 1000 * 4
+    assert head < fused <= head + 8 * 256 * 16
+    # the batched vocabulary projection: 250 work-groups of 38 column tiles each
+    assert L.vqv_qgemm_verify_workspace_bytes(64, 2560, 151936, 64, BF16) == head + 64 * 250 * 16
+    # 16 rows on the 16-row kernel (250 workers), fp32 on 16-column work-groups
+    assert L.vqv_qgemm_verify_workspace_bytes(16, 512, 1000, 64, BF16) == head + 16 * 250 * 16
+    assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 64, FP32) == head + 8 * 63 * 16
+    for M, K, N, group, act in [(16, 5120, 4000, 64, FP16), (64, 256, 700, 64, BF16),
+                                (32, 512, 200000, 64, BF16), (8, 512, 1000, 32, BF16),
+                                (40, 3072, 2000, 128, FP32), (1, 16384, 100, 64, BF16)]:
+        n = L.vqv_qgemm_verify_workspace_bytes(M, K, N, group, act)
+        assert head < n and (n - head) % (16 * M) == 0, (M, K, N, group, act, n)
     assert L.vqv_qgemm_verify_workspace_bytes(0, 512, 1000, 64, BF16) == 0
+    assert L.vqv_qgemm_verify_workspace_bytes(65, 512, 1000, 64, BF16) == 0
     assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 16, BF16) == 0
-    # group 32 has no fused kernel: room for the logits
-    assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 32, BF16) >= head + 8 * 1000 * 4
+    assert L.vqv_qgemm_verify_workspace_bytes(8, 512, 1000, 64, 7) == 0
     # group 128 takes the same paths as group 64
     assert (L.vqv_qgemm_verify_workspace_bytes(8, 5120, 17408, 128, BF16) ==
             L.vqv_qgemm_verify_workspace_bytes(8, 5120, 17408, 64, BF16))
@@ -175,10 +185,11 @@ def test_fused_ex_rejects(L, kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), ARG), (dict(B=2), ARG), (dict(group=16), UNSUP), (dict(am=AM + 2), ALIGN),
     (dict(mg=Y), ARG), (dict(dl=AM), ARG), (dict(y=X), ARG), (dict(K=16384 + 64), UNSUP),
-    # scratch beyond VQV_NOALLOC_SCRATCH_BYTES: the fused partials of a very wide
-    # projection, and the logits of a two-stage call without y
+    # scratch beyond VQV_NOALLOC_SCRATCH_BYTES: the partials of very wide
+    # projections on 64- or 80-column work-groups
     (dict(K=5120, N=1_000_000, wq=1 << 36, s=2 << 36, b=3 << 36, y=4 << 36), WS),
-    (dict(M=16, B=2, y=None, N=20000), WS),
+    (dict(M=64, B=4, T=16, K=5120, N=300_000, wq=1 << 36, s=2 << 36, b=3 << 36, y=4 << 36,
+          dr=5 << 36, dl=6 << 36, am=7 << 36, ac=8 << 36, mg=9 << 36), WS),
 ])
 def test_noalloc_rejects(L, kw, status):
     """Rejections of the allocation-free call come before it looks up its

@@ -4,8 +4,8 @@ draft counts (draft_len) and the top-1 minus top-2 margin of each row.
 vqv_verify_ex is fed the same fp32 logits as the oracle's verify_ref and must
 match it bit for bit: argmax, accept_len and margin (every NaN counts as one
 NaN). vqv_qgemm_verify_ex must equal vqv_qgemm followed by vqv_verify_ex on
-the fused path and on the fallback, and the oracle's verify of the GPU's own
-logits.
+every projection kernel's fused epilogue (1..64 rows), and the oracle's
+verify of the GPU's own logits.
 """
 
 import numpy as np
@@ -157,7 +157,8 @@ def compare_fused(vqv, c, B, T, accept=None, draft_len=None, want_y=True, ws=Non
                                             draft_len=lt, want_y=want_y, workspace=ws)
     torch.cuda.synchronize()
     if want_y:
-        assert torch.equal(y1, y2), "fused y differs from vqv_qgemm"
+        assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)), \
+            "fused y differs from vqv_qgemm"
     assert torch.equal(a1, a2)
     assert torch.equal(l1, l2), (l1.cpu().numpy(), l2.cpu().numpy())
     np.testing.assert_array_equal(bits(m2.cpu().numpy()), bits(m1.cpu().numpy()))
@@ -182,11 +183,36 @@ def test_fused_ex_matches_separate(vqv, M, K, N, act, B, T):
 
 
 @pytest.mark.parametrize("M,K,N,act,B,T", [
-    (16, 512, 1000, "bf16", 1, 16), (64, 256, 700, "fp16", 4, 16), (8, 512, 700, "fp32", 1, 8),
-    (8, 8192, 300, "bf16", 1, 8),
+    # 16-row kernel, general kernel (large K, fp32), batched vocabulary kernel,
+    # whole-tile kernel with 16 rows and with two row sets
+    (16, 512, 1000, "bf16", 1, 16), (64, 256, 700, "fp16", 4, 16), (32, 2560, 5000, "bf16", 2, 16),
+    (16, 5120, 3000, "bf16", 2, 8), (48, 3072, 900, "fp16", 3, 16), (8, 512, 700, "fp32", 1, 8),
+    (64, 512, 2000, "fp32", 4, 16), (8, 8192, 300, "bf16", 1, 8),
+    (64, 512, 40000, "bf16", 4, 16), (32, 1024, 151936, "fp16", 2, 16), (20, 256, 30000, "bf16", 4, 5),
+    (16, 1024, 66001, "bf16", 1, 16), (32, 512, 200000, "fp16", 4, 8),
 ])
-def test_fallback_ex_matches_separate(vqv, M, K, N, act, B, T):
+def test_rows_beyond_8_ex_matches_separate(vqv, M, K, N, act, B, T):
     compare_fused(vqv, case(M, K, N, act, seed=M + K + N + 3), B, T)
+
+
+@pytest.mark.parametrize("M,K,N,act,B,T", [
+    (8, 5120, 17408, "bf16", 1, 8), (8, 512, 70000, "fp16", 1, 8), (64, 512, 40000, "bf16", 4, 16),
+    (16, 512, 1000, "bf16", 2, 8), (16, 5120, 3000, "bf16", 1, 16), (8, 512, 700, "fp32", 1, 8),
+    (32, 512, 200000, "bf16", 2, 16), (4, 1280, 3000, "fp16", 2, 2),
+])
+def test_fused_ex_nan_columns(vqv, M, K, N, act, B, T):
+    """NaN scales in three columns make those logits NaN in every row: each
+    kernel family's epilogue must report the first of them as the argmax and a
+    NaN margin, as the separate path and the oracle do."""
+    c = case(M, K, N, act, seed=M * 5 + K + N)
+    s = c["scales"].copy()
+    cols = sorted({N // 3, N // 3 + 17, N - 2})
+    for col in cols:
+        s[col, 0] = np.uint16(0x7E00)                # fp16 NaN
+    c["scales"] = s
+    _, a, _, m = compare_fused(vqv, c, B, T)
+    assert (a.cpu().numpy() == cols[0]).all()
+    assert np.isnan(m.cpu().numpy()).all()
 
 
 def test_fused_ex_without_logits_and_reused_workspace(vqv):
@@ -208,3 +234,8 @@ def test_full_size_target_ex(vqv):
 def test_full_size_vocab_ex(vqv):
     compare_fused(vqv, gen.make_config("vocab_verify"), 1, 8, accept=np.array([7]),
                   draft_len=np.array([7], np.int32))
+
+
+def test_full_size_batched_ex(vqv):
+    compare_fused(vqv, gen.make_config("batched_vocab"), 4, 16,
+                  accept=np.array([15, 9, 0, 4]), draft_len=np.array([15, 12, 3, 2], np.int32))

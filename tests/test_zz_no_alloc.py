@@ -62,13 +62,16 @@ def _same(ref, out, what):
             f"{what}: y bits"
 
 
-# (M, K, N, act, B, T, with_y): a larger call, then a smaller one, per path.
-FUSED = [(8, 5120, 17408, "bf16", 1, 8, True), (4, 512, 1000, "fp16", 1, 4, True)]
-TWO_STAGE = [(16, 1024, 5000, "bf16", 2, 8, True), (12, 512, 3000, "bf16", 3, 4, False)]
+# (M, K, N, act, B, T, with_y): a larger call, then a smaller one, per kernel
+# family (8-row, 16-row and batched vocabulary kernels, fp32 activations).
+ROWS8 = [(8, 5120, 17408, "bf16", 1, 8, True), (4, 512, 1000, "fp16", 1, 4, True)]
+ROWS16 = [(16, 1024, 5000, "bf16", 2, 8, True), (12, 512, 3000, "bf16", 3, 4, False)]
+BATCHED = [(64, 512, 40000, "bf16", 4, 16, False), (32, 512, 33000, "fp16", 2, 16, True)]
 FP32 = [(8, 1024, 2048, "fp32", 2, 4, True), (4, 512, 700, "fp32", 1, 4, False)]
 
 
-@pytest.mark.parametrize("calls", [FUSED, TWO_STAGE, FP32], ids=["fused", "two_stage", "fp32"])
+@pytest.mark.parametrize("calls", [ROWS8, ROWS16, BATCHED, FP32],
+                         ids=["rows8", "rows16", "batched", "fp32"])
 def test_noalloc_matches_workspace_call(vqv, calls):
     for i, (M, K, N, act, B, T, with_y) in enumerate(calls):
         d, draft, dl = _case(M, K, N, act, B, T, seed=100 * M + i)
@@ -79,7 +82,7 @@ def test_noalloc_matches_workspace_call(vqv, calls):
 def test_noalloc_rejects_oversized_scratch(vqv):
     """A problem whose scratch exceeds the static array is refused before any
     launch: the outputs keep their sentinels."""
-    M, K, N, B, T = 16, 512, 20000, 2, 8        # two-stage, logits in scratch: 1.28 MB
+    M, K, N, B, T = 8, 64, 1_000_000, 1, 8      # 12,500 work-groups: 1.6 MB of partials
     d, draft, dl = _case(M, K, N, "bf16", B, T, seed=5)
     am = torch.full((B * T,), -7, dtype=torch.int32, device="cuda")
     al = torch.full((B,), -7, dtype=torch.int32, device="cuda")

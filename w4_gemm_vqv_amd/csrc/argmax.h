@@ -96,6 +96,61 @@ __device__ __forceinline__ Top2 top2_best64(Top2 t) {
   return r;
 }
 
+// A lane's running top two over values offered in increasing index order,
+// compared as fp32 (ties keep the earlier index, -0 ties +0, denormals
+// compare exactly: the kernels keep fp32 denormals). b1 is the best number
+// and i1 its index (b1 NaN and i1 INT_MAX while no number has been offered),
+// b2 the best of the other numbers (NaN while there is none), inan the index
+// of the first NaN offered (INT_MAX: none). About half the instructions of
+// top2_add per value.
+struct Top2Scan {
+  float b1, b2;
+  int i1, inan;
+};
+
+__device__ __forceinline__ Top2Scan top2_scan_none() {
+  const float none = __uint_as_float(0x7FC00000u);
+  return Top2Scan{none, none, INT_MAX, INT_MAX};
+}
+
+// Offer v at index i. `num` says v is not NaN; a caller that knows it passes
+// true and leaves inan alone. A NaN value (num false) is not a candidate, but
+// it may leave b2 NaN: a row with a NaN has the NaN margin whatever b2 is.
+__device__ __forceinline__ void top2_scan(Top2Scan& s, float v, int i, bool num = true) {
+  const bool take = num && !(v <= s.b1);       // the first number: b1 is NaN
+  const float other = take ? s.b1 : v;
+  s.b2 = !(other <= s.b2) ? other : s.b2;      // b2 NaN: none yet
+  s.b1 = take ? v : s.b1;
+  s.i1 = take ? i : s.i1;
+  if (!num) s.inan = min(s.inan, i);
+}
+
+// The scan as a Top2. With a NaN the first NaN is the best (key 0xFFFFFFFF)
+// and k2 is the best number's key: the exact k2 would be the NaN key when a
+// second NaN was offered, but a row holding a NaN has the NaN margin and its
+// first NaN as argmax either way.
+__device__ __forceinline__ Top2 top2_of_scan(const Top2Scan& s) {
+  const unsigned kb = s.i1 == INT_MAX ? 0u : order_key(s.b1);
+  if (s.inan != INT_MAX) return Top2{0xFFFFFFFFu, s.inan, kb};
+  return Top2{kb, s.i1, s.b2 != s.b2 ? 0u : order_key(s.b2)};
+}
+
+// A candidate packed for merging by 64-bit compares: (k1 << 32 | ~i1) puts
+// the higher key first and, among equal keys, the lower index.
+__device__ __forceinline__ unsigned long long top2_rank(unsigned k1, int i1) {
+  return (unsigned long long)k1 << 32 | (unsigned)~i1;
+}
+
+// top2_merge of a candidate (k1, i1, k2) into (ak1, ai1, ak2), on ranks.
+__device__ __forceinline__ void top2_merge_ranked(unsigned& ak1, int& ai1, unsigned& ak2,
+                                                  unsigned k1, int i1, unsigned k2) {
+  const bool win = top2_rank(k1, i1) > top2_rank(ak1, ai1);
+  const unsigned lose = win ? ak1 : k1;
+  ak2 = max(max(ak2, k2), lose);
+  ak1 = win ? k1 : ak1;
+  ai1 = win ? i1 : ai1;
+}
+
 // A partial as stored in a workspace: (k1, i1, k2, unused).
 __device__ __forceinline__ uint4 top2_pack(const Top2& t) {
   return make_uint4(t.k1, (unsigned)t.i1, t.k2, 0u);

@@ -121,7 +121,7 @@ template <int ACT, int R, int TILES, int WN, int WK, int D, int KC, bool XALL, i
 __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
-    float* __restrict__ y, int M, int K, int N, int cols) {
+    float* __restrict__ y, int M, int K, int N, int cols, VerifyArgs va) {
   using TR = ActTraits<ACT>;
   // GS: group 64 << GS for GS >= 0; GS = -1 is group 32, a scale and bias
   // per 32-k half: each step's MFMAs run once per half (the other half's
@@ -474,7 +474,12 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
           red[((((wk * WN + wn) * R + r) * TILES + tt) * 8 + 4 * (lane >> 4) + e) * 16 + j] = v;
       }
   __syncthreads();
+  // With the fused verify, the 16 outputs idx .. idx + 15 (one row, 16
+  // columns, held by 16 adjacent lanes) reduce to one top-two candidate in
+  // slot idx / 16 after the partial sums.
+  const bool fused = va.argmax != nullptr;           // uniform
   constexpr int OUTS = WN * R * TILES * 128;
+  unsigned* cand = reinterpret_cast<unsigned*>(red + WK * OUTS);  // [OUTS / 16] x (k1, i1, k2)
   for (int idx = tid; idx < OUTS; idx += NT) {
     float s = 0.0f;
 #pragma unroll
@@ -487,7 +492,37 @@ __global__ __launch_bounds__(64 * WN * WK) void qgemm_w4(
     const int wn2 = rest / (TILES * R);
     const int m = 8 * r + m8;
     const int c = wn2 * WCOLS + 16 * tt + jj;
-    if (m < M && c < wgcols) y[(size_t)m * N + wg0 + c] = s;
+    const bool out = m < M && c < wgcols;
+    if (out && (!fused || y)) y[(size_t)m * N + wg0 + c] = s;
+    if (fused) {                                     // uniform per 16 lanes
+      Top2 t = top2_none();
+      if (out) top2_add(t, s, wg0 + c);
+      top2_best16(t);
+      if (jj == 0) {
+        unsigned* q = cand + (idx >> 4) * 3;
+        q[0] = t.k1;
+        q[1] = (unsigned)t.i1;
+        q[2] = t.k2;
+      }
+    }
+  }
+  if (!fused) return;
+
+  // ---- fused greedy verify, first half: thread m < M merges row m's
+  // candidates, slots ((wn * R + m / 8) * TILES + tt) * 8 + m % 8, and writes
+  // the work-group's partial for that row.
+  __syncthreads();
+  if (tid < M) {
+    const int r = tid >> 3, m8 = tid & 7;
+    Top2 b = top2_none();
+#pragma unroll
+    for (int wn2 = 0; wn2 < WN; ++wn2)
+#pragma unroll
+      for (int tt = 0; tt < TILES; ++tt) {
+        const unsigned* q = cand + (((wn2 * R + r) * TILES + tt) * 8 + m8) * 3;
+        top2_merge(b, q[0], (int)q[1], q[2]);
+      }
+    va.partials[(size_t)tid * va.pgroups + blockIdx.x] = top2_pack(b);
   }
 }
 
@@ -961,7 +996,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m8(
       const unsigned* p = cand + (w * 4 + (lane & 3)) * 3;
       top2_merge(r, p[0], (int)p[1], p[2]);
     }
-    va.partials[(size_t)blockIdx.x * 8 + lane] = top2_pack(r);
+    va.partials[(size_t)lane * va.pgroups + blockIdx.x] = top2_pack(r);
   }
 }
 
@@ -971,14 +1006,15 @@ int lds_bytes_for(int K, int gs) {
   constexpr int P = ActTraits<ACT>::parts;
   const LdsLayout L = gs < 0 ? lds_layout<R, P, WK, KC, WGC, XALL, true>(K >> 6)
                              : lds_layout<R, P, WK, KC, WGC, XALL, false>(K >> 6);
-  const int red_bytes = WK * WN * R * TILES * 128 * 4;
+  // The partial sums of the reduction, then the fused verify's candidates.
+  const int red_bytes = WK * WN * R * TILES * 128 * 4 + WN * R * TILES * 8 * 12;
   return L.total > red_bytes ? L.total : red_bytes;
 }
 
 template <int ACT, int R, int TILES, int WN, int WK, int D, int KC, bool XALL>
 hipError_t launch_w4(const void* x, const uint8_t* wq, const uint16_t* scales,
                      const uint16_t* biases, float* y, int M, int K, int N, int cols, int gs,
-                     hipStream_t stream) {
+                     const VerifyArgs& va, hipStream_t stream) {
   const int lds_bytes = lds_bytes_for<ACT, R, TILES, WN, WK, D, KC, XALL>(K, gs);
   if (lds_bytes > kLdsLimit) return hipErrorInvalidValue;  // never launched
   auto kern = qgemm_w4<ACT, R, TILES, WN, WK, D, KC, XALL, 0>;
@@ -990,7 +1026,7 @@ hipError_t launch_w4(const void* x, const uint8_t* wq, const uint16_t* scales,
   }
   const dim3 grid((N + cols - 1) / cols);
   hipLaunchKernelGGL(kern, grid, dim3(64 * WN * WK), lds_bytes, stream, x, wq, scales, biases,
-                     y, M, K, N, cols);
+                     y, M, K, N, cols, va);
   return hipGetLastError();
 }
 
@@ -1068,110 +1104,166 @@ bool use_m8q(int M, int K, int act, int gs) {
   return forced_variant() != kVariantM8 && qgemm_m8q_fits(M, K, act, gs);
 }
 
-// Configuration per problem. M <= 8 (one row set): when the work-group's
-// whole activation range fits in LDS, the barrier-free XALL kernel; narrow N
-// is split into exactly one work-group per CU (columns rounded up to 4, up
-// to five waves of 16), wide N into 64-column groups.
+// ---------------------------------------------------------------------------
+// Kernel choice. plan_for picks the kernel of a problem (for qgemm_w4 also
+// its configuration and columns per work-group) before anything is
+// launched, and checks that its LDS image fits. The plain projection and the
+// fused verify take the same plan, so their outputs agree bit for bit.
+enum class Path { None, Rows, Wide, M8Q, M8, M16, W4 };
+struct Plan {
+  Path path;
+  int cfg;   // qgemm_w4 configuration (W4)
+  int cols;  // columns per work-group (M8Q, M8, W4)
+};
+
+// qgemm_w4 configurations (R, TILES, WN, WK, D, KC, XALL), by index.
+#define VQV_W4_CONFIGS(X)             \
+  X(0, 1, 1, 5, 2, 8, 1, true)        \
+  X(1, 1, 1, 1, 8, 1, 1, false)       \
+  X(2, 1, 1, 4, 2, 8, 1, true)        \
+  X(3, 1, 1, 4, 2, 4, 2, false)       \
+  X(4, 2, 1, 4, 2, 4, 2, false)       \
+  X(5, 2, 1, 2, 1, 2, 1, false)       \
+  X(6, 4, 1, 4, 1, 4, 1, false)       \
+  X(7, 4, 1, 2, 1, 2, 1, false)       \
+  X(8, 8, 1, 4, 1, 2, 1, false)       \
+  X(9, 8, 1, 2, 1, 2, 1, false)
+
 template <int ACT>
-hipError_t dispatch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
-                         const uint16_t* biases, float* y, int M, int K, int N, int gs,
-                         hipStream_t s) {
-  if constexpr (ACT != ACT_FP32) if (qgemm_rows_fits(M, K, N, ACT)) {
-    // 17..64 rows at vocabulary widths: all row sets on one weight stream.
-    return launch_qgemm_rows(x, wq, scales, biases, y, M, K, N, ACT, gs, s);
+bool w4_fits(int cfg, int K, int gs) {
+  switch (cfg) {
+#define VQV_W4_FITS(i, R, T, WN, WK, D, KC, XA) \
+  case i: return lds_bytes_for<ACT, R, T, WN, WK, D, KC, XA>(K, gs) <= kLdsLimit;
+    VQV_W4_CONFIGS(VQV_W4_FITS)
+#undef VQV_W4_FITS
   }
-  if (qgemm_wide_fits(M, K, N, ACT, gs)) {
-    // Vocabulary widths: whole-tile waves (the fused verify's projection
-    // takes the same kernel, so the two paths agree bit for bit).
-    const VerifyArgs none{};
-    return launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, ACT, gs, none, s);
+  return false;
+}
+
+template <int ACT>
+hipError_t launch_w4_cfg(int cfg, const void* x, const uint8_t* wq, const uint16_t* scales,
+                         const uint16_t* biases, float* y, int M, int K, int N, int cols, int gs,
+                         const VerifyArgs& va, hipStream_t s) {
+  switch (cfg) {
+#define VQV_W4_LAUNCH(i, R, T, WN, WK, D, KC, XA) \
+  case i:                                         \
+    return launch_w4<ACT, R, T, WN, WK, D, KC, XA>(x, wq, scales, biases, y, M, K, N, cols, gs, va, s);
+    VQV_W4_CONFIGS(VQV_W4_LAUNCH)
+#undef VQV_W4_LAUNCH
   }
-  if constexpr (ACT != ACT_FP32) if (M <= 8 && use_m8q(M, K, ACT, gs)) {
-    const VerifyArgs none{};
-    return launch_qgemm_m8q(x, wq, scales, biases, y, M, K, N, ACT, gs, none, s);
-  }
-  if constexpr (ACT != ACT_FP32) if (M <= 8 && m8_fits(K, gs)) {
-    const VerifyArgs none{};
-    return launch_m8_any<ACT>(x, wq, scales, biases, y, M, K, N, gs, none, s);
-  }
-  if (M > 8 && qgemm_m16_fits(M, K, ACT, gs))
-    return launch_qgemm_m16(x, wq, scales, biases, y, M, K, N, ACT, gs, s);
+  return hipErrorInvalidValue;
+}
+
+// M <= 8 (one row set) takes, in order: the whole-line kernel, the half-line
+// kernel, then qgemm_w4 (narrow N split into exactly one work-group per CU,
+// columns rounded up to 4; the W4A32 draft's narrow outputs one 16-column
+// tile per work-group with K split over 8 waves, measured fastest at
+// K = 5120, N = 1024: 11.1 us against 15.5 us for 64-column groups; wide N in
+// 64-column groups). 17..64 rows at vocabulary widths share one weight
+// stream (qgemm_w4_rows); vocabulary widths with K <= 2560 otherwise take
+// whole-tile waves (qgemm_w4_wide), 9..64 rows with K <= 2560 the 16-row
+// kernel; the rest qgemm_w4 with row sets of 8 and chunked staging (the
+// smaller fallback, 32 columns with one K range, keeps fp32 at large K
+// within LDS).
+template <int ACT>
+Plan plan_act(int M, int K, int N, int gs) {
+  constexpr bool h16 = ACT != ACT_FP32;
+  if (h16 && qgemm_rows_fits(M, K, N, ACT)) return {Path::Rows, 0, 0};
+  if (qgemm_wide_fits(M, K, N, ACT, gs)) return {Path::Wide, 0, 0};
+  if (h16 && M <= 8 && use_m8q(M, K, ACT, gs)) return {Path::M8Q, 0, qgemm_m8q_cols(N)};
+  if (h16 && M <= 8 && m8_fits(K, gs)) return {Path::M8, 0, m8_cols(N)};
+  if (M > 8 && qgemm_m16_fits(M, K, ACT, gs)) return {Path::M16, 0, 0};
   if (M <= 8) {
     const int cus = device_cus();
     const int share = ((N + cus - 1) / cus + 3) / 4 * 4;
-    if (share > 48 && share <= 80 &&
-        lds_bytes_for<ACT, 1, 1, 5, 2, 8, 1, true>(K, gs) <= kLdsLimit)
-      return launch_w4<ACT, 1, 1, 5, 2, 8, 1, true>(x, wq, scales, biases, y, M, K, N, share, gs, s);
-    // Narrow outputs (fewer 64-column groups than CUs, e.g. the W4A32 draft
-    // projection): one 16-column tile per work-group, K split over 8 waves,
-    // no weight prefetch beyond the current step (measured fastest at
-    // K = 5120, N = 1024: 11.1 us against 15.5 us for 64-column groups).
-    if ((N + 63) / 64 < cus && lds_bytes_for<ACT, 1, 1, 1, 8, 1, 1, false>(K, gs) <= kLdsLimit)
-      return launch_w4<ACT, 1, 1, 1, 8, 1, 1, false>(x, wq, scales, biases, y, M, K, N, 16, gs, s);
-    if (lds_bytes_for<ACT, 1, 1, 4, 2, 8, 1, true>(K, gs) <= kLdsLimit)
-      return launch_w4<ACT, 1, 1, 4, 2, 8, 1, true>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
-    return launch_w4<ACT, 1, 1, 4, 2, 4, 2, false>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
+    if (share > 48 && share <= 80 && w4_fits<ACT>(0, K, gs)) return {Path::W4, 0, share};
+    if ((N + 63) / 64 < cus && w4_fits<ACT>(1, K, gs)) return {Path::W4, 1, 16};
+    if (w4_fits<ACT>(2, K, gs)) return {Path::W4, 2, 64};
+    if (w4_fits<ACT>(3, K, gs)) return {Path::W4, 3, 64};
+    return {Path::None, 0, 0};
   }
-  // Several row sets: chunked staging; the smaller fallback (32 columns,
-  // one K range, one-step chunks) keeps fp32 at large K within LDS.
-  if (M <= 16) {
-    if (lds_bytes_for<ACT, 2, 1, 4, 2, 4, 2, false>(K, gs) <= kLdsLimit)
-      return launch_w4<ACT, 2, 1, 4, 2, 4, 2, false>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
-    return launch_w4<ACT, 2, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, gs, s);
+  const int cfg = M <= 16 ? 4 : M <= 32 ? 6 : 8;
+  if (w4_fits<ACT>(cfg, K, gs)) return {Path::W4, cfg, 64};
+  if (w4_fits<ACT>(cfg + 1, K, gs)) return {Path::W4, cfg + 1, 32};
+  return {Path::None, 0, 0};
+}
+
+Plan plan_for(int M, int K, int N, int act, int gs) {
+  switch (act) {
+    case ACT_BF16: return plan_act<ACT_BF16>(M, K, N, gs);
+    case ACT_FP16: return plan_act<ACT_FP16>(M, K, N, gs);
+    case ACT_FP32: return plan_act<ACT_FP32>(M, K, N, gs);
+    default: return {Path::None, 0, 0};
   }
-  if (M <= 32) {
-    if (lds_bytes_for<ACT, 4, 1, 4, 1, 4, 1, false>(K, gs) <= kLdsLimit)
-      return launch_w4<ACT, 4, 1, 4, 1, 4, 1, false>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
-    return launch_w4<ACT, 4, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, gs, s);
+}
+
+template <int ACT>
+hipError_t launch_plan(const Plan& p, const void* x, const uint8_t* wq, const uint16_t* scales,
+                       const uint16_t* biases, float* y, int M, int K, int N, int gs,
+                       const VerifyArgs& va, hipStream_t s) {
+  switch (p.path) {
+    case Path::Rows: return launch_qgemm_rows(x, wq, scales, biases, y, M, K, N, ACT, gs, va, s);
+    case Path::Wide: return launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, ACT, gs, va, s);
+    case Path::M8Q: return launch_qgemm_m8q(x, wq, scales, biases, y, M, K, N, ACT, gs, va, s);
+    case Path::M8:
+      if constexpr (ACT != ACT_FP32)
+        return launch_m8_any<ACT>(x, wq, scales, biases, y, M, K, N, gs, va, s);
+      break;
+    case Path::M16: return launch_qgemm_m16(x, wq, scales, biases, y, M, K, N, ACT, gs, va, s);
+    case Path::W4:
+      return launch_w4_cfg<ACT>(p.cfg, x, wq, scales, biases, y, M, K, N, p.cols, gs, va, s);
+    case Path::None: break;
   }
-  if (lds_bytes_for<ACT, 8, 1, 4, 1, 2, 1, false>(K, gs) <= kLdsLimit)
-    return launch_w4<ACT, 8, 1, 4, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 64, gs, s);
-  return launch_w4<ACT, 8, 1, 2, 1, 2, 1, false>(x, wq, scales, biases, y, M, K, N, 32, gs, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+bool qgemm_supported(int M, int K, int N, int act, int gs) {
+  return plan_for(M, K, N, act, gs).path != Path::None;
+}
+
 hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
                         const uint16_t* biases, float* y, int M, int K, int N, int act, int gs,
-                        hipStream_t stream) {
+                        const VerifyArgs& va, hipStream_t stream) {
+  const Plan p = plan_for(M, K, N, act, gs);
   switch (act) {
-    case ACT_BF16: return dispatch_rows<ACT_BF16>(x, wq, scales, biases, y, M, K, N, gs, stream);
-    case ACT_FP16: return dispatch_rows<ACT_FP16>(x, wq, scales, biases, y, M, K, N, gs, stream);
-    case ACT_FP32: return dispatch_rows<ACT_FP32>(x, wq, scales, biases, y, M, K, N, gs, stream);
+    case ACT_BF16:
+      return launch_plan<ACT_BF16>(p, x, wq, scales, biases, y, M, K, N, gs, va, stream);
+    case ACT_FP16:
+      return launch_plan<ACT_FP16>(p, x, wq, scales, biases, y, M, K, N, gs, va, stream);
+    case ACT_FP32:
+      return launch_plan<ACT_FP32>(p, x, wq, scales, biases, y, M, K, N, gs, va, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 int qgemm_verify_groups(int M, int K, int N, int act, int gs) {
-  // The projection kernel of the fused path writes one partial per
-  // work-group and row; verify_finish (verify.hip) reduces them. Vocabulary widths
-  // take the persistent whole-tile kernel (one partial per CU and row
-  // instead of one per 80 columns).
-  if (M > 8 || act == ACT_FP32) return 0;
-  if (qgemm_wide_fits(M, K, N, act, gs)) return qgemm_wide_groups(M);
-  if (use_m8q(M, K, act, gs)) {
-    const int cols = qgemm_m8q_cols(N);
-    return (N + cols - 1) / cols;
+  // Partials per row: one per work-group that covers the row. The
+  // persistent kernels (qgemm_w4_wide, qgemm_w4_m16) give each row set
+  // `workers` work-groups of its own.
+  const Plan p = plan_for(M, K, N, act, gs);
+  switch (p.path) {
+    case Path::Rows: return qgemm_rows_groups(N);
+    case Path::Wide: return qgemm_wide_workers(M);
+    case Path::M16: return qgemm_m16_workers(M, N);
+    case Path::M8Q:
+    case Path::M8:
+    case Path::W4: return (N + p.cols - 1) / p.cols;
+    case Path::None: break;
   }
-  if (!m8_fits(K, gs)) return 0;
-  const int cols = m8_cols(N);
-  return (N + cols - 1) / cols;
+  return 0;
 }
 
 hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* scales,
                                const uint16_t* biases, float* y, int M, int K, int N, int act,
                                int gs, const VerifyArgs& va, hipStream_t stream) {
-  hipError_t e = hipErrorInvalidValue;
-  if (qgemm_wide_fits(M, K, N, act, gs))
-    e = launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, act, gs, va, stream);
-  else if (use_m8q(M, K, act, gs))
-    e = launch_qgemm_m8q(x, wq, scales, biases, y, M, K, N, act, gs, va, stream);
-  else if (act == ACT_BF16)
-    e = launch_m8_any<ACT_BF16>(x, wq, scales, biases, y, M, K, N, gs, va, stream);
-  else if (act == ACT_FP16)
-    e = launch_m8_any<ACT_FP16>(x, wq, scales, biases, y, M, K, N, gs, va, stream);
+  VerifyArgs v = va;
+  v.pgroups = qgemm_verify_groups(M, K, N, act, gs);
+  if (v.pgroups <= 0) return hipErrorInvalidValue;
+  const hipError_t e = launch_qgemm(x, wq, scales, biases, y, M, K, N, act, gs, v, stream);
   if (e != hipSuccess) return e;
-  return launch_verify_finish(va.partials, qgemm_verify_groups(M, K, N, act, gs), va, stream);
+  return launch_verify_finish(v, stream);
 }
 
 Variant forced_variant() {

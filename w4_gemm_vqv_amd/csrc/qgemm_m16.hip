@@ -134,7 +134,8 @@ template <int ACT, int NW, int TW, int DB, int RB, int D0, int XB, bool SWIGLU, 
 __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
-    float* __restrict__ y, int M, int K, int N, int cols, int rsets, int workers) {
+    float* __restrict__ y, int M, int K, int N, int cols, int rsets, int workers,
+    VerifyArgs va) {
   using TR = ActTraits<ACT>;
   // GS: group 64 << GS for GS >= 0; GS = -1 is group 32 (pair_step_halves:
   // four partial sums per group pair, each with its own scale, bias and
@@ -161,10 +162,16 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
     rs = local % rsets;
     wk = (local / rsets) * 8 + xcd;
   }
-  if (wk >= workers || wk >= ngroups) return;        // the whole group leaves
+  const bool fused = !SWIGLU && va.argmax != nullptr;  // uniform
+  const int rows = min(16, M - 16 * rs);            // rows of this row set
+  if (wk >= workers || wk >= ngroups) {              // the whole group leaves
+    if (fused && (int)threadIdx.x < rows)            // with empty partials
+      va.partials[(size_t)(16 * rs + threadIdx.x) * va.pgroups + wk] = top2_pack(top2_none());
+    return;
+  }
   x = static_cast<const uint16_t*>(x) + (size_t)rs * 16 * K;
-  y += (size_t)rs * 16 * (SWIGLU ? N / 2 : N);
-  M = min(16, M - 16 * rs);
+  if (y) y += (size_t)rs * 16 * (SWIGLU ? N / 2 : N);
+  M = rows;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
@@ -271,6 +278,9 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
     }
   }
 
+  // With the fused verify each thread keeps the top two of its outputs, all
+  // of row (tid >> 4) & 15 (the reduction's output order, NT a multiple of 256).
+  Top2 best = top2_none();
   for (int cg = wk; cg < ngroups; cg += workers) {
     const int wg0 = cg * cols;                        // first logical column
     const int wgcols = min(cols, N - wg0);
@@ -554,10 +564,37 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
         const int t = idx >> 8;
         const int m = (idx >> 4) & 15;
         const int c = t * 16 + (idx & 15);
-        if (m < M && c < wgcols) y[(size_t)m * N + wg0 + c] = tile_sum(t, idx & 255);
+        if (m < M && c < wgcols) {
+          const float v = tile_sum(t, idx & 255);
+          if (!fused || y) y[(size_t)m * N + wg0 + c] = v;
+          if (fused) top2_add(best, v, wg0 + c);
+        }
       }
     }
     __syncthreads();                                  // the table, runs and partials are reused
+  }
+  if (!fused) return;
+
+  // ---- fused greedy verify, first half: the 16 lanes of a row in a wave
+  // reduce, then lane m of wave 0 merges row m's two holders (waves m/4 and
+  // m/4 + 4, quarter m % 4) and writes the row set's partial for this worker.
+  static_assert(NW == 8, "two waves per row in the epilogue");
+  top2_best16(best);
+  unsigned* cand = reinterpret_cast<unsigned*>(lds);  // [NW][4] x (k1, i1, k2)
+  if (j == 0) {
+    unsigned* p = cand + (wave * 4 + h) * 3;
+    p[0] = best.k1;
+    p[1] = (unsigned)best.i1;
+    p[2] = best.k2;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < M) {
+    Top2 r = top2_none();
+    for (int w = lane >> 2; w < NW; w += 4) {
+      const unsigned* p = cand + (w * 4 + (lane & 3)) * 3;
+      top2_merge(r, p[0], (int)p[1], p[2]);
+    }
+    va.partials[(size_t)(16 * rs + lane) * va.pgroups + wk] = top2_pack(r);
   }
 }
 
@@ -571,10 +608,10 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
 // private (s, b) table in LDS rebuilt per tile from loads issued a tile
 // ahead, and each finished tile stored straight to y. No barrier, partial
 // sum or reduction follows the staging. Row sets and the XCD layout are as
-// in qgemm_w4_m16. With va.argmax set (one row set, M <= 8) each lane also
-// keeps the top two of its rows over all its columns, and the work-group
-// writes one top-two partial per row for verify_finish (the greedy verify's
-// first half, as in qgemm_w4_m8's fused epilogue).
+// in qgemm_w4_m16. With va.argmax set each lane also keeps the top two of
+// its rows over all its columns, and the work-group writes one top-two
+// partial per row of its row set (the greedy verify's first half, as in
+// qgemm_w4_m8's fused epilogue).
 template <int ACT, int DB, int RB, int GS>
 __global__ __launch_bounds__(512) void qgemm_w4_wide(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
@@ -603,14 +640,15 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
     wk = (local / rsets) * 8 + xcd;
   }
   const int tbeg = wk * tpw, tend = min(T, tbeg + tpw);
+  const int rows = min(16, M - 16 * rs);            // rows of this row set
   if (wk >= workers || tbeg >= T) {                  // the whole group leaves
-    if (fused && threadIdx.x < 8)                     // with an empty partial
-      va.partials[(size_t)blockIdx.x * 8 + threadIdx.x] = top2_pack(top2_none());
+    if (fused && (int)threadIdx.x < rows)            // with empty partials
+      va.partials[(size_t)(16 * rs + threadIdx.x) * va.pgroups + wk] = top2_pack(top2_none());
     return;
   }
   x = static_cast<const uint16_t*>(x) + (size_t)rs * 16 * K;
-  y += (size_t)rs * 16 * N;
-  M = min(16, M - 16 * rs);
+  if (y) y += (size_t)rs * 16 * N;
+  M = rows;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int tid = threadIdx.x;
@@ -793,9 +831,10 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
     }
   };
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  Top2 best[4] = {top2_none(), top2_none(), top2_none(), top2_none()};
+  Top2Scan best[4] = {top2_scan_none(), top2_scan_none(), top2_scan_none(), top2_scan_none()};
   // A finished tile goes straight to y: lane (j, h) holds rows 4h .. 4h+3 of
-  // column j.
+  // column j (a lane's tiles come in increasing column order, as top2_scan
+  // needs).
   auto store_tile = [&](int k) {
     const int c = col0(k) + j;
 #pragma unroll
@@ -803,7 +842,7 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
       const int m = 4 * h + e;
       if (m < M && c < N) {
         if (!fused || y) y[(size_t)m * N + c] = acc[e];
-        if (fused) top2_add(best[e], acc[e], c);
+        if (fused) top2_scan(best[e], acc[e], c, acc[e] == acc[e]);
       }
       acc[e] = 0.0f;
     }
@@ -899,28 +938,29 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
 
   if (fused) {
     // The 16 lanes of a (row, h) group reduce; the waves' results combine in
-    // wave order in LDS (the activation image is no longer read once every
-    // wave is past its loop); lane m of wave 0 writes row m's partial.
+    // LDS (the activation image is no longer read once every wave is past
+    // its loop); lane m of wave 0 writes the partial of the row set's row m.
     __syncthreads();
-    unsigned* cand = reinterpret_cast<unsigned*>(lds);  // [NW][8 rows] x (k1, i1, k2)
+    unsigned* cand = reinterpret_cast<unsigned*>(lds);  // [NW][16 rows] x (k1, i1, k2)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      top2_best16(best[e]);
-      if (j == 0 && h < 2) {
-        unsigned* q = cand + (wave * 8 + 4 * h + e) * 3;
-        q[0] = best[e].k1;
-        q[1] = (unsigned)best[e].i1;
-        q[2] = best[e].k2;
+      Top2 t = top2_of_scan(best[e]);
+      top2_best16(t);
+      if (j == 0) {
+        unsigned* q = cand + (wave * 16 + 4 * h + e) * 3;
+        q[0] = t.k1;
+        q[1] = (unsigned)t.i1;
+        q[2] = t.k2;
       }
     }
     __syncthreads();
-    if (wave == 0 && lane < 8) {
+    if (wave == 0 && lane < M) {
       Top2 r = top2_none();
       for (int w = 0; w < NW; ++w) {
-        const unsigned* q = cand + (w * 8 + lane) * 3;
+        const unsigned* q = cand + (w * 16 + lane) * 3;
         top2_merge(r, q[0], (int)q[1], q[2]);
       }
-      va.partials[(size_t)blockIdx.x * 8 + lane] = top2_pack(r);
+      va.partials[(size_t)(16 * rs + lane) * va.pgroups + wk] = top2_pack(r);
     }
   }
 }
@@ -941,18 +981,34 @@ constexpr int kM16Waves = 8;
 constexpr int kM16Tiles = 5;
 constexpr int kM16XB = 5;
 
-template <int ACT, int DB, int RB, bool SWIGLU>
-hipError_t launch_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
-                      const uint16_t* biases, float* y, int M, int K, int N, int cols,
-                      int gs, hipStream_t stream) {
-  // One work-group per CU: rsets row sets of `workers` workers each (a
-  // multiple of 8 when there are several row sets, for the XCD layout).
+// Columns per column group of qgemm_w4_m16: an equal share of the CUs,
+// rounded up to 4, at most kM16Tiles tiles.
+int m16_cols(int N) {
+  const int cus = device_cus();
+  const int share = ((N + cus - 1) / cus + 3) / 4 * 4;
+  return share < 16 * kM16Tiles ? share : 16 * kM16Tiles;
+}
+
+// Workers per row set of qgemm_w4_m16: one work-group per CU, rsets row
+// sets of `workers` each (a multiple of 8 when there are several row sets,
+// for the XCD layout); one row set takes no more workers than groups.
+int m16_workers(int M, int N) {
   const int rsets = (M + 15) / 16;
+  const int cols = m16_cols(N);
   const int groups = (N + cols - 1) / cols;
   const int cus = device_cus();
   int workers = rsets > 1 ? (cus / rsets) / 8 * 8 : cus;
   if (workers < 8) workers = 8;
   if (rsets == 1 && workers > groups) workers = groups;
+  return workers;
+}
+
+template <int ACT, int DB, int RB, bool SWIGLU>
+hipError_t launch_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
+                      const uint16_t* biases, float* y, int M, int K, int N, int cols,
+                      int gs, const VerifyArgs& va, hipStream_t stream) {
+  const int rsets = (M + 15) / 16;
+  const int workers = m16_workers(M, N);
   const M16Layout L = m16_layout(K >> 6, 16 * kM16Tiles, kM16Waves, kM16XB, gs < 0);
   if (L.total > kLdsLimit) return hipErrorInvalidValue;  // never launched
   constexpr int D0 = DB;                                // one block ahead of the staging
@@ -976,22 +1032,23 @@ hipError_t launch_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
   }
   const dim3 grid(workers * rsets);
   hipLaunchKernelGGL(kern, grid, dim3(64 * kM16Waves), L.total, stream, x, wq, scales, biases,
-                     y, M, K, N, cols, rsets, workers);
+                     y, M, K, N, cols, rsets, workers, va);
   return hipGetLastError();
 }
 
 template <int ACT, bool SWIGLU>
 hipError_t launch_m16_blocks(const void* x, const uint8_t* wq, const uint16_t* scales,
                              const uint16_t* biases, float* y, int M, int K, int N,
-                             int gs, hipStream_t s) {
-  const int cus = device_cus();
-  const int share = ((N + cus - 1) / cus + 3) / 4 * 4;
-  const int cols = share < 16 * kM16Tiles ? share : 16 * kM16Tiles;
+                             int gs, const VerifyArgs& va, hipStream_t s) {
+  const int cols = m16_cols(N);
   const int GP = ((K >> 6) + 1) >> 1;
-  if (GP % 5 == 0) return launch_m16<ACT, 5, 1, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, gs, s);
-  if (GP % 4 == 0) return launch_m16<ACT, 4, 2, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, gs, s);
-  if (GP % 2 == 0) return launch_m16<ACT, 2, 4, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, gs, s);
-  return launch_m16<ACT, 1, 8, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, gs, s);
+  if (GP % 5 == 0)
+    return launch_m16<ACT, 5, 1, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, gs, va, s);
+  if (GP % 4 == 0)
+    return launch_m16<ACT, 4, 2, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, gs, va, s);
+  if (GP % 2 == 0)
+    return launch_m16<ACT, 2, 4, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, gs, va, s);
+  return launch_m16<ACT, 1, 8, SWIGLU>(x, wq, scales, biases, y, M, K, N, cols, gs, va, s);
 }
 
 template <int ACT, int DB, int RB>
@@ -1038,12 +1095,14 @@ hipError_t launch_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
 //   chunk boundaries, so the next chunk's first weights are in flight during
 //   its staging. Steps past a wave's tiles or past K read zeros.
 // * The work-group's tiles: [tbeg, tbeg + tpw); wave w takes tbeg + w + 8k.
-// Every sum runs in a fixed order, so results are deterministic.
+// Every sum runs in a fixed order, so results are deterministic. With
+// va.argmax set the work-group also writes one top-two partial per row over
+// its columns (the greedy verify's first half, as in qgemm_w4_wide).
 template <int ACT, int RS, int KT, int KCP, int GS>
 __global__ __launch_bounds__(512) void qgemm_w4_rows(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
-    float* __restrict__ y, int M, int K, int N, int tpw) {
+    float* __restrict__ y, int M, int K, int N, int tpw, VerifyArgs va) {
   using TR = ActTraits<ACT>;
   // GS: group 64 << GS for GS >= 0; GS = -1 is group 32 (as in
   // qgemm_w4_m16: four partial sums per pair and row set, one per group
@@ -1286,18 +1345,116 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
     }
   }
 
-  // ---- results: lane (j, h) holds rows 4h .. 4h+3 of column j of each row set.
-#pragma unroll
-  for (int k = 0; k < KT; ++k) {
-    const int col = tile[k] * 16 + j;
-    if (!tin[k] || col >= N) continue;
+  const bool fused = va.argmax != nullptr;           // uniform
+  if (fused) {
+    // ---- fused greedy verify, first half. Each lane takes the top two of its
+    // tiles in each of its rows into LDS, [wave][lane column j][row]; lane m of
+    // each wave then merges row m's 16 columns, and lane m of wave 0 the 8
+    // waves. The lanes scan in fp32 (top2_scan); a wave with a NaN among its
+    // outputs scans again with order keys. Rows m >= M are scanned too (their
+    // accumulators hold finite sums of zero activations) and never read.
+    constexpr int R16 = 16 * RS;
+    constexpr int JS = 3 * R16 + 1;                    // dwords per (wave, j) line
+    static_assert(NW * 16 * JS * 4 + NW * R16 * 12 <=
+                      KCP * RS * (kPair16 + 4 * XSF) + NW * KT * 16 * NQ * KCP * 4,
+                  "the candidates fit in the kernel's LDS");
+    __syncthreads();                                   // every wave is past its last LDS read
+    unsigned* cand = reinterpret_cast<unsigned*>(lds);
+    unsigned* cand2 = cand + NW * 16 * JS;             // [NW][R16] x (k1, i1, k2)
+    unsigned* line = cand + (wave * 16 + j) * JS;
+    auto put = [&](int m, const Top2& t) {
+      line[3 * m] = t.k1;
+      line[3 * m + 1] = (unsigned)t.i1;
+      line[3 * m + 2] = t.k2;
+    };
+    // Tile-major, so that each tile's range test is made once (uniform).
+    float chk[4] = {0.0f, 0.0f, 0.0f, 0.0f};           // NaN if some output is NaN (or inf - inf)
+    Top2Scan sc[RS][4];
 #pragma unroll
     for (int r = 0; r < RS; ++r)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = 16 * r + 4 * h + e;
-        if (m < M) y[(size_t)m * N + col] = acc[k][r][e];
+      for (int e = 0; e < 4; ++e) sc[r][e] = top2_scan_none();
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      const int col = tile[k] * 16 + j;
+      if (tin[k] && tile[k] * 16 + 16 <= N) {         // uniform: a whole tile
+#pragma unroll
+        for (int r = 0; r < RS; ++r)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            chk[e] += acc[k][r][e];
+            top2_scan(sc[r][e], acc[k][r][e], col);
+          }
+      } else if (tin[k] && col < N) {                 // the last, partial tile
+#pragma unroll
+        for (int r = 0; r < RS; ++r)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            chk[e] += acc[k][r][e];
+            top2_scan(sc[r][e], acc[k][r][e], col);
+          }
       }
+    }
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) put(16 * r + 4 * h + e, top2_of_scan(sc[r][e]));
+    const float chk_all = (chk[0] + chk[1]) + (chk[2] + chk[3]);
+    if (__ballot(chk_all != chk_all) != 0) {           // uniform
+#pragma unroll
+      for (int r = 0; r < RS; ++r)
+#pragma unroll 1
+        for (int e = 0; e < 4; ++e) {
+          Top2 t = top2_none();
+#pragma unroll
+          for (int k = 0; k < KT; ++k) {
+            const int col = tile[k] * 16 + j;
+            if (tin[k] && col < N) top2_add(t, acc[k][r][e], col);
+          }
+          put(16 * r + 4 * h + e, t);
+        }
+    }
+    __syncthreads();
+    if (lane < R16) {
+      const unsigned* q = cand + wave * 16 * JS + 3 * lane;
+      unsigned k1 = q[0], k2 = q[2];
+      int i1 = (int)q[1];
+#pragma unroll
+      for (int jj = 1; jj < 16; ++jj)
+        top2_merge_ranked(k1, i1, k2, q[jj * JS], (int)q[jj * JS + 1], q[jj * JS + 2]);
+      unsigned* o = cand2 + (wave * R16 + lane) * 3;
+      o[0] = k1;
+      o[1] = (unsigned)i1;
+      o[2] = k2;
+    }
+    __syncthreads();
+    if (wave == 0 && lane < M) {
+      const unsigned* q = cand2 + lane * 3;
+      unsigned k1 = q[0], k2 = q[2];
+      int i1 = (int)q[1];
+#pragma unroll
+      for (int w = 1; w < NW; ++w)
+        top2_merge_ranked(k1, i1, k2, q[w * R16 * 3], (int)q[w * R16 * 3 + 1], q[w * R16 * 3 + 2]);
+      va.partials[(size_t)lane * va.pgroups + blockIdx.x] = make_uint4(k1, (unsigned)i1, k2, 0u);
+    }
+  }
+
+  // ---- results: lane (j, h) holds rows 4h .. 4h+3 of column j of each row set.
+  // With the fused verify the logits are stored last, after its barriers,
+  // which would otherwise wait for every store to complete.
+  if (!fused || y) {
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      const int col = tile[k] * 16 + j;
+      if (!tin[k] || col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < RS; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 16 * r + 4 * h + e;
+          if (m < M) y[(size_t)m * N + col] = acc[k][r][e];
+        }
+    }
   }
 }
 
@@ -1309,10 +1466,17 @@ constexpr int rows_lds_bytes() {
 constexpr int kRowsKT = 5;
 constexpr int kRowsKCP = 5;
 
+// Column tiles per work-group of qgemm_w4_rows: an equal share of the CUs.
+int rows_tiles_per_group(int N) {
+  const int cus = device_cus();
+  const int T = (N + 15) / 16;
+  return (T + cus - 1) / cus;
+}
+
 template <int ACT, int RS>
 hipError_t launch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                        const uint16_t* biases, float* y, int M, int K, int N, int gs,
-                       hipStream_t stream) {
+                       const VerifyArgs& va, hipStream_t stream) {
   const int lds_bytes = gs < 0 ? rows_lds_bytes<RS, kRowsKT, kRowsKCP, true>()
                               : rows_lds_bytes<RS, kRowsKT, kRowsKCP, false>();
   static_assert(rows_lds_bytes<4, kRowsKT, kRowsKCP, true>() <= kLdsLimit, "LDS budget");
@@ -1321,12 +1485,10 @@ hipError_t launch_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
   if (gs < 0) kern = qgemm_w4_rows<ACT, RS, kRowsKT, kRowsKCP, -1>;
   const hipError_t e = allow_lds(reinterpret_cast<const void*>(kern));
   if (e != hipSuccess) return e;
-  const int cus = device_cus();
   const int T = (N + 15) / 16;
-  const int tpw = (T + cus - 1) / cus;
-  const int groups = (T + tpw - 1) / tpw;
-  hipLaunchKernelGGL(kern, dim3(groups), dim3(512), lds_bytes, stream, x, wq, scales, biases, y,
-                     M, K, N, tpw);
+  const int tpw = rows_tiles_per_group(N);
+  hipLaunchKernelGGL(kern, dim3((T + tpw - 1) / tpw), dim3(512), lds_bytes, stream, x, wq,
+                     scales, biases, y, M, K, N, tpw, va);
   return hipGetLastError();
 }
 
@@ -1365,25 +1527,29 @@ bool qgemm_rows_fits(int M, int K, int N, int act) {
   // and at most kRowsKT tiles per wave with every wave busy.
   if (M <= 16 || M > 64 || act == ACT_FP32 || K % 128 != 0) return false;
   if ((size_t)N * (size_t)(K / 2) >= 0x7F000000u) return false;
-  const int cus = device_cus();
-  const long long T = (N + 15) / 16;
-  const long long tpw = (T + cus - 1) / cus;
+  const int tpw = rows_tiles_per_group(N);
   return tpw >= 8 && tpw <= 8 * kRowsKT;
+}
+
+int qgemm_rows_groups(int N) {
+  const int T = (N + 15) / 16;
+  const int tpw = rows_tiles_per_group(N);
+  return (T + tpw - 1) / tpw;
 }
 
 hipError_t launch_qgemm_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                              const uint16_t* biases, float* y, int M, int K, int N, int act,
-                             int gs, hipStream_t stream) {
+                             int gs, const VerifyArgs& va, hipStream_t s) {
   const int rs = (M + 15) / 16;
   if (act == ACT_BF16) {
-    if (rs == 2) return launch_rows<ACT_BF16, 2>(x, wq, scales, biases, y, M, K, N, gs, stream);
-    if (rs == 3) return launch_rows<ACT_BF16, 3>(x, wq, scales, biases, y, M, K, N, gs, stream);
-    return launch_rows<ACT_BF16, 4>(x, wq, scales, biases, y, M, K, N, gs, stream);
+    if (rs == 2) return launch_rows<ACT_BF16, 2>(x, wq, scales, biases, y, M, K, N, gs, va, s);
+    if (rs == 3) return launch_rows<ACT_BF16, 3>(x, wq, scales, biases, y, M, K, N, gs, va, s);
+    return launch_rows<ACT_BF16, 4>(x, wq, scales, biases, y, M, K, N, gs, va, s);
   }
   if (act == ACT_FP16) {
-    if (rs == 2) return launch_rows<ACT_FP16, 2>(x, wq, scales, biases, y, M, K, N, gs, stream);
-    if (rs == 3) return launch_rows<ACT_FP16, 3>(x, wq, scales, biases, y, M, K, N, gs, stream);
-    return launch_rows<ACT_FP16, 4>(x, wq, scales, biases, y, M, K, N, gs, stream);
+    if (rs == 2) return launch_rows<ACT_FP16, 2>(x, wq, scales, biases, y, M, K, N, gs, va, s);
+    if (rs == 3) return launch_rows<ACT_FP16, 3>(x, wq, scales, biases, y, M, K, N, gs, va, s);
+    return launch_rows<ACT_FP16, 4>(x, wq, scales, biases, y, M, K, N, gs, va, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1400,7 +1566,7 @@ bool qgemm_wide_fits(int M, int K, int N, int act, int gs) {
          m16_layout(G, 16, 8, 5, gs < 0).sb + 8 * 16 * (gs < 0 ? 2 * G : G) * 4 <= kLdsLimit;
 }
 
-int qgemm_wide_groups(int M) { return wide_workers((M + 15) / 16) * ((M + 15) / 16); }
+int qgemm_wide_workers(int M) { return wide_workers((M + 15) / 16); }
 
 hipError_t launch_qgemm_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
                              const uint16_t* biases, float* y, int M, int K, int N, int act,
@@ -1425,25 +1591,28 @@ bool qgemm_swiglu_fused(int M, int K, int N, int act, int gs) {
   return qgemm_m16_fits(M, K, act, gs) && (size_t)N * (size_t)(K / 2) < 0x7F000000u;
 }
 
+int qgemm_m16_workers(int M, int N) { return m16_workers(M, N); }
+
 hipError_t launch_qgemm_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
                             const uint16_t* biases, float* y, int M, int K, int N, int act,
-                            int gs, hipStream_t stream) {
+                            int gs, const VerifyArgs& va, hipStream_t stream) {
   if (act == ACT_BF16)
-    return launch_m16_blocks<ACT_BF16, false>(x, wq, scales, biases, y, M, K, N, gs, stream);
+    return launch_m16_blocks<ACT_BF16, false>(x, wq, scales, biases, y, M, K, N, gs, va, stream);
   if (act == ACT_FP16)
-    return launch_m16_blocks<ACT_FP16, false>(x, wq, scales, biases, y, M, K, N, gs, stream);
+    return launch_m16_blocks<ACT_FP16, false>(x, wq, scales, biases, y, M, K, N, gs, va, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_qgemm_swiglu(const void* x, const uint8_t* wq, const uint16_t* scales,
                                const uint16_t* biases, float* h, int M, int K, int N, int act,
                                int gs, float* scratch_y, hipStream_t stream) {
+  const VerifyArgs none{};
   if (qgemm_swiglu_fused(M, K, N, act, gs)) {
     if (act == ACT_BF16)
-      return launch_m16_blocks<ACT_BF16, true>(x, wq, scales, biases, h, M, K, N, gs, stream);
-    return launch_m16_blocks<ACT_FP16, true>(x, wq, scales, biases, h, M, K, N, gs, stream);
+      return launch_m16_blocks<ACT_BF16, true>(x, wq, scales, biases, h, M, K, N, gs, none, stream);
+    return launch_m16_blocks<ACT_FP16, true>(x, wq, scales, biases, h, M, K, N, gs, none, stream);
   }
-  hipError_t e = launch_qgemm(x, wq, scales, biases, scratch_y, M, K, N, act, gs, stream);
+  hipError_t e = launch_qgemm(x, wq, scales, biases, scratch_y, M, K, N, act, gs, none, stream);
   if (e != hipSuccess) return e;
   const long long total = (long long)M * (N / 2);
   const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);

@@ -467,7 +467,7 @@ __global__ __launch_bounds__(512) void qgemm_w4_m8q(
       const unsigned* p = cand + (w * 4 + (lane & 3)) * 3;
       top2_merge(r, p[0], (int)p[1], p[2]);
     }
-    va.partials[(size_t)blockIdx.x * 8 + lane] = top2_pack(r);
+    va.partials[(size_t)lane * va.pgroups + blockIdx.x] = top2_pack(r);
   }
 }
 

@@ -11,12 +11,14 @@
 // scans with 16-byte loads and reduces top-two partials (argmax.h: best key,
 // its lowest index, best other key) across lanes by DPP and across the four
 // waves in LDS.
-// Stage 2: one work-group per sequence. A wave reduces one row's chunk
-// partials at a time (lanes over chunks, all loads in flight), writes argmax
-// (and the top-1 minus top-2 margin when asked); then wave 0 compares each
-// row's argmax with its draft, and a ballot's count of trailing ones is the
-// accept length. A sequence with fewer valid drafts (draft_len) stops its
-// walk there.
+// Stage 2: one work-group per sequence. A wave reduces one row's partials at
+// a time (lanes over partials, all loads in flight), writes argmax (and the
+// top-1 minus top-2 margin when asked); then wave 0 compares each row's
+// argmax with its draft, and a ballot's count of trailing ones is the accept
+// length. A sequence with fewer valid drafts (draft_len) stops its walk
+// there. The fused projection (qgemm*.hip) writes its per-work-group
+// partials in the same [rows][partials per row] layout, and this kernel
+// finishes that path too.
 
 #include <limits.h>
 
@@ -83,10 +85,12 @@ __global__ __launch_bounds__(256) void verify_stage1(const float* __restrict__ l
   }
 }
 
-// One work-group per sequence: wave w reduces the chunk partials of rows w,
-// w+8, ... (lanes over chunks), then wave 0 walks the sequence.
-__global__ __launch_bounds__(512) void verify_stage2(const uint4* __restrict__ part, int nchunks,
-                                                     VerifyArgs va) {
+// One work-group per sequence: wave w reduces the partials of rows w, w+16,
+// ... (lanes over partials), then wave 0 walks the sequence.
+constexpr int kStage2Waves = 16;
+
+__global__ __launch_bounds__(64 * kStage2Waves) void verify_stage2(const uint4* __restrict__ part,
+                                                                   int nparts, VerifyArgs va) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int T = va.T;
@@ -96,9 +100,9 @@ __global__ __launch_bounds__(512) void verify_stage2(const uint4* __restrict__ p
     limit = draft_len_of_row(va.draft_len ? va.draft_len + b : nullptr, 1, T);
   }
   __shared__ int best[64];
-  for (int i = wave; i < T; i += 8) {
+  for (int i = wave; i < T; i += kStage2Waves) {
     const size_t row = (size_t)b * T + i;
-    const Top2 t = top2_reduce_strided(part + row * nchunks, nchunks, 1);
+    const Top2 t = top2_reduce_strided(part + row * nparts, nparts, 1);
     if (lane == 0) {
       va.argmax[row] = t.i1;
       if (va.margin) va.margin[row] = top2_margin(t);
@@ -113,39 +117,11 @@ __global__ __launch_bounds__(512) void verify_stage2(const uint4* __restrict__ p
   }
 }
 
-// The fused projection's second half: wave m reduces row m's per-group
-// partials, and wave 0 walks every sequence.
-__global__ __launch_bounds__(512) void verify_finish(const uint4* __restrict__ part, int groups,
-                                                     VerifyArgs va) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int B = va.B, T = va.T, rows = B * T;
-  int d = -1, limit = T - 1;  // limit: raw valid-draft count, clamped at the walk
-  if (wave == 0) {
-    d = draft_of_row(va.draft, B, T);
-    limit = draft_len_of_row(va.draft_len, B, T);
-  }
-  __shared__ int best[8];
-  if (wave < rows) {
-    const Top2 t = top2_reduce_strided(part + wave, groups, 8);
-    if (lane == 0) {
-      va.argmax[wave] = t.i1;
-      if (va.margin) va.margin[wave] = top2_margin(t);
-      best[wave] = t.i1;
-    }
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const int len =
-        accept_lengths_of(lane < rows ? best[lane] : -1, d, clamp_limit(limit, T), B, T);
-    if (lane < B) va.accept_len[lane] = len;
-  }
-}
-
 }  // namespace
 
-hipError_t launch_verify_finish(const uint4* partials, int groups, const VerifyArgs& va,
-                                hipStream_t stream) {
-  hipLaunchKernelGGL(verify_finish, dim3(1), dim3(512), 0, stream, partials, groups, va);
+hipError_t launch_verify_finish(const VerifyArgs& va, hipStream_t stream) {
+  hipLaunchKernelGGL(verify_stage2, dim3(va.B), dim3(64 * kStage2Waves), 0, stream, va.partials,
+                     va.pgroups, va);
   return hipGetLastError();
 }
 
@@ -160,7 +136,8 @@ hipError_t launch_verify(const float* logits, int N, const VerifyArgs& va, hipSt
                        va.partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_stage2, dim3(va.B), dim3(512), 0, stream, va.partials, nchunks, va);
+  hipLaunchKernelGGL(verify_stage2, dim3(va.B), dim3(64 * kStage2Waves), 0, stream, va.partials,
+                     nchunks, va);
   return hipGetLastError();
 }
 

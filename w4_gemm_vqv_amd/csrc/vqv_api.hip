@@ -82,15 +82,16 @@ vqv_status vqv_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
     return VQV_ERR_ARG;
   if (workspace_bytes < vqv_qgemm_workspace_bytes(M, K, N, group, act_dtype))
     return VQV_ERR_WORKSPACE;
+  if (!vqv::qgemm_supported(M, K, N, (int)act_dtype, gs)) return VQV_ERR_UNSUPPORTED;
   (void)hipGetLastError();  // start from a clean error state
+  const vqv::VerifyArgs plain{};
   const hipError_t e = vqv::launch_qgemm(x, wq, scales, biases, y, M, K, N, (int)act_dtype, gs,
-                                         static_cast<hipStream_t>(hip_stream));
+                                         plain, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? VQV_OK : VQV_ERR_HIP;
 }
 
-// Fused projection + verify: a 256-byte head (unused), then either the fused
-// kernel's per-group partials or, where the fused kernel does not apply,
-// room for the logits and the two-stage verify's partials.
+// Fused projection + verify: a 256-byte head (unused), then the projection's
+// per-row partials, [M][groups] 16-byte slots.
 constexpr size_t kHead = 256;
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -98,9 +99,9 @@ static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 size_t vqv_qgemm_verify_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype) {
   const int gs = group_shift(group);
   if (M < 1 || M > kMaxRows || N < 1 || K < kGroup || gs == kNoGroup) return 0;
+  if (act_dtype != VQV_BF16 && act_dtype != VQV_FP16 && act_dtype != VQV_FP32) return 0;
   const int groups = vqv::qgemm_verify_groups(M, K, N, (int)act_dtype, gs);
-  if (groups > 0) return kHead + (size_t)groups * 8 * 16;
-  return kHead + align256((size_t)M * N * 4) + (size_t)M * vqv::verify_chunks(N) * 16;
+  return groups > 0 ? kHead + (size_t)M * groups * 16 : 0;
 }
 
 vqv_status vqv_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* scales,
@@ -169,35 +170,19 @@ vqv_status check_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* 
   return VQV_OK;
 }
 
-// Scratch bytes the call needs: the fused kernel's partials, or the two-stage
-// verify's partials after room for the logits (logits_room bytes, used when y
-// is NULL).
-size_t qgemm_verify_scratch(int M, int K, int N, int gs, vqv_dtype act, size_t logits_room) {
-  const int groups = vqv::qgemm_verify_groups(M, K, N, (int)act, gs);
-  if (groups > 0) return kHead + (size_t)groups * 8 * 16;
-  return kHead + logits_room + (size_t)M * vqv::verify_chunks(N) * 16;
-}
-
-// The launch sequence of a checked call, with its scratch at ws (laid out as
-// qgemm_verify_scratch describes).
+// The launch sequence of a checked call whose scratch (the partials, at
+// ws + kHead) holds M * groups slots.
 vqv_status launch_qgemm_verify_at(const void* x, const uint8_t* wq, const uint16_t* scales,
                                   const uint16_t* biases, float* y, int M, int K, int N, int gs,
                                   vqv_dtype act_dtype, const int32_t* draft,
                                   const int32_t* draft_len, int B, int T, int32_t* argmax,
                                   int32_t* accept_len, float* margin, unsigned char* ws,
-                                  size_t logits_room, hipStream_t st) {
+                                  hipStream_t st) {
   (void)hipGetLastError();
-  vqv::VerifyArgs va{draft, draft_len, B, T, argmax, accept_len, margin,
-                     reinterpret_cast<uint4*>(ws + kHead)};
-  hipError_t e;
-  if (vqv::qgemm_verify_groups(M, K, N, (int)act_dtype, gs) > 0) {
-    e = vqv::launch_qgemm_verify(x, wq, scales, biases, y, M, K, N, (int)act_dtype, gs, va, st);
-  } else {
-    float* logits = y ? y : reinterpret_cast<float*>(ws + kHead);
-    va.partials = reinterpret_cast<uint4*>(ws + kHead + logits_room);
-    e = vqv::launch_qgemm(x, wq, scales, biases, logits, M, K, N, (int)act_dtype, gs, st);
-    if (e == hipSuccess) e = vqv::launch_verify(logits, N, va, st);
-  }
+  const vqv::VerifyArgs va{draft, draft_len, B, T, argmax, accept_len, margin,
+                           reinterpret_cast<uint4*>(ws + kHead), 0};
+  const hipError_t e =
+      vqv::launch_qgemm_verify(x, wq, scales, biases, y, M, K, N, (int)act_dtype, gs, va, st);
   return e == hipSuccess ? VQV_OK : VQV_ERR_HIP;
 }
 
@@ -247,6 +232,7 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
                                            draft, draft_len, B, T, argmax, accept_len, margin, &fs);
   if (st != VQV_OK) return st;
   const size_t need = vqv_qgemm_verify_workspace_bytes(M, K, N, group, act_dtype);
+  if (need == 0) return VQV_ERR_UNSUPPORTED;  // no kernel takes the problem
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return VQV_ERR_WORKSPACE;
   const void* ins[6] = {x, wq, scales, biases, draft, draft_len};
   const size_t insz[6] = {fs.xbytes, fs.wbytes, fs.sbytes, fs.sbytes,
@@ -260,7 +246,7 @@ vqv_status vqv_qgemm_verify_ex(const void* x, const uint8_t* wq, const uint16_t*
     if (overlaps(workspace, need, outs[o], outsz[o])) return VQV_ERR_ARG;
   return launch_qgemm_verify_at(x, wq, scales, biases, y, M, K, N, fs.gs, act_dtype, draft,
                                 draft_len, B, T, argmax, accept_len, margin,
-                                static_cast<unsigned char*>(workspace), align256(fs.ybytes),
+                                static_cast<unsigned char*>(workspace),
                                 static_cast<hipStream_t>(hip_stream));
 }
 
@@ -273,13 +259,13 @@ vqv_status vqv_qgemm_verify_ex_noalloc(const void* x, const uint8_t* wq, const u
   const vqv_status st = check_qgemm_verify(x, wq, scales, biases, y, M, K, N, group, act_dtype,
                                            draft, draft_len, B, T, argmax, accept_len, margin, &fs);
   if (st != VQV_OK) return st;
-  const size_t room = y ? 0 : align256(fs.ybytes);
-  if (qgemm_verify_scratch(M, K, N, fs.gs, act_dtype, room) > VQV_NOALLOC_SCRATCH_BYTES)
-    return VQV_ERR_WORKSPACE;
+  const size_t need = vqv_qgemm_verify_workspace_bytes(M, K, N, group, act_dtype);
+  if (need == 0) return VQV_ERR_UNSUPPORTED;  // no kernel takes the problem
+  if (need > VQV_NOALLOC_SCRATCH_BYTES) return VQV_ERR_WORKSPACE;
   unsigned char* ws = nullptr;
   if (scratch_of_current_device(&ws) != hipSuccess) return VQV_ERR_HIP;
   return launch_qgemm_verify_at(x, wq, scales, biases, y, M, K, N, fs.gs, act_dtype, draft,
-                                draft_len, B, T, argmax, accept_len, margin, ws, room,
+                                draft_len, B, T, argmax, accept_len, margin, ws,
                                 static_cast<hipStream_t>(hip_stream));
 }
 
@@ -324,6 +310,9 @@ vqv_status vqv_qgemm_swiglu(const void* x, const uint8_t* wq, const uint16_t* sc
     if (need && overlaps(workspace, need, ins[i], insz[i])) return VQV_ERR_ARG;
   }
   if (need && overlaps(h, hbytes, workspace, need)) return VQV_ERR_ARG;
+  if (!vqv::qgemm_swiglu_fused(M, K, N, (int)act_dtype, gs) &&
+      !vqv::qgemm_supported(M, K, N, (int)act_dtype, gs))
+    return VQV_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   const hipError_t e = vqv::launch_qgemm_swiglu(x, wq, scales, biases, h, M, K, N,
                                                 (int)act_dtype, gs, static_cast<float*>(workspace),

@@ -15,20 +15,13 @@ enum ActKind { ACT_BF16 = 0, ACT_FP16 = 1, ACT_FP32 = 2 };
 constexpr int kMaxK = 16384;
 constexpr int kMaxK32 = 8192;
 
-// y[M,N] = x[M,K] . W^T for 1 <= M <= 64, 64 <= K <= kMaxK, K % 64 == 0.
-// Every launcher takes the group shift gs: scales and biases hold one entry
-// per group of a row, 64 << gs values for gs = 0 (group 64) and gs = 1
-// (group 128, K % 128 == 0), 32 values for gs = -1 (group 32, K <= kMaxK32;
-// the whole-tile kernel takes it only where K/128 is a multiple of 4).
-hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
-                        const uint16_t* biases, float* y, int M, int K, int N, int act, int gs,
-                        hipStream_t stream);
-
-// Greedy verify fused into the projection's epilogue (M = B*T <= 8, 16-bit
-// activations, K within the single-row-set kernel's LDS budget): each
-// work-group reduces its columns to one top-two partial per row, and a
-// one-work-group kernel then reduces the partials, writes argmax, the margins
-// (when asked) and the accept lengths.
+// The greedy verify's arguments. With argmax set, a projection launch is the
+// fused verify's first half: each work-group reduces its columns to one
+// top-two partial (argmax.h) per row it covers, written to
+// partials[row * pgroups + g] (g: the work-group's index among the
+// work-groups that cover the row). verify_stage2 (verify.hip) then reduces
+// each row's pgroups partials, writes argmax, the margins (when asked) and
+// the accept lengths. With argmax NULL a launch is the plain projection.
 struct VerifyArgs {
   const int32_t* draft;      // [B, T-1]
   const int32_t* draft_len;  // [B] valid drafts per sequence, or NULL for T-1
@@ -36,21 +29,38 @@ struct VerifyArgs {
   int32_t* argmax;           // [B*T]
   int32_t* accept_len;       // [B]
   float* margin;             // [B*T] or NULL
-  uint4* partials;           // [work-groups][8]: (k1, i1, k2, -)
+  uint4* partials;           // [B*T][pgroups]: (k1, i1, k2, -)
+  int pgroups;               // partials per row
 };
 
-// Reduces `groups` partials per row ([groups][8], rows 0..B*T-1 <= 8) to the
-// argmax (and margin) of each row, then the accept walk of each sequence.
-hipError_t launch_verify_finish(const uint4* partials, int groups, const VerifyArgs& va,
-                                hipStream_t stream);
+// y[M,N] = x[M,K] . W^T for 1 <= M <= 64, 64 <= K <= kMaxK, K % 64 == 0.
+// Every launcher takes the group shift gs: scales and biases hold one entry
+// per group of a row, 64 << gs values for gs = 0 (group 64) and gs = 1
+// (group 128, K % 128 == 0), 32 values for gs = -1 (group 32, K <= kMaxK32;
+// the whole-tile kernel takes it only where K/128 is a multiple of 4).
+// With va.argmax set (va.pgroups = qgemm_verify_groups) the launch also
+// writes the fused verify's partials; y may then be NULL (not written).
+hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
+                        const uint16_t* biases, float* y, int M, int K, int N, int act, int gs,
+                        const VerifyArgs& va, hipStream_t stream);
 
-// The number of work-groups the fused projection launches, or 0 when the
-// fused path does not take this problem.
+// Whether some kernel takes the problem (its LDS image fits); checked before
+// anything is launched.
+bool qgemm_supported(int M, int K, int N, int act, int gs);
+
+// Partials per row of the fused verify (the work-groups that cover a row of
+// the kernel launch_qgemm picks), or 0 when no kernel takes the problem.
 int qgemm_verify_groups(int M, int K, int N, int act, int gs);
 
+// The fused verify: the projection with the top-two epilogue, then
+// verify_stage2 over its partials (va.partials holds M * qgemm_verify_groups
+// 16-byte slots; va.pgroups is set here).
 hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t* scales,
                                const uint16_t* biases, float* y, int M, int K, int N, int act,
                                int gs, const VerifyArgs& va, hipStream_t stream);
+
+// verify_stage2 over va.partials ([B*T][va.pgroups]).
+hipError_t launch_verify_finish(const VerifyArgs& va, hipStream_t stream);
 
 // M <= 8 with 16-bit activations, group 64 or 128 (gs 0 or 1), K % 256 == 0:
 // qgemm_w4_m8q (qgemm_m8.hip), codes read in whole 128-byte lines. With
@@ -69,26 +79,28 @@ enum Variant { kVariantAuto = 0, kVariantM8 = 1, kVariantM8Q = 2 };
 Variant forced_variant();
 
 // 9..64 rows in row sets of 16 (bf16/fp16, K within the kernel's LDS
-// budget): qgemm_w4_m16 (qgemm_m16.hip). Whether it takes the problem, and
-// the launch.
+// budget): qgemm_w4_m16 (qgemm_m16.hip). Whether it takes the problem, its
+// workers per row set (the fused verify's partials per row), and the launch.
 bool qgemm_m16_fits(int M, int K, int act, int gs);
+int qgemm_m16_workers(int M, int N);
 hipError_t launch_qgemm_m16(const void* x, const uint8_t* wq, const uint16_t* scales,
                             const uint16_t* biases, float* y, int M, int K, int N, int act,
-                            int gs, hipStream_t stream);
+                            int gs, const VerifyArgs& va, hipStream_t stream);
 
 // 17..64 rows at vocabulary widths: one weight stream for every row set
-// (qgemm_w4_rows, qgemm_m16.hip).
+// (qgemm_w4_rows, qgemm_m16.hip); one work-group covers all rows of its
+// columns (qgemm_rows_groups(N) work-groups).
 bool qgemm_rows_fits(int M, int K, int N, int act);
+int qgemm_rows_groups(int N);
 hipError_t launch_qgemm_rows(const void* x, const uint8_t* wq, const uint16_t* scales,
                              const uint16_t* biases, float* y, int M, int K, int N, int act,
-                             int gs, hipStream_t stream);
+                             int gs, const VerifyArgs& va, hipStream_t stream);
 
 // Wide outputs (at least two column tiles per wave of one work-group per
-// CU): qgemm_w4_wide (qgemm_m16.hip), waves own whole tiles over all of K.
-// With va.argmax (M <= 8) it is the fused verify's projection, one partial
-// per row and work-group (qgemm_wide_groups(M) work-groups).
+// CU): qgemm_w4_wide (qgemm_m16.hip), waves own whole tiles over all of K;
+// each row set has qgemm_wide_workers(M) work-groups.
 bool qgemm_wide_fits(int M, int K, int N, int act, int gs);
-int qgemm_wide_groups(int M);
+int qgemm_wide_workers(int M);
 hipError_t launch_qgemm_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
                              const uint16_t* biases, float* y, int M, int K, int N, int act,
                              int gs, const VerifyArgs& va, hipStream_t stream);
@@ -108,7 +120,7 @@ constexpr int kVerifyChunk = 4096;
 inline int verify_chunks(int N) { return (N + kVerifyChunk - 1) / kVerifyChunk; }
 
 // Two-stage greedy verify over fp32 logits [B*T, N]; `va.partials` holds
-// B*T*verify_chunks(N) 16-byte slots.
+// B*T*verify_chunks(N) 16-byte slots (va.pgroups is not used).
 hipError_t launch_verify(const float* logits, int N, const VerifyArgs& va, hipStream_t stream);
 
 }  // namespace vqv
