@@ -21,7 +21,7 @@ by its mean launch time (HIP events around a graph of back-to-back QMM
 launches, on the stream they run on) against the 8 TB/s HBM peak;
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
-`--variant m8|m8q` pins the projection kernel family of the M <= 8 path
+`--variant m8|m8q|v` pins the projection kernel family of the M <= 8 path
 (through VQV_FORCE_VARIANT) so that a profiler trace holds one variant only.
 On the target workload the line also carries the M=8 versus M=4 verified-row
 throughput at K=5120, N=1024 (the shape of the pages' 1.811133x figure); on
@@ -67,30 +67,8 @@ def qgemm_bytes(M, K, N, esz, group=64):
     return K * N // 2 + 4 * N * (K // group) + M * K * esz + 4 * M * N
 
 
-KERNEL_SOURCES = ("qgemm.hip", "qgemm_common.h", "qgemm_m16.hip", "qgemm_m8.hip")
-
-
-def projection_kernel(M, K, N, act, cus, group=64, variant="auto"):
-    """Name of the projection kernel the library launches for this shape (the
-    order of the library's dispatch; a label for the bench line only)."""
-    G, T = K // 64, (N + 15) // 16
-    rsets = (M + 15) // 16
-    if act == "fp32":
-        return "qgemm_w4"
-    tpw = (T + cus - 1) // cus
-    if 16 < M <= 64 and K % 128 == 0 and N * (K // 2) < 0x7F000000 and 8 <= tpw <= 40:
-        return "qgemm_w4_rows"
-    workers = max(8, (cus // rsets) // 8 * 8) if rsets > 1 else cus
-    if (M <= 64 and K <= 2560 and G % 8 == 0 and N * (K // 2) < 0x7F000000
-            and T >= 16 * workers and (group != 32 or (G // 2) % 4 == 0)):
-        return "qgemm_w4_wide"
-    if M <= 8 and K % 256 == 0 and group in (64, 128) and variant != "m8":
-        return "qgemm_w4_m8q"
-    if M <= 8 and K <= 5120:
-        return "qgemm_w4_m8"
-    if M <= 64 and K <= 2560:
-        return "qgemm_w4_m16"
-    return "qgemm_w4"
+KERNEL_SOURCES = ("qgemm.hip", "qgemm_common.h", "qgemm_m16.hip", "qgemm_m8.hip",
+                  "qgemm_v.hip")
 
 
 def kernel_sha():
@@ -256,9 +234,10 @@ def main():
                     help="one step: the projection with the verify fused into its epilogue, "
                          "the two calls back to back, or (gate/up) the projection with its "
                          "SwiGLU epilogue")
-    ap.add_argument("--variant", choices=["auto", "m8", "m8q"], default="auto",
+    ap.add_argument("--variant", choices=["auto", "m8", "m8q", "v"], default="auto",
                     help="pin the M <= 8 projection kernel (sets VQV_FORCE_VARIANT): m8q is "
-                         "the whole-line kernel, m8 the half-line one")
+                         "the whole-line MFMA kernel, m8 the half-line one, v the vector-ALU "
+                         "kernel (one or two rows)")
     ap.add_argument("--counter-pass", action="store_true",
                     help="eager QMM launches + a copy kernel, for one rocprofv3 --pmc pass")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -469,7 +448,7 @@ def main():
     # Rows/s against M with the same weights (the first M rows of x): the
     # plain projection's per-launch time at M = 1 and 4 as well.
     by_m, n1024 = {}, None
-    if args.workload == "target":
+    if args.workload == "target" and M == c["M"]:
         for m_sub in (1, 4):
             xs_sub = [cp[0][:m_sub].contiguous() for cp in copies]
             ys_sub = torch.empty((m_sub, N), dtype=torch.float32, device=dev)
@@ -531,7 +510,7 @@ def main():
     # epilogue, 8 bytes per row and work-group, and is timed with the finish
     # kernel in fused_us_mean).
     k_us = q_mean
-    kname = projection_kernel(M, K, N, act, props.multi_processor_count, group, args.variant)
+    kname = vqv.vqv_qgemm_kernel(M, K, N, group, vqv_act)
     if use_swiglu:
         # The step's kernel is the projection with the SwiGLU epilogue: it
         # writes h [M, N/2] instead of y [M, N].

@@ -120,6 +120,18 @@ const char* vqv_status_string(vqv_status s);
  */
 size_t vqv_qgemm_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype);
 
+/*
+ * The projection kernel that vqv_qgemm (and the fused calls) run for these
+ * sizes on the current device: a static string such as "qgemm_w4_m8q", the
+ * name a kernel trace shows, or NULL for arguments vqv_qgemm rejects. For
+ * profiling, the environment variable VQV_FORCE_VARIANT (read at each call)
+ * pins the one- and two-row and 8-row choice: "m8" the half-line
+ * MFMA kernel, "m8q" the whole-line one, "v" the vector-ALU kernel where it
+ * applies ("perf: tune DFlash2 M=8 verification for M1 and M2", PR
+ * description: the single-variant mode for tracing).
+ */
+const char* vqv_qgemm_kernel(int M, int K, int N, int group, vqv_dtype act_dtype);
+
 vqv_status vqv_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
                      const uint16_t* biases, float* y, int M, int K, int N, int group,
                      vqv_dtype act_dtype, void* workspace, size_t workspace_bytes,

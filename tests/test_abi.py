@@ -35,7 +35,8 @@ def declared_functions():
 
 def test_header_declares_the_calls():
     assert declared_functions() == sorted(
-        ["vqv_abi_version", "vqv_status_string", "vqv_qgemm_workspace_bytes", "vqv_qgemm",
+        ["vqv_abi_version", "vqv_status_string", "vqv_qgemm_kernel", "vqv_qgemm_workspace_bytes",
+         "vqv_qgemm",
          "vqv_verify_workspace_bytes", "vqv_verify", "vqv_verify_ex",
          "vqv_qgemm_verify_workspace_bytes", "vqv_qgemm_verify", "vqv_qgemm_verify_ex",
          "vqv_qgemm_swiglu_workspace_bytes", "vqv_qgemm_swiglu", "vqv_qgemm_verify_ex_noalloc"])
@@ -66,6 +67,44 @@ def test_workspace_queries(L):
     assert L.vqv_verify_workspace_bytes(4, 16, 151936) == 64 * 38 * 16
     assert L.vqv_verify_workspace_bytes(1, 1, 1) == 16
     assert L.vqv_verify_workspace_bytes(0, 8, 10) == 0
+
+
+def test_kernel_query(L):
+    """The kernel a problem runs on, planned for 256 CUs without a GPU."""
+    L.vqv_qgemm_kernel.restype = ctypes.c_char_p
+    k = lambda *a: L.vqv_qgemm_kernel(*a)
+    assert k(8, 5120, 17408, 64, BF16) == b"qgemm_w4_m8q"
+    assert k(64, 2560, 151936, 64, BF16) == b"qgemm_w4_rows"
+    assert k(8, 2560, 151936, 64, FP16) == b"qgemm_w4_wide"
+    assert k(16, 2560, 18432, 64, BF16) == b"qgemm_w4_m16"
+    assert k(8, 5120, 1024, 64, FP32) == b"qgemm_w4"
+    assert k(8, 5120, 17408, 32, BF16) == b"qgemm_w4_m8"
+    assert k(1, 5120, 17408, 64, BF16) == b"qgemm_w4_v"
+    assert k(1, 2560, 151936, 64, FP16) == b"qgemm_w4_wide"
+    assert k(1, 5120, 17408, 32, BF16) == b"qgemm_w4_m8"
+    assert k(2, 5120, 17408, 64, BF16) == b"qgemm_w4_m8q"
+    assert k(0, 5120, 17408, 64, BF16) is None
+    assert k(8, 5120, 17408, 16, BF16) is None
+    assert k(8, 5120, 17408, 64, 9) is None
+
+
+def test_variant_switch(L, monkeypatch):
+    """VQV_FORCE_VARIANT is read per call: "v" pins the vector-ALU kernel where
+    it applies (one or two rows of 16-bit activations), "m8q" and "m8" the
+    8-row MFMA kernels; other shapes ignore it."""
+    L.vqv_qgemm_kernel.restype = ctypes.c_char_p
+    monkeypatch.setenv("VQV_FORCE_VARIANT", "v")
+    assert L.vqv_qgemm_kernel(1, 5120, 17408, 64, BF16) == b"qgemm_w4_v"
+    assert L.vqv_qgemm_kernel(2, 2560, 1000, 128, FP16) == b"qgemm_w4_v"
+    assert L.vqv_qgemm_kernel(8, 5120, 17408, 64, BF16) == b"qgemm_w4_m8q"
+    assert L.vqv_qgemm_kernel(1, 5120, 1024, 64, FP32) == b"qgemm_w4"
+    assert L.vqv_qgemm_kernel(1, 5120, 1024, 32, BF16) != b"qgemm_w4_v"
+    assert L.vqv_qgemm_kernel(1, 2560, 151936, 64, BF16) == b"qgemm_w4_v"
+    monkeypatch.setenv("VQV_FORCE_VARIANT", "m8q")
+    assert L.vqv_qgemm_kernel(1, 5120, 17408, 64, BF16) == b"qgemm_w4_m8q"
+    assert L.vqv_qgemm_kernel(1, 2560, 151936, 64, BF16) == b"qgemm_w4_wide"
+    monkeypatch.setenv("VQV_FORCE_VARIANT", "m8")
+    assert L.vqv_qgemm_kernel(1, 5120, 17408, 64, BF16) == b"qgemm_w4_m8"
 
 
 def test_fused_workspace_queries(L):

@@ -20,7 +20,8 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["vqv_api.hip", "qgemm.hip", "qgemm_m8.hip", "qgemm_m16.hip", "verify.hip"]
+SOURCES = ["vqv_api.hip", "qgemm.hip", "qgemm_m8.hip", "qgemm_m16.hip", "qgemm_v.hip",
+           "verify.hip"]
 LIB = os.path.join(PKG, "libvqv.so")
 ARCH = "gfx950"
 

@@ -1109,7 +1109,7 @@ bool use_m8q(int M, int K, int act, int gs) {
 // its configuration and columns per work-group) before anything is
 // launched, and checks that its LDS image fits. The plain projection and the
 // fused verify take the same plan, so their outputs agree bit for bit.
-enum class Path { None, Rows, Wide, M8Q, M8, M16, W4 };
+enum class Path { None, Rows, Wide, V, M8Q, M8, M16, W4 };
 struct Plan {
   Path path;
   int cfg;   // qgemm_w4 configuration (W4)
@@ -1154,8 +1154,10 @@ hipError_t launch_w4_cfg(int cfg, const void* x, const uint8_t* wq, const uint16
   return hipErrorInvalidValue;
 }
 
-// M <= 8 (one row set) takes, in order: the whole-line kernel, the half-line
-// kernel, then qgemm_w4 (narrow N split into exactly one work-group per CU,
+// One row of 16-bit activations (group 64 or 128, K <= 8192) below
+// vocabulary widths takes the vector-ALU kernel. M <= 8 (one row set) takes,
+// in order: the whole-line
+// kernel, the half-line kernel, then qgemm_w4 (narrow N split into exactly one work-group per CU,
 // columns rounded up to 4; the W4A32 draft's narrow outputs one 16-column
 // tile per work-group with K split over 8 waves, measured fastest at
 // K = 5120, N = 1024: 11.1 us against 15.5 us for 64-column groups; wide N in
@@ -1169,7 +1171,14 @@ template <int ACT>
 Plan plan_act(int M, int K, int N, int gs) {
   constexpr bool h16 = ACT != ACT_FP32;
   if (h16 && qgemm_rows_fits(M, K, N, ACT)) return {Path::Rows, 0, 0};
+  // One row: the vector-ALU kernel, measured faster than the 8-row MFMA
+  // kernels at M = 1 and slower from M = 2, and slower than the whole-tile
+  // kernel at vocabulary widths; a profiling run may pin either.
+  const Variant fv = forced_variant();
+  const bool vfit = h16 && qgemm_v_fits(M, K, N, ACT, gs);
+  if (vfit && fv == kVariantV) return {Path::V, 0, 0};
   if (qgemm_wide_fits(M, K, N, ACT, gs)) return {Path::Wide, 0, 0};
+  if (vfit && fv == kVariantAuto && M == 1) return {Path::V, 0, 0};
   if (h16 && M <= 8 && use_m8q(M, K, ACT, gs)) return {Path::M8Q, 0, qgemm_m8q_cols(N)};
   if (h16 && M <= 8 && m8_fits(K, gs)) return {Path::M8, 0, m8_cols(N)};
   if (M > 8 && qgemm_m16_fits(M, K, ACT, gs)) return {Path::M16, 0, 0};
@@ -1204,6 +1213,7 @@ hipError_t launch_plan(const Plan& p, const void* x, const uint8_t* wq, const ui
   switch (p.path) {
     case Path::Rows: return launch_qgemm_rows(x, wq, scales, biases, y, M, K, N, ACT, gs, va, s);
     case Path::Wide: return launch_qgemm_wide(x, wq, scales, biases, y, M, K, N, ACT, gs, va, s);
+    case Path::V: return launch_qgemm_v(x, wq, scales, biases, y, M, K, N, ACT, gs, va, s);
     case Path::M8Q: return launch_qgemm_m8q(x, wq, scales, biases, y, M, K, N, ACT, gs, va, s);
     case Path::M8:
       if constexpr (ACT != ACT_FP32)
@@ -1221,6 +1231,20 @@ hipError_t launch_plan(const Plan& p, const void* x, const uint8_t* wq, const ui
 
 bool qgemm_supported(int M, int K, int N, int act, int gs) {
   return plan_for(M, K, N, act, gs).path != Path::None;
+}
+
+const char* qgemm_kernel_name(int M, int K, int N, int act, int gs) {
+  switch (plan_for(M, K, N, act, gs).path) {
+    case Path::Rows: return "qgemm_w4_rows";
+    case Path::Wide: return "qgemm_w4_wide";
+    case Path::V: return "qgemm_w4_v";
+    case Path::M8Q: return "qgemm_w4_m8q";
+    case Path::M8: return "qgemm_w4_m8";
+    case Path::M16: return "qgemm_w4_m16";
+    case Path::W4: return "qgemm_w4";
+    case Path::None: break;
+  }
+  return nullptr;
 }
 
 hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales,
@@ -1246,6 +1270,7 @@ int qgemm_verify_groups(int M, int K, int N, int act, int gs) {
   switch (p.path) {
     case Path::Rows: return qgemm_rows_groups(N);
     case Path::Wide: return qgemm_wide_workers(M);
+    case Path::V: return qgemm_v_groups(N);
     case Path::M16: return qgemm_m16_workers(M, N);
     case Path::M8Q:
     case Path::M8:
@@ -1267,14 +1292,14 @@ hipError_t launch_qgemm_verify(const void* x, const uint8_t* wq, const uint16_t*
 }
 
 Variant forced_variant() {
-  static const Variant v = [] {
-    const char* e = getenv("VQV_FORCE_VARIANT");
-    if (!e) return kVariantAuto;
-    if (!strcmp(e, "m8")) return kVariantM8;
-    if (!strcmp(e, "m8q")) return kVariantM8Q;
-    return kVariantAuto;
-  }();
-  return v;
+  // Read on every plan (a short scan of the environment), so that a process
+  // can switch variants between calls.
+  const char* e = getenv("VQV_FORCE_VARIANT");
+  if (!e) return kVariantAuto;
+  if (!strcmp(e, "m8")) return kVariantM8;
+  if (!strcmp(e, "m8q")) return kVariantM8Q;
+  if (!strcmp(e, "v")) return kVariantV;
+  return kVariantAuto;
 }
 
 }  // namespace vqv

@@ -48,6 +48,15 @@ const char* vqv_status_string(vqv_status s) {
   return "unknown status";
 }
 
+const char* vqv_qgemm_kernel(int M, int K, int N, int group, vqv_dtype act_dtype) {
+  const int gs = group_shift(group);
+  if (M < 1 || M > kMaxRows || N < 1 || K < kGroup || gs == kNoGroup || K % group ||
+      K % kGroup || K > (gs < 0 ? vqv::kMaxK32 : vqv::kMaxK))
+    return nullptr;
+  if (act_dtype != VQV_BF16 && act_dtype != VQV_FP16 && act_dtype != VQV_FP32) return nullptr;
+  return vqv::qgemm_kernel_name(M, K, N, (int)act_dtype, gs);
+}
+
 size_t vqv_qgemm_workspace_bytes(int M, int K, int N, int group, vqv_dtype act_dtype) {
   (void)M; (void)K; (void)N; (void)group; (void)act_dtype;
   return 0;  // partial sums are reduced on chip

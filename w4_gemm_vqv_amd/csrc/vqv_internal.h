@@ -45,8 +45,9 @@ hipError_t launch_qgemm(const void* x, const uint8_t* wq, const uint16_t* scales
                         const VerifyArgs& va, hipStream_t stream);
 
 // Whether some kernel takes the problem (its LDS image fits); checked before
-// anything is launched.
+// anything is launched. The name of that kernel, or NULL.
 bool qgemm_supported(int M, int K, int N, int act, int gs);
+const char* qgemm_kernel_name(int M, int K, int N, int act, int gs);
 
 // Partials per row of the fused verify (the work-groups that cover a row of
 // the kernel launch_qgemm picks), or 0 when no kernel takes the problem.
@@ -72,10 +73,21 @@ hipError_t launch_qgemm_m8q(const void* x, const uint8_t* wq, const uint16_t* sc
                             const uint16_t* biases, float* y, int M, int K, int N, int act,
                             int gs, const VerifyArgs& va, hipStream_t stream);
 
+// One or two rows of 16-bit activations on the vector ALUs (qgemm_v.hip):
+// qgemm_w4_v, a K-major dot2 matvec, qgemm_v_groups(N) work-groups (one
+// partial per row and work-group with va.argmax).
+bool qgemm_v_fits(int M, int K, int N, int act, int gs);
+int qgemm_v_groups(int N);
+hipError_t launch_qgemm_v(const void* x, const uint8_t* wq, const uint16_t* scales,
+                          const uint16_t* biases, float* y, int M, int K, int N, int act, int gs,
+                          const VerifyArgs& va, hipStream_t stream);
+
 // The kernel family a bench or profiler run pins through the environment
-// variable VQV_FORCE_VARIANT (read once per process): kVariantAuto when it is
-// unset or names no family. Only the M <= 8 projection honours it.
-enum Variant { kVariantAuto = 0, kVariantM8 = 1, kVariantM8Q = 2 };
+// variable VQV_FORCE_VARIANT (read at each plan): "m8" the half-line
+// 8-row kernel, "m8q" the whole-line one, "v" the vector-ALU kernel where it
+// fits; kVariantAuto when it is unset or names no family. Only the M <= 8
+// projection honours it.
+enum Variant { kVariantAuto = 0, kVariantM8 = 1, kVariantM8Q = 2, kVariantV = 3 };
 Variant forced_variant();
 
 // 9..64 rows in row sets of 16 (bf16/fp16, K within the kernel's LDS

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libvqv.so")
 
 VQV_BF16, VQV_FP16, VQV_FP32 = 0, 1, 2
 VQV_OK, VQV_ERR_ARG, VQV_ERR_UNSUPPORTED, VQV_ERR_ALIGN, VQV_ERR_WORKSPACE, VQV_ERR_HIP = range(6)
-EXPORTS = ("vqv_abi_version", "vqv_status_string", "vqv_qgemm_workspace_bytes", "vqv_qgemm",
+EXPORTS = ("vqv_abi_version", "vqv_status_string", "vqv_qgemm_kernel",
+           "vqv_qgemm_workspace_bytes", "vqv_qgemm",
            "vqv_verify_workspace_bytes", "vqv_verify", "vqv_verify_ex",
            "vqv_qgemm_verify_workspace_bytes", "vqv_qgemm_verify", "vqv_qgemm_verify_ex",
            "vqv_qgemm_swiglu_workspace_bytes", "vqv_qgemm_swiglu", "vqv_qgemm_verify_ex_noalloc")
@@ -47,6 +48,8 @@ def lib() -> ctypes.CDLL:
         L.vqv_abi_version.argtypes = []
         L.vqv_status_string.restype = ctypes.c_char_p
         L.vqv_status_string.argtypes = [i]
+        L.vqv_qgemm_kernel.restype = ctypes.c_char_p
+        L.vqv_qgemm_kernel.argtypes = [i, i, i, i, i]
         L.vqv_qgemm_workspace_bytes.restype = sz
         L.vqv_qgemm_workspace_bytes.argtypes = [i, i, i, i, i]
         L.vqv_qgemm.restype = i
@@ -129,6 +132,13 @@ def vqv_abi_version() -> int:
 
 def vqv_status_string(status: int) -> str:
     return lib().vqv_status_string(status).decode()
+
+
+def vqv_qgemm_kernel(M: int, K: int, N: int, group: int = 64,
+                     act_dtype: int = VQV_BF16) -> str | None:
+    """Name of the projection kernel these sizes run on (None if rejected)."""
+    r = lib().vqv_qgemm_kernel(M, K, N, group, act_dtype)
+    return r.decode() if r is not None else None
 
 
 def vqv_qgemm_workspace_bytes(M: int, K: int, N: int, group: int = 64,
