@@ -62,6 +62,7 @@ def test_version_and_strings(L):
 
 def test_workspace_queries(L):
     assert L.vqv_qgemm_workspace_bytes(8, 5120, 17408, 64, BF16) == 0
+    assert L.vqv_qgemm_workspace_bytes(8, 5120, 1024, 64, FP32) == 0
     # one 16-byte top-two partial per (row, chunk of 4096 logits)
     assert L.vqv_verify_workspace_bytes(1, 8, 17408) == 8 * 5 * 16
     assert L.vqv_verify_workspace_bytes(4, 16, 151936) == 64 * 38 * 16
@@ -78,6 +79,7 @@ def test_kernel_query(L):
     assert k(8, 2560, 151936, 64, FP16) == b"qgemm_w4_wide"
     assert k(16, 2560, 18432, 64, BF16) == b"qgemm_w4_m16"
     assert k(8, 5120, 1024, 64, FP32) == b"qgemm_w4"
+    assert k(8, 5120, 1024, 64, BF16) == b"qgemm_w4_m8q"
     assert k(8, 5120, 17408, 32, BF16) == b"qgemm_w4_m8"
     assert k(1, 5120, 17408, 64, BF16) == b"qgemm_w4_v"
     assert k(1, 2560, 151936, 64, FP16) == b"qgemm_w4_wide"

@@ -1301,13 +1301,12 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
             cq[q] = fmaf(-TR::c0, sq[q], half_hi(sb[q]));
           }
         } else {
+          // The bias term is added per chunk (below): only the scales here.
 #pragma unroll
           for (int t = 0; t < 4; ++t) bq[t] = unpack_codes(v[t], magic);
           const u32x2 sb = *reinterpret_cast<const u32x2*>(tab + (k * 16 + j) * GC + 2 * p);
           sq[0] = half_lo(sb.x);
           sq[1] = half_lo(sb.y);
-          cq[0] = fmaf(-TR::c0, sq[0], half_hi(sb.x));
-          cq[1] = fmaf(-TR::c0, sq[1], half_hi(sb.y));
         }
 #pragma unroll
         for (int r = 0; r < RS; ++r) {
@@ -1328,19 +1327,45 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
                 acc[k][r][e] = fmaf(sq[q], C[q][e], fmaf(cq[q], xq[e], acc[k][r][e]));
             }
           } else {
+            (void)xs;
             f32x4 C0 = mfma16x16x32<TR::f16>(Ar[0], bq[0], zero4);
             f32x4 C1 = mfma16x16x32<TR::f16>(Ar[2], bq[2], zero4);
             C0 = mfma16x16x32<TR::f16>(Ar[1], bq[1], C0);
             C1 = mfma16x16x32<TR::f16>(Ar[3], bq[3], C1);
-            const f32x4 xs0 = *reinterpret_cast<const f32x4*>(xs);
-            const f32x4 xs1 = *reinterpret_cast<const f32x4*>(xs + 16);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              acc[k][r][e] = fmaf(sq[0], C0[e], fmaf(cq[0], xs0[e], acc[k][r][e]));
-              acc[k][r][e] = fmaf(sq[1], C1[e], fmaf(cq[1], xs1[e], acc[k][r][e]));
-            }
+            for (int e = 0; e < 4; ++e)
+              acc[k][r][e] = fmaf(sq[1], C1[e], fmaf(sq[0], C0[e], acc[k][r][e]));
           }
         }
+      }
+    }
+
+    if constexpr (!HV) {
+      // ---- the chunk's bias term, sum_g (b - c0*s)[n, g] * xs[m, g] over its
+      // 2*KCP groups: a [16 rows x groups] x [groups x 16 columns] contraction
+      // on the fp32 MFMA, four groups at a time, added into the accumulators
+      // (same output layout). Lane (i, h) brings xs of row i, group 4u + h;
+      // lane (j, h) brings b - c0*s of column j, the same group; groups past
+      // the chunk bring zeros.
+      constexpr int NU = (GC + 3) / 4;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int gl = 4 * u + h;
+        const bool gin = gl < GC;
+        float xa[RS], bb[KT];
+#pragma unroll
+        for (int r = 0; r < RS; ++r)
+          xa[r] = gin ? xsl[((gl >> 1) * RS + r) * XSF + (gl & 1) * 16 + j] : 0.0f;
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+          const unsigned sb = gin ? tab[(k * 16 + j) * GC + gl] : 0u;
+          bb[k] = fmaf(-TR::c0, half_lo(sb), half_hi(sb));
+        }
+#pragma unroll
+        for (int k = 0; k < KT; ++k)
+#pragma unroll
+          for (int r = 0; r < RS; ++r)
+            acc[k][r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[r], bb[k], acc[k][r], 0, 0, 0);
       }
     }
   }
