@@ -29,9 +29,12 @@ the batched workload, the committed tokens per round with per-row accepts
 against a round clamped to the shortest sequence, for drafts planted at
 accept lengths drawn uniformly from 0..T-1.
 
-Two further modes serve rocprofv3 counter runs: `--counter-pass` launches the
-QMM and a copy kernel of known size eagerly, and `--write-traffic` turns a
-FETCH_SIZE run and a WRITE_SIZE run of it into per-launch HBM bytes.
+Three further modes read rocprofv3 runs: `--counter-pass` launches the QMM
+and a copy kernel of known size eagerly, `--write-traffic` turns a FETCH_SIZE
+run and a WRITE_SIZE run of it into per-launch HBM bytes, and `--gap-report`
+turns a kernel trace into a table of kernel durations and of the idle time
+between consecutive dispatches (the GPU timeline's holes), per pair of
+neighbouring kernels.
 """
 
 from __future__ import annotations
@@ -41,6 +44,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -79,18 +83,19 @@ def kernel_sha():
     return h.hexdigest()
 
 
-def traffic_key(workload, M, group):
-    return f"{workload}:M={M}" + ("" if group == 64 else f":group={group}")
+def traffic_key(workload, M, group, path="fused"):
+    return (f"{workload}:M={M}" + ("" if group == 64 else f":group={group}")
+            + (":swiglu" if path == "swiglu" else ""))
 
 
-def traffic_record(workload, M, group=64):
+def traffic_record(workload, M, group=64, path="fused"):
     """Measured HBM bytes per launch from committed rocprofv3 counter runs,
     valid only while the kernel source is unchanged."""
-    path = os.path.join(ROOT, "profiles", "qgemm_traffic.json")
-    if not os.path.exists(path):
+    fpath = os.path.join(ROOT, "profiles", "qgemm_traffic.json")
+    if not os.path.exists(fpath):
         return None
-    rec = json.load(open(path))
-    entry = rec.get("workloads", {}).get(traffic_key(workload, M, group))
+    rec = json.load(open(fpath))
+    entry = rec.get("workloads", {}).get(traffic_key(workload, M, group, path))
     if not entry or rec.get("kernel_sources_sha256") != kernel_sha():
         return None
     return entry["fetch_bytes"] + entry["write_bytes"]
@@ -168,6 +173,41 @@ def _counter_rows(run_dir):
     return rows
 
 
+def _short_kernel(name):
+    """A trace's kernel name without its namespace and argument list."""
+    name = re.sub(r"^void ", "", name).replace("vqv::(anonymous namespace)::", "")
+    return re.sub(r"\(.*$", "", name)
+
+
+def gap_report(run_dir):
+    """Per pair of neighbouring dispatches (kernel A, then kernel B) in a
+    rocprofv3 kernel trace: how often it occurs, B's median duration and the
+    median and 90th-percentile idle time from A's end to B's start (us)."""
+    import glob
+    import sqlite3
+    rows = []
+    for path in glob.glob(os.path.join(run_dir, "**", "*_results.db"), recursive=True):
+        db = sqlite3.connect(path)
+        rows += db.execute("select name, start, end from kernels").fetchall()
+    if not rows:
+        raise SystemExit(f"no kernel records under {run_dir}")
+    rows.sort(key=lambda r: r[1])
+    pairs = {}
+    for (a, _, a_end), (b, b_start, b_end) in zip(rows, rows[1:]):
+        key = (_short_kernel(a), _short_kernel(b))
+        d = pairs.setdefault(key, ([], []))
+        d[0].append((b_end - b_start) / 1e3)
+        d[1].append((b_start - a_end) / 1e3)
+    out = []
+    for (a, b), (dur, gap) in sorted(pairs.items(), key=lambda kv: -len(kv[1][0])):
+        gap.sort()
+        out.append({"after": a, "kernel": b, "count": len(dur),
+                    "kernel_us_median": statistics.median(dur),
+                    "gap_us_median": statistics.median(gap),
+                    "gap_us_p90": gap[min(len(gap) - 1, int(0.9 * len(gap)))]})
+    print(json.dumps(out, indent=1))
+
+
 def _fused_kernel(kname):
     """The M <= 8 projection kernels' instances with the verify epilogue (the
     eighth template argument of qgemm_w4_m8, the fifth of qgemm_w4_m8q)."""
@@ -178,7 +218,7 @@ def _fused_kernel(kname):
     return False
 
 
-def write_traffic(fetch_dir, write_dir, workload, M, group=64):
+def write_traffic(fetch_dir, write_dir, workload, M, group=64, path="fused"):
     """Per-launch HBM bytes of the QMM from a FETCH_SIZE pass and a WRITE_SIZE
     pass of `bench.py --counter-pass`, each scaled by what the same counter
     reads for the copy kernel (COPY_PROBE_BYTES read and written per launch)."""
@@ -207,7 +247,7 @@ def write_traffic(fetch_dir, write_dir, workload, M, group=64):
     sha = kernel_sha()
     if rec.get("kernel_sources_sha256") != sha:
         rec = {"kernel_sources_sha256": sha, "workloads": {}}
-    key = traffic_key(workload, M, group)
+    key = traffic_key(workload, M, group, path)
     rec["workloads"][key] = out
     json.dump(rec, open(path, "w"), indent=1, sort_keys=True)
     print(json.dumps({key: out}))
@@ -242,11 +282,17 @@ def main():
                     help="eager QMM launches + a copy kernel, for one rocprofv3 --pmc pass")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize two --counter-pass runs into profiles/qgemm_traffic.json")
+    ap.add_argument("--gap-report", metavar="TRACE_DIR",
+                    help="kernel durations and idle gaps between neighbouring dispatches "
+                         "of a rocprofv3 --kernel-trace run")
     args = ap.parse_args()
+    if args.gap_report:
+        gap_report(args.gap_report)
+        return
     if args.write_traffic:
         import gen
         write_traffic(*args.write_traffic, args.workload,
-                      args.m or gen.CONFIGS[args.workload]["M"], args.group)
+                      args.m or gen.CONFIGS[args.workload]["M"], args.group, args.path)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -357,10 +403,11 @@ def main():
 
     if args.counter_pass:
         # Eager launches for rocprofv3 --pmc (one counter pass per run): the
-        # QMM over every weight copy twice, then a plain copy kernel of known
-        # size whose counter reading calibrates bytes per counted unit.
+        # QMM (with --path swiglu the gate/up projection with its SwiGLU
+        # epilogue) over every weight copy twice, then a plain copy kernel of
+        # known size whose counter reading calibrates bytes per counted unit.
         for i in range(2 * R):
-            qmm(i, stream)
+            (swiglu if use_swiglu else qmm)(i, stream)
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -443,7 +490,25 @@ def main():
     g_c = graph_of(lambda i, st: cdst.copy_(csrc), 4)
     g_c.replay()
     copy_gbs = 2 * COPY_REF_BYTES * 4 / (min(timed(g_c) for _ in range(3)) * 1e-3) / 1e9
-    del csrc, cdst, g_c
+    # Read-only reference: a sum over 1 GiB (the reduction writes 4 bytes),
+    # the streaming-read rate torch's reduction reaches on this device. Launched
+    # eagerly (the reduction may clear memory with memsets, which stay out of
+    # graphs); four back-to-back sums between events.
+    rsrc = torch.empty(2 * COPY_REF_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    torch.sum(rsrc)
+    r_ms = []
+    for _ in range(3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(4):
+            torch.sum(rsrc)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        r_ms.append(e0.elapsed_time(e1))
+    read_gbs = 4 * 2 * COPY_REF_BYTES / (min(r_ms) * 1e-3) / 1e9
+    del csrc, cdst, g_c, rsrc
 
     # Rows/s against M with the same weights (the first M rows of x): the
     # plain projection's per-launch time at M = 1 and 4 as well.
@@ -554,14 +619,16 @@ def main():
                             if f_runs else None),
         "device": device,
         "copy_probe_gbs": copy_gbs,
+        "read_probe_gbs": read_gbs,
         "qgemm_by_M": by_m or None,
         "k5120_n1024_by_M": n1024,
         "batched_accepts": clamp,
         "variant": args.variant,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "frac_of_copy_probe": achieved / copy_gbs,
-                     "traffic": None if use_swiglu or args.n else
-                                traffic_record(args.workload, M, group),
+                     "frac_of_read_probe": achieved / read_gbs,
+                     "traffic": None if args.n else
+                                traffic_record(args.workload, M, group, args.path),
                      "kernel": kname, "bytes_per_launch": qb, "us_per_launch": k_us},
         "cpu_baseline": None,
     }
