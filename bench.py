@@ -181,14 +181,20 @@ def _short_kernel(name):
 
 def gap_report(run_dir):
     """Per pair of neighbouring dispatches (kernel A, then kernel B) in a
-    rocprofv3 kernel trace: how often it occurs, B's median duration and the
-    median and 90th-percentile idle time from A's end to B's start (us)."""
+    rocprofv3 kernel trace (CSV output or SQLite database): how often it
+    occurs, B's median duration and the median and 90th-percentile idle time
+    from A's end to B's start (us)."""
+    import csv
     import glob
     import sqlite3
     rows = []
-    for path in glob.glob(os.path.join(run_dir, "**", "*_results.db"), recursive=True):
-        db = sqlite3.connect(path)
-        rows += db.execute("select name, start, end from kernels").fetchall()
+    for path in glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += [(r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+                 for r in csv.DictReader(open(path))]
+    if not rows:
+        for path in glob.glob(os.path.join(run_dir, "**", "*_results.db"), recursive=True):
+            db = sqlite3.connect(path)
+            rows += db.execute("select name, start, end from kernels").fetchall()
     if not rows:
         raise SystemExit(f"no kernel records under {run_dir}")
     rows.sort(key=lambda r: r[1])
@@ -242,14 +248,14 @@ def write_traffic(fetch_dir, write_dir, workload, M, group=64, path="fused"):
         out[f"{key}_counter_kib"] = q_kib
         out[f"{key}_copy_calibration"] = per_byte
         out[f"{key}_dispatches"] = len(q) - half
-    path = os.path.join(ROOT, "profiles", "qgemm_traffic.json")
-    rec = json.load(open(path)) if os.path.exists(path) else {}
+    out_path = os.path.join(ROOT, "profiles", "qgemm_traffic.json")
+    rec = json.load(open(out_path)) if os.path.exists(out_path) else {}
     sha = kernel_sha()
     if rec.get("kernel_sources_sha256") != sha:
         rec = {"kernel_sources_sha256": sha, "workloads": {}}
     key = traffic_key(workload, M, group, path)
     rec["workloads"][key] = out
-    json.dump(rec, open(path, "w"), indent=1, sort_keys=True)
+    json.dump(rec, open(out_path, "w"), indent=1, sort_keys=True)
     print(json.dumps({key: out}))
 
 

@@ -1087,17 +1087,26 @@ hipError_t launch_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
 // the waves' (s, b) tables are staged, then each wave runs its tiles over
 // the chunk's pairs with one unpack per code and RS x 4 MFMAs per step,
 // accumulating in registers across chunks (KT tiles x RS row sets).
-// * Step order: pair-major within a chunk (pair p of tiles 0..KT-1, then
-//   pair p+1). Each step unpacks one tile's codes once for all row sets; the
-//   first RH row sets' A operands are read once per pair and held, the other
-//   row sets' operands and the row sums are read per step (registers).
-// * Weight ring: slot k holds tile k's next pair (D = KT), and runs on across
-//   chunk boundaries, so the next chunk's first weights are in flight during
-//   its staging. Steps past a wave's tiles or past K read zeros.
+// * Step order: tile-major within a chunk (pairs 0..KCP-1 of tile k, then
+//   of tile k+1). Each step unpacks one tile's codes once for all row sets
+//   and reads the row sets' A operands from LDS; the accumulators of a tile
+//   are finished with the tile's steps. (Pair-major order, which held some A
+//   operands in registers across the tiles, measured about 4% slower.)
+// * Weight ring: kRowsRing steps ahead, running on across chunk boundaries,
+//   so the next chunk's first weights are in flight during its staging; the
+//   two halves of each column's 128-byte line are loaded by consecutive
+//   steps. Non-temporal: the codes are read once, and the activations and
+//   tables, which every chunk reads again, keep more of L2. Steps past a
+//   wave's tiles or past K read zeros.
 // * The work-group's tiles: [tbeg, tbeg + tpw); wave w takes tbeg + w + 8k.
 // Every sum runs in a fixed order, so results are deterministic. With
 // va.argmax set the work-group also writes one top-two partial per row over
 // its columns (the greedy verify's first half, as in qgemm_w4_wide).
+// Weight loads in flight per wave in qgemm_w4_rows (steps ahead; 8 and 10
+// measured no faster), and their cache policy bits (non-temporal).
+constexpr int kRowsRing = 5;
+constexpr int kRowsAux = 2;
+
 template <int ACT, int RS, int KT, int KCP, int GS>
 __global__ __launch_bounds__(512) void qgemm_w4_rows(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
@@ -1113,7 +1122,6 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
   constexpr int XSF = 16 * NQ;                      // row sums per image
   static_assert(TR::parts == 1, "16-bit activations only");
   constexpr int NW = 8;
-  constexpr int RH = RS >= 4 ? 1 : (RS < 2 ? RS : 2);  // row sets whose A stays in registers
   constexpr int GC = 2 * KCP;                        // groups per chunk
   constexpr int ITEMS = GC * 2 * RS;                 // (group, row octet) staging items
   constexpr int XR = (ITEMS + NW - 1) / NW;          // staging loads per lane
@@ -1168,10 +1176,15 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
                ? (unsigned)tile[k] * 16u * rowbytes + 64u * (unsigned)pg
                : kSkip;
   };
-  u32x4 ring[KT];
+  // The weight loads in flight: ring[i] holds step s + i's codes at step s,
+  // where the steps run tile-major through each chunk and on into the next.
+  constexpr int RD = kRowsRing;
+  static_assert(RD <= KT * KCP, "the ring reaches at most one chunk ahead");
+  u32x4 ring[RD];
 #pragma unroll
-  for (int k = 0; k < KT; ++k)
-    ring[k] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, codes_at(0, 0, k), 0);
+  for (int i = 0; i < RD; ++i)
+    ring[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff,
+                                                    codes_at(i / (KT * KCP), i % KCP, (i / KCP) % KT), kRowsAux);
 
   f32x4 acc[KT][RS];
 #pragma unroll
@@ -1260,29 +1273,30 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
     }
     __syncthreads();
 
-    // ---- the chunk's steps, pair-major: (pair p, tile k) for k = 0..KT-1.
+    // ---- the chunk's steps, tile-major: (tile k, pair p) for p = 0..KCP-1.
 #pragma unroll
-    for (int p = 0; p < KCP; ++p) {
-      // The first RH row sets' A operands stay in registers for the pair's
-      // KT steps; the others' and all row sums are read per step.
-      const unsigned a_lane = (unsigned)(h * 16 + j) * kSlot16;
-      auto a_of = [&](int r, int t, unsigned base) {
-        return *reinterpret_cast<const u32x4*>(ximg + base + (p * RS + r) * kPair16 + t * kTRow16);
-      };
-      u32x4 A[RH][4];
+    for (int k = 0; k < KT; ++k) {
 #pragma unroll
-      for (int r = 0; r < RH; ++r)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) A[r][t] = a_of(r, t, a_lane);
-#pragma unroll
-      for (int k = 0; k < KT; ++k) {
-        // Per-step LDS offsets behind an empty asm: the per-step reads below
-        // must not be hoisted out of the tile loop (registers).
-        unsigned a_step = a_lane, x_step = 4u * (unsigned)h;
+      for (int p = 0; p < KCP; ++p) {
+        // Per-step LDS offsets behind an empty asm: the steps' reads must not
+        // be hoisted out of the loops (registers).
+        unsigned a_step = (unsigned)(h * 16 + j) * kSlot16, x_step = 4u * (unsigned)h;
         asm volatile("" : "+v"(a_step), "+v"(x_step));
-        const u32x4 w = ring[k];
-        ring[k] = __builtin_amdgcn_raw_buffer_load_b128(
-            wr, woff, p + 1 < KCP ? codes_at(c, p + 1, k) : codes_at(c + 1, 0, k), 0);
+        auto a_of = [&](int r, int t) {
+          return *reinterpret_cast<const u32x4*>(ximg + a_step + (p * RS + r) * kPair16 +
+                                                 t * kTRow16);
+        };
+        // Shift the ring (register renaming in the unrolled chunk) and load
+        // the step RD ahead.
+        const u32x4 w = ring[0];
+#pragma unroll
+        for (int i = 0; i + 1 < RD; ++i) ring[i] = ring[i + 1];
+        {
+          const int nx = k * KCP + p + RD;           // the step to load, from this chunk's start
+          const int kn = (nx / KCP) % KT, pn = nx % KCP, cn = nx / (KT * KCP);
+          ring[RD - 1] = __builtin_amdgcn_raw_buffer_load_b128(
+              wr, woff, cn ? codes_at(c + 1, pn, kn) : codes_at(c, pn, kn), kRowsAux);
+        }
         const u32x4 v = split_groups(w);
         u32x4 bq[4];
         float sq[NQ], cq[NQ];
@@ -1313,7 +1327,7 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
           const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
           u32x4 Ar[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) Ar[t] = r < RH ? A[r < RH ? r : 0][t] : a_of(r, t, a_step);
+          for (int t = 0; t < 4; ++t) Ar[t] = a_of(r, t);
           const float* xs = xsl + (p * RS + r) * XSF + x_step;
           if constexpr (HV) {
             f32x4 C[4];
@@ -1336,6 +1350,10 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
             for (int e = 0; e < 4; ++e)
               acc[k][r][e] = fmaf(sq[1], C1[e], fmaf(sq[0], C0[e], acc[k][r][e]));
           }
+          // The tile's sums are not read again before the chunk's bias term:
+          // without this the compiler defers every step's update to there and
+          // keeps all the steps' products live.
+          asm volatile("" : "+v"(acc[k][r]));
         }
       }
     }
