@@ -224,10 +224,35 @@ def _fused_kernel(kname):
     return False
 
 
-def write_traffic(fetch_dir, write_dir, workload, M, group=64, path="fused"):
+def _request_bytes(run_dir):
+    """Read bytes per dispatch of a rocprofv3 --pmc pass over TCC_EA0_RDREQ_32B,
+    _64B and _128B (CSV output): 32, 64 and 128 bytes per request of each size,
+    summed over the instances. Returns (QMM dispatches, copy dispatches)."""
+    import csv
+    import glob
+    per = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            size = {"TCC_EA0_RDREQ_32B": 32, "TCC_EA0_RDREQ_64B": 64,
+                    "TCC_EA0_RDREQ_128B": 128}.get(r["Counter_Name"])
+            if size is None:
+                continue
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            per[key] = per.get(key, 0.0) + size * float(r["Counter_Value"])
+    q = [b for (_, k), b in sorted(per.items()) if "qgemm_w4" in k and not _fused_kernel(k)]
+    cp = [b for (_, k), b in sorted(per.items()) if "neg" in k.lower()]
+    if not q or not cp:
+        raise SystemExit(f"no QMM or copy dispatches with request counts under {run_dir}")
+    return q, cp
+
+
+def write_traffic(fetch_dir, write_dir, workload, M, group=64, path="fused", req_dir=None):
     """Per-launch HBM bytes of the QMM from a FETCH_SIZE pass and a WRITE_SIZE
     pass of `bench.py --counter-pass`, each scaled by what the same counter
-    reads for the copy kernel (COPY_PROBE_BYTES read and written per launch)."""
+    reads for the copy kernel (COPY_PROBE_BYTES read and written per launch).
+    With a third pass over the read request counts by size, the read bytes
+    are also summed request by request, a check of the copy-kernel scaling
+    that needs no calibration."""
     out = {}
     for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         q, cp = [], []
@@ -248,6 +273,10 @@ def write_traffic(fetch_dir, write_dir, workload, M, group=64, path="fused"):
         out[f"{key}_counter_kib"] = q_kib
         out[f"{key}_copy_calibration"] = per_byte
         out[f"{key}_dispatches"] = len(q) - half
+    if req_dir:
+        q, cp = _request_bytes(req_dir)
+        out["read_bytes_by_request_size"] = statistics.fmean(q[len(q) // 2:])
+        out["copy_read_bytes_by_request_size"] = statistics.fmean(cp)
     out_path = os.path.join(ROOT, "profiles", "qgemm_traffic.json")
     rec = json.load(open(out_path)) if os.path.exists(out_path) else {}
     sha = kernel_sha()
@@ -286,8 +315,9 @@ def main():
                          "kernel (one or two rows)")
     ap.add_argument("--counter-pass", action="store_true",
                     help="eager QMM launches + a copy kernel, for one rocprofv3 --pmc pass")
-    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="summarize two --counter-pass runs into profiles/qgemm_traffic.json")
+    ap.add_argument("--write-traffic", nargs="+", metavar="DIR",
+                    help="summarize --counter-pass runs into profiles/qgemm_traffic.json: "
+                         "FETCH_SIZE dir, WRITE_SIZE dir [, TCC_EA0_RDREQ_32B/64B/128B dir]")
     ap.add_argument("--gap-report", metavar="TRACE_DIR",
                     help="kernel durations and idle gaps between neighbouring dispatches "
                          "of a rocprofv3 --kernel-trace run")
@@ -297,8 +327,11 @@ def main():
         return
     if args.write_traffic:
         import gen
-        write_traffic(*args.write_traffic, args.workload,
-                      args.m or gen.CONFIGS[args.workload]["M"], args.group, args.path)
+        if len(args.write_traffic) not in (2, 3):
+            raise SystemExit("--write-traffic takes FETCH_DIR WRITE_DIR [REQUEST_DIR]")
+        fdir, wdir, *rdir = args.write_traffic
+        write_traffic(fdir, wdir, args.workload, args.m or gen.CONFIGS[args.workload]["M"],
+                      args.group, args.path, rdir[0] if rdir else None)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -496,10 +529,11 @@ def main():
     g_c = graph_of(lambda i, st: cdst.copy_(csrc), 4)
     g_c.replay()
     copy_gbs = 2 * COPY_REF_BYTES * 4 / (min(timed(g_c) for _ in range(3)) * 1e-3) / 1e9
-    # Read-only reference: a sum over 1 GiB (the reduction writes 4 bytes),
-    # the streaming-read rate torch's reduction reaches on this device. Launched
-    # eagerly (the reduction may clear memory with memsets, which stay out of
-    # graphs); four back-to-back sums between events.
+    # Read-only context: torch's own sum over 1 GiB (it writes 4 bytes). It
+    # reads at about 3.9-4.0 TB/s here, below what the copy and the projection
+    # kernels stream, so it is reported as context and no fraction is taken of
+    # it. Launched eagerly (the reduction may clear memory with memsets, which
+    # stay out of graphs); four back-to-back sums between events.
     rsrc = torch.empty(2 * COPY_REF_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
     torch.sum(rsrc)
     r_ms = []
@@ -625,14 +659,13 @@ def main():
                             if f_runs else None),
         "device": device,
         "copy_probe_gbs": copy_gbs,
-        "read_probe_gbs": read_gbs,
+        "torch_sum_read_gbs": read_gbs,
         "qgemm_by_M": by_m or None,
         "k5120_n1024_by_M": n1024,
         "batched_accepts": clamp,
         "variant": args.variant,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "frac_of_copy_probe": achieved / copy_gbs,
-                     "frac_of_read_probe": achieved / read_gbs,
                      "traffic": None if args.n else
                                 traffic_record(args.workload, M, group, args.path),
                      "kernel": kname, "bytes_per_launch": qb, "us_per_launch": k_us},
