@@ -31,7 +31,9 @@ accept lengths drawn uniformly from 0..T-1.
 
 Three further modes read rocprofv3 runs: `--counter-pass` launches the QMM
 and a copy kernel of known size eagerly, `--write-traffic` turns a FETCH_SIZE
-run and a WRITE_SIZE run of it into per-launch HBM bytes, and `--gap-report`
+run and a WRITE_SIZE run of it (and optionally a run over the read request
+counts by size, a check that needs no calibration) into per-launch HBM
+bytes, and `--gap-report`
 turns a kernel trace into a table of kernel durations and of the idle time
 between consecutive dispatches (the GPU timeline's holes), per pair of
 neighbouring kernels.
