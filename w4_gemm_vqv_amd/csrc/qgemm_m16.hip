@@ -1102,6 +1102,16 @@ hipError_t launch_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
 // Every sum runs in a fixed order, so results are deterministic. With
 // va.argmax set the work-group also writes one top-two partial per row over
 // its columns (the greedy verify's first half, as in qgemm_w4_wide).
+// LDS of qgemm_w4_rows: the chunk's activation images and row sums and each
+// wave's (s, b) table during the loop; the fused verify's candidates after
+// it (one line per wave and column, then one entry per wave and row).
+template <int RS, int KT, int KCP, bool HV>
+constexpr int rows_lds_bytes() {
+  const int loop = KCP * RS * (kPair16 + (HV ? 256 : 128)) + 8 * KT * 16 * (HV ? 4 : 2) * KCP * 4;
+  const int cand = 8 * 16 * (3 * 16 * RS + 1) * 4 + 8 * 16 * RS * 12;
+  return loop > cand ? loop : cand;
+}
+
 // Weight loads in flight per wave in qgemm_w4_rows (steps ahead; 8 and 10
 // measured no faster), and their cache policy bits (non-temporal).
 constexpr int kRowsRing = 5;
@@ -1398,8 +1408,7 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
     // accumulators hold finite sums of zero activations) and never read.
     constexpr int R16 = 16 * RS;
     constexpr int JS = 3 * R16 + 1;                    // dwords per (wave, j) line
-    static_assert(NW * 16 * JS * 4 + NW * R16 * 12 <=
-                      KCP * RS * (kPair16 + 4 * XSF) + NW * KT * 16 * NQ * KCP * 4,
+    static_assert(NW * 16 * JS * 4 + NW * R16 * 12 <= rows_lds_bytes<RS, KT, KCP, HV>(),
                   "the candidates fit in the kernel's LDS");
     __syncthreads();                                   // every wave is past its last LDS read
     unsigned* cand = reinterpret_cast<unsigned*>(lds);
@@ -1501,13 +1510,12 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
   }
 }
 
-template <int RS, int KT, int KCP, bool HV>
-constexpr int rows_lds_bytes() {
-  return KCP * RS * (kPair16 + (HV ? 256 : 128)) + 8 * KT * 16 * (HV ? 4 : 2) * KCP * 4;
-}
 
 constexpr int kRowsKT = 5;
-constexpr int kRowsKCP = 5;
+// Group pairs per chunk: even, so that no 128-byte line of a column's codes
+// is split between two chunks (with 5, the lines of pairs 4-5 and 14-15 were
+// read twice: 305 against 288.5 MB per launch at K = 2560).
+constexpr int kRowsKCP = 4;
 
 // Column tiles per work-group of qgemm_w4_rows: an equal share of the CUs.
 int rows_tiles_per_group(int N) {
