@@ -1092,12 +1092,14 @@ hipError_t launch_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
 //   and reads the row sets' A operands from LDS; the accumulators of a tile
 //   are finished with the tile's steps. (Pair-major order, which held some A
 //   operands in registers across the tiles, measured about 4% slower.)
-// * Weight ring: kRowsRing steps ahead, running on across chunk boundaries,
-//   so the next chunk's first weights are in flight during its staging; the
-//   two halves of each column's 128-byte line are loaded by consecutive
-//   steps. Non-temporal: the codes are read once, and the activations and
-//   tables, which every chunk reads again, keep more of L2. Steps past a
-//   wave's tiles or past K read zeros.
+// * Weight ring: whole-line units (qgemm_common.h: a tile times 128 bytes of
+//   each column, two loads of eight whole lines each, rearranged into the
+//   two steps' operands by exchange()), kRowsRing units ahead, running on
+//   across chunk boundaries, so the next chunk's first weights are in flight
+//   during its staging. Loading each line in two 64-byte halves, one step
+//   apart, read a third of the lines twice (1.32x the weight bytes; 1.04x
+//   whole). Non-temporal: the codes are read once. Units past a wave's tiles
+//   or past K read zeros.
 // * The work-group's tiles: [tbeg, tbeg + tpw); wave w takes tbeg + w + 8k.
 // Every sum runs in a fixed order, so results are deterministic. With
 // va.argmax set the work-group also writes one top-two partial per row over
@@ -1112,9 +1114,11 @@ constexpr int rows_lds_bytes() {
   return loop > cand ? loop : cand;
 }
 
-// Weight loads in flight per wave in qgemm_w4_rows (steps ahead; 8 and 10
-// measured no faster), and their cache policy bits (non-temporal).
-constexpr int kRowsRing = 5;
+// Whole-line units of weights in flight per wave in qgemm_w4_rows (two steps
+// each; 2 and 3 measured about 1 % slower), and their cache policy bits
+// (non-temporal: without them the kernel read 319 against 227 MB per launch
+// at K = 2560, N = 151936, and ran 6 % slower).
+constexpr int kRowsRing = 4;
 constexpr int kRowsAux = 2;
 
 template <int ACT, int RS, int KT, int KCP, int GS>
@@ -1179,22 +1183,37 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
     tile[k] = tbeg + wave + NW * k;
     tin[k] = tile[k] < tend;
   }
-  const unsigned woff = (unsigned)j * rowbytes + 16u * h;
-  auto codes_at = [&](int c, int p, int k) {        // step (chunk, pair, tile)
-    const int pg = c * KCP + p;
+  // Whole-line units (qgemm_common.h): tile k times the 128 bytes of group
+  // pairs 2q and 2q+1 of the chunk, two loads (columns 0-7 and 8-15).
+  static_assert(KCP % 2 == 0, "chunks of whole 128-byte lines");
+  constexpr int QC = KCP / 2;                        // units per tile and chunk
+  const unsigned voff_a = (unsigned)(j & 7) * rowbytes + 64u * (unsigned)(j >> 3) + 16u * h;
+  const unsigned voff_b = voff_a + 8u * rowbytes;
+  auto codes_at = [&](int c, int q, int k) {        // unit (chunk, pair pair, tile)
+    const int pg = c * KCP + 2 * q;
     return tin[k] && c < nch && pg < GP
                ? (unsigned)tile[k] * 16u * rowbytes + 64u * (unsigned)pg
                : kSkip;
   };
-  // The weight loads in flight: ring[i] holds step s + i's codes at step s,
-  // where the steps run tile-major through each chunk and on into the next.
-  constexpr int RD = kRowsRing;
-  static_assert(RD <= KT * KCP, "the ring reaches at most one chunk ahead");
-  u32x4 ring[RD];
+  // The units in flight: ring[i] holds unit u + i's codes when unit u is
+  // next, the units running tile-major through each chunk and on into the
+  // next (unit u of a chunk: tile u / QC, pairs 2(u % QC) and 2(u % QC) + 1).
+  constexpr int RU = kRowsRing;
+  static_assert(RU <= KT * QC, "the ring reaches at most one chunk ahead");
+  struct Unit {
+    u32x4 a, b;
+  };
+  auto unit_load = [&](int c, int u) {
+    const int dc = u / (KT * QC), w = u % (KT * QC);
+    const unsigned so = codes_at(c + dc, w % QC, w / QC);
+    Unit r;
+    r.a = __builtin_amdgcn_raw_buffer_load_b128(wr, voff_a, so, kRowsAux);
+    r.b = __builtin_amdgcn_raw_buffer_load_b128(wr, voff_b, so, kRowsAux);
+    return r;
+  };
+  Unit ring[RU];
 #pragma unroll
-  for (int i = 0; i < RD; ++i)
-    ring[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff,
-                                                    codes_at(i / (KT * KCP), i % KCP, (i / KCP) % KT), kRowsAux);
+  for (int i = 0; i < RU; ++i) ring[i] = unit_load(0, i);
 
   f32x4 acc[KT][RS];
 #pragma unroll
@@ -1284,6 +1303,7 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
     __syncthreads();
 
     // ---- the chunk's steps, tile-major: (tile k, pair p) for p = 0..KCP-1.
+    u32x4 w_odd;                                     // the second step of the current unit
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
 #pragma unroll
@@ -1296,16 +1316,20 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
           return *reinterpret_cast<const u32x4*>(ximg + a_step + (p * RS + r) * kPair16 +
                                                  t * kTRow16);
         };
-        // Shift the ring (register renaming in the unrolled chunk) and load
-        // the step RD ahead.
-        const u32x4 w = ring[0];
+        // An even step takes the next unit: the exchange gives its two steps'
+        // operands, the ring shifts (register renaming in the unrolled chunk)
+        // and loads the unit RU ahead; the odd step uses the second operand.
+        u32x4 w;
+        if (p % 2 == 0) {
+          exchange(ring[0].a, ring[0].b, w, w_odd);
+          // Both operands are complete before the refill is issued, so the
+          // slot's registers are free for it.
+          asm volatile("" : "+v"(w), "+v"(w_odd) :: "memory");
 #pragma unroll
-        for (int i = 0; i + 1 < RD; ++i) ring[i] = ring[i + 1];
-        {
-          const int nx = k * KCP + p + RD;           // the step to load, from this chunk's start
-          const int kn = (nx / KCP) % KT, pn = nx % KCP, cn = nx / (KT * KCP);
-          ring[RD - 1] = __builtin_amdgcn_raw_buffer_load_b128(
-              wr, woff, cn ? codes_at(c + 1, pn, kn) : codes_at(c, pn, kn), kRowsAux);
+          for (int i = 0; i + 1 < RU; ++i) ring[i] = ring[i + 1];
+          ring[RU - 1] = unit_load(c, k * QC + p / 2 + RU);
+        } else {
+          w = w_odd;
         }
         const u32x4 v = split_groups(w);
         u32x4 bq[4];

@@ -73,34 +73,6 @@ __host__ __device__ inline Q8Layout q8_layout(int G, int WGC, int NW, int XB) {
   return L;
 }
 
-// The MFMA operands of a unit's two steps from its two loads (see the
-// header): s0 = j < 8 ? a[lane] : b[lane - 8], s1 = j < 8 ? a[lane + 8] :
-// b[lane], one v_cndmask_b32 with a row-shifted DPP source per dword (VCC
-// holds the lanes that keep their own value). The row shifts write every
-// lane, so no result is tied to a ring register and the ring can be refilled
-// as soon as this has run. The leading s_nop covers a VALU write of a or b
-// just before (two wait states before a DPP read).
-__device__ __forceinline__ void exchange(const u32x4& a, const u32x4& b, u32x4& s0, u32x4& s1) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "s_mov_b32 vcc_lo, 0x00ff00ff\n\t"
-      "s_mov_b32 vcc_hi, 0x00ff00ff\n\t"
-      "v_cndmask_b32_dpp %0, %8, %12, vcc row_shr:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_cndmask_b32_dpp %1, %9, %13, vcc row_shr:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_cndmask_b32_dpp %2, %10, %14, vcc row_shr:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_cndmask_b32_dpp %3, %11, %15, vcc row_shr:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "s_mov_b32 vcc_lo, 0xff00ff00\n\t"
-      "s_mov_b32 vcc_hi, 0xff00ff00\n\t"
-      "v_cndmask_b32_dpp %4, %12, %8, vcc row_shl:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_cndmask_b32_dpp %5, %13, %9, vcc row_shl:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_cndmask_b32_dpp %6, %14, %10, vcc row_shl:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_cndmask_b32_dpp %7, %15, %11, vcc row_shl:8 row_mask:0xf bank_mask:0xf bound_ctrl:1"
-      : "=&v"(s0.x), "=&v"(s0.y), "=&v"(s0.z), "=&v"(s0.w), "=&v"(s1.x), "=&v"(s1.y),
-        "=&v"(s1.z), "=&v"(s1.w)
-      : "v"(b.x), "v"(b.y), "v"(b.z), "v"(b.w), "v"(a.x), "v"(a.y), "v"(a.z), "v"(a.w)
-      : "vcc");
-}
-
 template <int ACT, int D, int XB, int AUX, bool FUSED, int GS>
 __global__ __launch_bounds__(512) void qgemm_w4_m8q(
     const void* __restrict__ x, const uint8_t* __restrict__ wq,
