@@ -1087,11 +1087,12 @@ hipError_t launch_wide(const void* x, const uint8_t* wq, const uint16_t* scales,
 // the waves' (s, b) tables are staged, then each wave runs its tiles over
 // the chunk's pairs with one unpack per code and RS x 4 MFMAs per step,
 // accumulating in registers across chunks (KT tiles x RS row sets).
-// * Step order: tile-major within a chunk (pairs 0..KCP-1 of tile k, then
-//   of tile k+1). Each step unpacks one tile's codes once for all row sets
-//   and reads the row sets' A operands from LDS; the accumulators of a tile
-//   are finished with the tile's steps. (Pair-major order, which held some A
-//   operands in registers across the tiles, measured about 4% slower.)
+// * Step order: the wave's tiles in blocks of two; within a block the pairs
+//   in order, and at each pair both tiles' codes are unpacked once for all
+//   row sets, then each row set's A operands are read once from LDS for
+//   both tiles. (Pair-major order over all tiles, holding some A operands in
+//   registers, was about 4 % slower than one tile at a time; two tiles per
+//   A read is 2 % faster than one.)
 // * Weight ring: whole-line units (qgemm_common.h: a tile times 128 bytes of
 //   each column, two loads of eight whole lines each, rearranged into the
 //   two steps' operands by exchange()), kRowsRing units ahead, running on
@@ -1203,9 +1204,15 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
   struct Unit {
     u32x4 a, b;
   };
+  // Unit u of a chunk in consumption order: tiles in blocks of two (the
+  // last block of one when KT is odd), and within a block the quads in
+  // order, the block's two tiles alternating.
   auto unit_load = [&](int c, int u) {
+    constexpr int F = (KT / 2) * 2 * QC;             // units in two-tile blocks
     const int dc = u / (KT * QC), w = u % (KT * QC);
-    const unsigned so = codes_at(c + dc, w % QC, w / QC);
+    const int k = w < F ? 2 * (w / (2 * QC)) + (w % 2) : KT - 1;
+    const int q = w < F ? (w % (2 * QC)) / 2 : w - F;
+    const unsigned so = codes_at(c + dc, q, k);
     Unit r;
     r.a = __builtin_amdgcn_raw_buffer_load_b128(wr, voff_a, so, kRowsAux);
     r.b = __builtin_amdgcn_raw_buffer_load_b128(wr, voff_b, so, kRowsAux);
@@ -1302,92 +1309,108 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
     }
     __syncthreads();
 
-    // ---- the chunk's steps, tile-major: (tile k, pair p) for p = 0..KCP-1.
-    u32x4 w_odd;                                     // the second step of the current unit
+    // ---- the chunk's steps in blocks of two tiles (the last block of an odd
+    // KT has one): for each pair p the codes of the block's tiles are
+    // unpacked, then each row set's A operands are read once from LDS and
+    // meet both tiles. An even pair takes the next unit of each tile: the
+    // exchange gives the unit's two steps' operands, the ring shifts
+    // (register renaming in the unrolled chunk) and loads the unit RU ahead;
+    // the odd pair uses the second operands.
+    u32x4 w_odd[2];
+    int u = 0;                                       // this chunk's next unit (compile-time)
 #pragma unroll
-    for (int k = 0; k < KT; ++k) {
+    for (int kb = 0; kb < (KT + 1) / 2; ++kb) {
+      const int nk = 2 * kb + 1 < KT ? 2 : 1;
 #pragma unroll
       for (int p = 0; p < KCP; ++p) {
         // Per-step LDS offsets behind an empty asm: the steps' reads must not
         // be hoisted out of the loops (registers).
         unsigned a_step = (unsigned)(h * 16 + j) * kSlot16, x_step = 4u * (unsigned)h;
         asm volatile("" : "+v"(a_step), "+v"(x_step));
-        auto a_of = [&](int r, int t) {
-          return *reinterpret_cast<const u32x4*>(ximg + a_step + (p * RS + r) * kPair16 +
-                                                 t * kTRow16);
-        };
-        // An even step takes the next unit: the exchange gives its two steps'
-        // operands, the ring shifts (register renaming in the unrolled chunk)
-        // and loads the unit RU ahead; the odd step uses the second operand.
-        u32x4 w;
-        if (p % 2 == 0) {
-          exchange(ring[0].a, ring[0].b, w, w_odd);
-          // Both operands are complete before the refill is issued, so the
-          // slot's registers are free for it.
-          asm volatile("" : "+v"(w), "+v"(w_odd) :: "memory");
+        u32x4 bq[2][4];
+        float sq[2][NQ], cq[2][NQ];
 #pragma unroll
-          for (int i = 0; i + 1 < RU; ++i) ring[i] = ring[i + 1];
-          ring[RU - 1] = unit_load(c, k * QC + p / 2 + RU);
-        } else {
-          w = w_odd;
-        }
-        const u32x4 v = split_groups(w);
-        u32x4 bq[4];
-        float sq[NQ], cq[NQ];
-        if constexpr (HV) {
-          // One more swap per group: MFMA q sees half q % 2 of group 2p + q / 2.
-          const auto a = __builtin_amdgcn_permlane16_swap(v.x, v.y, false, false);
-          const auto b = __builtin_amdgcn_permlane16_swap(v.z, v.w, false, false);
-          bq[0] = unpack_codes(a[0], magic);
-          bq[1] = unpack_codes(a[1], magic);
-          bq[2] = unpack_codes(b[0], magic);
-          bq[3] = unpack_codes(b[1], magic);
-          const u32x4 sb = *reinterpret_cast<const u32x4*>(tab + (k * 16 + j) * (NQ * KCP) + NQ * p);
+        for (int kk = 0; kk < 2; ++kk) {
+          if (kk >= nk) continue;
+          const int k = 2 * kb + kk;
+          u32x4 w;
+          if (p % 2 == 0) {
+            exchange(ring[0].a, ring[0].b, w, w_odd[kk]);
+            // Both operands are complete before the refill is issued, so the
+            // slot's registers are free for it.
+            asm volatile("" : "+v"(w), "+v"(w_odd[kk]) :: "memory");
 #pragma unroll
-          for (int q = 0; q < NQ; ++q) {
-            sq[q] = half_lo(sb[q]);
-            cq[q] = fmaf(-TR::c0, sq[q], half_hi(sb[q]));
+            for (int i = 0; i + 1 < RU; ++i) ring[i] = ring[i + 1];
+            ring[RU - 1] = unit_load(c, u + RU);
+            ++u;
+          } else {
+            w = w_odd[kk];
           }
-        } else {
-          // The bias term is added per chunk (below): only the scales here.
+          const u32x4 v = split_groups(w);
+          if constexpr (HV) {
+            // One more swap per group: MFMA q sees half q % 2 of group 2p + q / 2.
+            const auto a = __builtin_amdgcn_permlane16_swap(v.x, v.y, false, false);
+            const auto b = __builtin_amdgcn_permlane16_swap(v.z, v.w, false, false);
+            bq[kk][0] = unpack_codes(a[0], magic);
+            bq[kk][1] = unpack_codes(a[1], magic);
+            bq[kk][2] = unpack_codes(b[0], magic);
+            bq[kk][3] = unpack_codes(b[1], magic);
+            const u32x4 sb =
+                *reinterpret_cast<const u32x4*>(tab + (k * 16 + j) * (NQ * KCP) + NQ * p);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) bq[t] = unpack_codes(v[t], magic);
-          const u32x2 sb = *reinterpret_cast<const u32x2*>(tab + (k * 16 + j) * GC + 2 * p);
-          sq[0] = half_lo(sb.x);
-          sq[1] = half_lo(sb.y);
+            for (int q = 0; q < NQ; ++q) {
+              sq[kk][q] = half_lo(sb[q]);
+              cq[kk][q] = fmaf(-TR::c0, sq[kk][q], half_hi(sb[q]));
+            }
+          } else {
+            // The bias term is added per chunk (below): only the scales here.
+#pragma unroll
+            for (int t = 0; t < 4; ++t) bq[kk][t] = unpack_codes(v[t], magic);
+            const u32x2 sb = *reinterpret_cast<const u32x2*>(tab + (k * 16 + j) * GC + 2 * p);
+            sq[kk][0] = half_lo(sb.x);
+            sq[kk][1] = half_lo(sb.y);
+          }
         }
 #pragma unroll
         for (int r = 0; r < RS; ++r) {
           const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
           u32x4 Ar[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) Ar[t] = a_of(r, t);
+          for (int t = 0; t < 4; ++t)
+            Ar[t] = *reinterpret_cast<const u32x4*>(ximg + a_step + (p * RS + r) * kPair16 +
+                                                    t * kTRow16);
           const float* xs = xsl + (p * RS + r) * XSF + x_step;
-          if constexpr (HV) {
-            f32x4 C[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) C[q] = mfma16x16x32<TR::f16>(Ar[q], bq[q], zero4);
+          for (int kk = 0; kk < 2; ++kk) {
+            if (kk >= nk) continue;
+            const int k = 2 * kb + kk;
+            if constexpr (HV) {
+              f32x4 C[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x4 xq = *reinterpret_cast<const f32x4*>(xs + 16 * q);
+              for (int q = 0; q < 4; ++q) C[q] = mfma16x16x32<TR::f16>(Ar[q], bq[kk][q], zero4);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const f32x4 xq = *reinterpret_cast<const f32x4*>(xs + 16 * q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  acc[k][r][e] =
+                      fmaf(sq[kk][q], C[q][e], fmaf(cq[kk][q], xq[e], acc[k][r][e]));
+              }
+            } else {
+              (void)xs;
+              f32x4 C0 = mfma16x16x32<TR::f16>(Ar[0], bq[kk][0], zero4);
+              f32x4 C1 = mfma16x16x32<TR::f16>(Ar[2], bq[kk][2], zero4);
+              C0 = mfma16x16x32<TR::f16>(Ar[1], bq[kk][1], C0);
+              C1 = mfma16x16x32<TR::f16>(Ar[3], bq[kk][3], C1);
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                acc[k][r][e] = fmaf(sq[q], C[q][e], fmaf(cq[q], xq[e], acc[k][r][e]));
+                acc[k][r][e] = fmaf(sq[kk][1], C1[e], fmaf(sq[kk][0], C0[e], acc[k][r][e]));
             }
-          } else {
-            (void)xs;
-            f32x4 C0 = mfma16x16x32<TR::f16>(Ar[0], bq[0], zero4);
-            f32x4 C1 = mfma16x16x32<TR::f16>(Ar[2], bq[2], zero4);
-            C0 = mfma16x16x32<TR::f16>(Ar[1], bq[1], C0);
-            C1 = mfma16x16x32<TR::f16>(Ar[3], bq[3], C1);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[k][r][e] = fmaf(sq[1], C1[e], fmaf(sq[0], C0[e], acc[k][r][e]));
+            // The tile's sums are not read again before the chunk's bias
+            // term: without this the compiler defers every step's update to
+            // there and keeps all the steps' products live.
+            asm volatile("" : "+v"(acc[k][r]));
           }
-          // The tile's sums are not read again before the chunk's bias term:
-          // without this the compiler defers every step's update to there and
-          // keeps all the steps' products live.
-          asm volatile("" : "+v"(acc[k][r]));
         }
       }
     }
