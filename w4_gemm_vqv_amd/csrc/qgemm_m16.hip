@@ -1234,21 +1234,29 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
       HV ? (e8 >> 2) * kTRow16 + ((e8 & 3) * 16 + mm) * kSlot16
          : (e8 & 1) * kTRow16 + (sigma_slot(e8 >> 1) * 16 + mm) * kSlot16;
 
-  for (int c = 0; c < nch; ++c) {
-    if (c > 0) __syncthreads();                      // chunk c-1's image and tables are read
-    // ---- activations of all rows for groups c*GC .. c*GC + GC-1, and this
-    // wave's table; items (group gl, row octet ro) are dealt to the waves.
-    u32x4 xv[XR];
+  // ---- activations of all rows for groups cc*GC .. cc*GC + GC-1; items
+  // (group gl, row octet ro) are dealt to the waves. Chunk 0's are loaded
+  // here, each later chunk's during the previous chunk's last block of
+  // tiles, so that its staging finds them in registers (chunks past K load
+  // nothing).
+  u32x4 xv[XR];
+  auto x_load = [&](int cc) {
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
       const int it = wave + NW * i;
       const int gl = it / (2 * RS), ro = it % (2 * RS);
       const int row = 8 * ro + mm;
-      const int kk = 64 * (c * GC + gl) + 8 * e8;
+      const int kk = 64 * (cc * GC + gl) + 8 * e8;
       const bool ok = it < ITEMS && row < M && kk < K;
       xv[i] = __builtin_amdgcn_raw_buffer_load_b128(
           xr, ok ? (unsigned)((row * K + kk) * 2) : kOutOfRange, 0, 0);
     }
+  };
+  x_load(0);
+
+  for (int c = 0; c < nch; ++c) {
+    if (c > 0) __syncthreads();                      // chunk c-1's image and tables are read
+    // ---- this wave's table for the chunk, and the activations' image.
     // One dword per entry pair, two with HV (four entries).
     using TabWord = std::conditional_t<HV, u32x2, unsigned>;
     TabWord ts[TABL], tb[TABL];
@@ -1327,6 +1335,7 @@ __global__ __launch_bounds__(512) void qgemm_w4_rows(
         // be hoisted out of the loops (registers).
         unsigned a_step = (unsigned)(h * 16 + j) * kSlot16, x_step = 4u * (unsigned)h;
         asm volatile("" : "+v"(a_step), "+v"(x_step));
+        if (kb == (KT - 1) / 2 && p == 0) x_load(c + 1);  // the next chunk's activations
         u32x4 bq[2][4];
         float sq[2][NQ], cq[2][NQ];
 #pragma unroll
