@@ -286,8 +286,14 @@ __global__ __launch_bounds__(64 * NW) void qgemm_w4_m16(
     const int wgcols = min(cols, N - wg0);
     const int tiles = (wgcols + 15) >> 4;
     const int nblk = tiles * bpt;
-    const int b0 = (wave * nblk) / NW;
-    const int nb = ((wave + 1) * nblk) / NW - b0;
+    // SIMD s = wave % 4 takes the s-th quarter of the blocks. Its two waves
+    // share the SIMD's issue slots and the older one (waves 0-3 are
+    // dispatched first) wins the arbitration, so it takes 9/16 of them,
+    // rounded up.
+    const int sq0 = ((wave & 3) * nblk) >> 2, sq1 = (((wave & 3) + 1) * nblk) >> 2;
+    const int smid = sq0 + (((sq1 - sq0) * 9 + 15) >> 4);
+    const int b0 = NW == 8 ? (wave < 4 ? sq0 : smid) : (wave * nblk) / NW;
+    const int nb = NW == 8 ? (wave < 4 ? smid : sq1) - b0 : ((wave + 1) * nblk) / NW - b0;
     const int tfirst = b0 / bpt;
     // Weight row of logical column c of this group, relative to `row0`.
     const int row0 = SWIGLU ? (wg0 >> 1) : wg0;
