@@ -20,6 +20,10 @@ it). `roofline` reports the QMM kernel's algorithmic bytes per launch divided
 by its mean launch time (HIP events around a graph of back-to-back QMM
 launches, on the stream they run on) against the 8 TB/s HBM peak;
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+The step writes the logits y, as the plain projection does; on the fused
+path the line also times the same call without them (y is optional there:
+the argmax and accept lengths do not need it), `fused_no_logits_us_mean` and
+`rows_per_s_no_logits`.
 
 `--variant m8|m8q|v` pins the projection kernel family of the M <= 8 path
 (through VQV_FORCE_VARIANT) so that a profiler trace holds one variant only.
@@ -519,10 +523,24 @@ def main():
         g_s.replay()
         s_runs = [timed(g_s) * 1e3 / nq for _ in range(5)]
     f_runs = None
+    fn_runs = None
     if use_fused:
         g_f = graph_of(fused, nq)
         g_f.replay()
         f_runs = [timed(g_f) * 1e3 / nq for _ in range(5)]
+
+        # The same fused call without the logits: y is not written, and the
+        # argmax and accept lengths are the same (the fused verify needs no
+        # logits; the step above writes them, as the plain projection does).
+        def fused_no_logits(i, st):
+            xc, wc, sc, bc = copies[i % R]
+            vqv.vqv_qgemm_verify(xc, wc, sc, bc, draft if T > 1 else None, B, T, y=None,
+                                 want_y=False, argmax=am, accept_len=al, workspace=fws,
+                                 group=group, stream=st)
+
+        g_fn = graph_of(fused_no_logits, nq)
+        g_fn.replay()
+        fn_runs = [timed(g_fn) * 1e3 / nq for _ in range(5)]
 
     # Secondary bandwidth reference: a device copy of 512 MiB each way,
     # timed the same way (graph of back-to-back copies).
@@ -651,6 +669,8 @@ def main():
         "qgemm_us_runs": q_runs,
         "verify_us_mean": statistics.fmean(v_runs),
         "fused_us_mean": statistics.fmean(f_runs) if f_runs else None,
+        "fused_no_logits_us_mean": statistics.fmean(fn_runs) if fn_runs else None,
+        "rows_per_s_no_logits": M / (statistics.fmean(fn_runs) * 1e-6) if fn_runs else None,
         "swiglu_us_mean": statistics.fmean(s_runs) if s_runs else None,
         "step_path": "fused" if use_fused else ("swiglu" if use_swiglu else "separate"),
         "step_hbm_gbs": (qb + (4 * M * N if T and not use_fused else 0)) / (ms_step * 1e-3) / 1e9,
