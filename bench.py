@@ -343,7 +343,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:
-            print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+            print(f"bench.py measures one GPU only: the library has no multi-GPU path "
                   f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
 

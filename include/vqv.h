@@ -64,7 +64,7 @@ typedef enum {
 typedef enum {
   VQV_OK = 0,
   VQV_ERR_ARG = 1,         /* NULL pointer, size out of range, or aliasing   */
-  VQV_ERR_UNSUPPORTED = 2, /* valid request this build does not handle     */
+  VQV_ERR_UNSUPPORTED = 2, /* valid request the library does not handle  */
   VQV_ERR_ALIGN = 3,       /* a pointer breaks its alignment requirement    */
   VQV_ERR_WORKSPACE = 4,   /* workspace missing or smaller than queried     */
   VQV_ERR_HIP = 5          /* the HIP runtime refused the launch            */
