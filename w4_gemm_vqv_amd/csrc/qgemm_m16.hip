@@ -840,14 +840,16 @@ __global__ __launch_bounds__(512) void qgemm_w4_wide(
   Top2Scan best[4] = {top2_scan_none(), top2_scan_none(), top2_scan_none(), top2_scan_none()};
   // A finished tile goes straight to y: lane (j, h) holds rows 4h .. 4h+3 of
   // column j (a lane's tiles come in increasing column order, as top2_scan
-  // needs).
+  // needs). The stores are non-temporal: nothing here reads y again, and at
+  // the vocabulary width (4.9 MB of logits) the projection ran 46.8 against
+  // 47.7 us with ordinary stores.
   auto store_tile = [&](int k) {
     const int c = col0(k) + j;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int m = 4 * h + e;
       if (m < M && c < N) {
-        if (!fused || y) y[(size_t)m * N + c] = acc[e];
+        if (!fused || y) __builtin_nontemporal_store(acc[e], &y[(size_t)m * N + c]);
         if (fused) top2_scan(best[e], acc[e], c, acc[e] == acc[e]);
       }
       acc[e] = 0.0f;
