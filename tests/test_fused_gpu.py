@@ -233,3 +233,13 @@ def test_graph_replays(vqv):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, want[0]) and torch.equal(a, want[1]) and torch.equal(l, want[2]), rep
+
+
+@pytest.mark.parametrize("name,B,T", [("vocab_verify", 1, 8), ("batched_vocab", 4, 16)])
+def test_full_size_without_logits(vqv, name, B, T):
+    """The logits-free fused call at the vocabulary and batched workloads'
+    full sizes (the call `bench.py` times beside the step): its argmax and
+    accept lengths equal the two-call path's and the oracle walk's."""
+    c = gen.make_config(name)
+    y, _, _ = compare(vqv, c, B, T, want_y=False)
+    assert y is None
